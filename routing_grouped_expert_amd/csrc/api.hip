@@ -1,0 +1,231 @@
+// C ABI of libmoe.so (declared in include/moe.h): argument checks on the
+// host, workspace carving, and the stream-ordered launch chain. No call
+// allocates, synchronises or copies to the host.
+#include "moe.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace moe {
+hipError_t launch_router_logits(const uint16_t* x, const float* wg, const float* bias, int T, int H,
+                                int E, float* logits, hipStream_t stream);
+hipError_t launch_route(const float* logits, int T, int E, int k, int* ids, float* w,
+                        hipStream_t stream);
+size_t permute_workspace_bytes(int T, int E, int L);
+hipError_t launch_permute(const int* ids, int T, int k, int E, int first, int L, int* counts,
+                          int* offsets, int* perm, int* e2p, void* ws, hipStream_t stream);
+size_t ffn_workspace_bytes(int T, int k, int I);
+hipError_t launch_grouped_ffn(const uint16_t* x, const int* perm, const int* offsets, int L, int T,
+                              int k, int H, int I, const uint16_t* w1, const uint16_t* w2,
+                              float* out, void* ws, hipStream_t stream);
+hipError_t launch_combine(const float* eo, const int* e2p, const float* w, int T, int k, int H,
+                          uint16_t* y, hipStream_t stream);
+}  // namespace moe
+
+namespace {
+
+constexpr int kMaxExperts = 4096;
+constexpr int kMaxTopK = 32;
+constexpr int64_t kMaxIndex = (int64_t)1 << 31;
+
+size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+moe_status launched(hipError_t e) { return e == hipSuccess ? MOE_SUCCESS : MOE_ERROR_LAUNCH; }
+
+// Sizes shared by every call; returns the status for invalid/unsupported.
+moe_status check_common(int64_t T, int64_t E, int64_t k) {
+  if (T < 0 || E < 1 || k < 1) return MOE_ERROR_INVALID_VALUE;
+  if (k > E) return MOE_ERROR_INVALID_VALUE;
+  if (E > kMaxExperts || k > kMaxTopK) return MOE_ERROR_UNSUPPORTED;
+  if (T * k >= kMaxIndex) return MOE_ERROR_UNSUPPORTED;
+  return MOE_SUCCESS;
+}
+
+moe_status check_share(int64_t E, int64_t first, int64_t L) {
+  if (first < 0 || L < 0 || first + L > E) return MOE_ERROR_INVALID_VALUE;
+  return MOE_SUCCESS;
+}
+
+moe_status check_dims(int64_t T, int64_t k, int64_t H, int64_t I) {
+  if (H < 1 || I < 1) return MOE_ERROR_INVALID_VALUE;
+  const int64_t m = H > I ? H : I;
+  if (T * k * m >= kMaxIndex || 2 * I * H >= kMaxIndex) return MOE_ERROR_UNSUPPORTED;
+  return MOE_SUCCESS;
+}
+
+// Workspace layout of moe_forward; every region starts 256-byte aligned.
+struct Layout {
+  size_t logits, ids, weights, counts, offsets, perm, e2p, permute_ws, ffn_ws, expert_out, total;
+};
+
+Layout layout(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k, int64_t L) {
+  Layout o{};
+  size_t at = 0;
+  auto take = [&](size_t bytes) {
+    size_t here = at;
+    at += align256(bytes > 0 ? bytes : 1);
+    return here;
+  };
+  const size_t n = (size_t)T * k;
+  o.logits = take((size_t)T * E * 4);
+  o.ids = take(n * 4);
+  o.weights = take(n * 4);
+  o.counts = take((size_t)E * 4);
+  o.offsets = take((size_t)(L + 1) * 4);
+  o.perm = take(n * 4);
+  o.e2p = take(n * 4);
+  o.permute_ws = take(moe::permute_workspace_bytes((int)T, (int)E, (int)L));
+  o.ffn_ws = take(moe::ffn_workspace_bytes((int)T, (int)k, (int)I));
+  o.expert_out = take(n * (size_t)H * 4);
+  o.total = at;
+  return o;
+}
+
+bool aligned256(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 255u) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(moe_status s) {
+  switch (s) {
+    case MOE_SUCCESS: return "MOE_SUCCESS";
+    case MOE_ERROR_INVALID_VALUE: return "MOE_ERROR_INVALID_VALUE";
+    case MOE_ERROR_UNSUPPORTED: return "MOE_ERROR_UNSUPPORTED";
+    case MOE_ERROR_WORKSPACE: return "MOE_ERROR_WORKSPACE";
+    case MOE_ERROR_LAUNCH: return "MOE_ERROR_LAUNCH";
+  }
+  return "MOE_ERROR_UNKNOWN";
+}
+
+moe_status moe_partition(int32_t E, int32_t S, int32_t s, int32_t* first_expert,
+                         int32_t* num_local) {
+  if (!first_expert || !num_local || E < 1 || S < 1 || s < 0 || s >= S)
+    return MOE_ERROR_INVALID_VALUE;
+  const int32_t base = E / S, rem = E % S;
+  // Shares before s: every one holds base experts, and the first min(s, rem)
+  // of them one more.
+  *first_expert = s * base + (s < rem ? s : rem);
+  *num_local = base + (s < rem ? 1 : 0);
+  return MOE_SUCCESS;
+}
+
+moe_status moe_workspace_size(int32_t T, int32_t H, int32_t I, int32_t E, int32_t k,
+                              int32_t num_local, size_t* bytes) {
+  if (!bytes) return MOE_ERROR_INVALID_VALUE;
+  moe_status st = check_common(T, E, k);
+  if (st == MOE_SUCCESS) st = check_share(E, 0, num_local);
+  if (st == MOE_SUCCESS) st = check_dims(T, k, H, I);
+  if (st != MOE_SUCCESS) return st;
+  *bytes = layout(T, H, I, E, k, num_local).total;
+  return MOE_SUCCESS;
+}
+
+moe_status moe_router_logits(const uint16_t* x, const float* w_gate, const float* bias, int32_t T,
+                             int32_t H, int32_t E, float* logits, void* stream) {
+  if (T < 0 || H < 1 || E < 1) return MOE_ERROR_INVALID_VALUE;
+  if (E > kMaxExperts || (int64_t)T * H >= kMaxIndex || (int64_t)E * H >= kMaxIndex ||
+      (int64_t)T * E >= kMaxIndex)
+    return MOE_ERROR_UNSUPPORTED;
+  if (T == 0) return MOE_SUCCESS;
+  if (!x || !w_gate || !logits) return MOE_ERROR_INVALID_VALUE;
+  return launched(moe::launch_router_logits(x, w_gate, bias, T, H, E, logits, as_stream(stream)));
+}
+
+moe_status moe_route(const float* logits, int32_t T, int32_t E, int32_t k, int32_t* topk_ids,
+                     float* topk_weights, void* stream) {
+  moe_status st = check_common(T, E, k);
+  if (st != MOE_SUCCESS) return st;
+  if ((int64_t)T * E >= kMaxIndex) return MOE_ERROR_UNSUPPORTED;
+  if (T == 0) return MOE_SUCCESS;
+  if (!logits || !topk_ids || !topk_weights) return MOE_ERROR_INVALID_VALUE;
+  return launched(moe::launch_route(logits, T, E, k, topk_ids, topk_weights, as_stream(stream)));
+}
+
+moe_status moe_permute(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E,
+                       int32_t first_expert, int32_t num_local, int32_t* expert_counts,
+                       int32_t* expert_offsets, int32_t* permuted_rows,
+                       int32_t* expanded_to_permuted, void* ws, size_t ws_bytes, void* stream) {
+  moe_status st = check_common(T, E, k);
+  if (st == MOE_SUCCESS) st = check_share(E, first_expert, num_local);
+  if (st != MOE_SUCCESS) return st;
+  if (T == 0) return MOE_SUCCESS;
+  if (!topk_ids || !expert_counts || !expert_offsets || !permuted_rows || !expanded_to_permuted)
+    return MOE_ERROR_INVALID_VALUE;
+  const size_t need = moe::permute_workspace_bytes(T, E, num_local);
+  if (need > 0 && (!ws || ws_bytes < need || !aligned256(ws))) return MOE_ERROR_WORKSPACE;
+  return launched(moe::launch_permute(topk_ids, T, k, E, first_expert, num_local, expert_counts,
+                                      expert_offsets, permuted_rows, expanded_to_permuted, ws,
+                                      as_stream(stream)));
+}
+
+moe_status moe_grouped_ffn(const uint16_t* x, const int32_t* permuted_rows,
+                           const int32_t* expert_offsets, int32_t num_local, int32_t T, int32_t k,
+                           int32_t H, int32_t I, const uint16_t* w1, const uint16_t* w2,
+                           float* expert_out, void* ws, size_t ws_bytes, void* stream) {
+  if (T < 0 || k < 1 || num_local < 0) return MOE_ERROR_INVALID_VALUE;
+  if (k > kMaxTopK || num_local > kMaxExperts || (int64_t)T * k >= kMaxIndex)
+    return MOE_ERROR_UNSUPPORTED;
+  moe_status st = check_dims(T, k, H, I);
+  if (st != MOE_SUCCESS) return st;
+  if (T == 0 || num_local == 0) return MOE_SUCCESS;
+  if (!x || !permuted_rows || !expert_offsets || !w1 || !w2 || !expert_out)
+    return MOE_ERROR_INVALID_VALUE;
+  const size_t need = moe::ffn_workspace_bytes(T, k, I);
+  if (!ws || ws_bytes < need || !aligned256(ws)) return MOE_ERROR_WORKSPACE;
+  return launched(moe::launch_grouped_ffn(x, permuted_rows, expert_offsets, num_local, T, k, H, I,
+                                          w1, w2, expert_out, ws, as_stream(stream)));
+}
+
+moe_status moe_combine(const float* expert_out, const int32_t* expanded_to_permuted,
+                       const float* topk_weights, int32_t T, int32_t k, int32_t H, uint16_t* y,
+                       void* stream) {
+  if (T < 0 || k < 1 || H < 1) return MOE_ERROR_INVALID_VALUE;
+  if (k > kMaxTopK || (int64_t)T * k * H >= kMaxIndex) return MOE_ERROR_UNSUPPORTED;
+  if (T == 0) return MOE_SUCCESS;
+  if (!expert_out || !expanded_to_permuted || !topk_weights || !y) return MOE_ERROR_INVALID_VALUE;
+  return launched(moe::launch_combine(expert_out, expanded_to_permuted, topk_weights, T, k, H, y,
+                                      as_stream(stream)));
+}
+
+moe_status moe_forward(const uint16_t* x, const float* w_gate, const float* router_bias,
+                       const uint16_t* w1, const uint16_t* w2, int32_t T, int32_t H, int32_t I,
+                       int32_t E, int32_t k, int32_t first_expert, int32_t num_local, uint16_t* y,
+                       float* logits_out, int32_t* topk_ids_out, float* topk_weights_out,
+                       void* ws, size_t ws_bytes, void* stream) {
+  moe_status st = check_common(T, E, k);
+  if (st == MOE_SUCCESS) st = check_share(E, first_expert, num_local);
+  if (st == MOE_SUCCESS) st = check_dims(T, k, H, I);
+  if (st != MOE_SUCCESS) return st;
+  if ((int64_t)T * E >= kMaxIndex || (int64_t)E * H >= kMaxIndex) return MOE_ERROR_UNSUPPORTED;
+  if (T == 0) return MOE_SUCCESS;
+  if (!x || !w_gate || !y || (num_local > 0 && (!w1 || !w2))) return MOE_ERROR_INVALID_VALUE;
+  const Layout lo = layout(T, H, I, E, k, num_local);
+  if (!ws || ws_bytes < lo.total || !aligned256(ws)) return MOE_ERROR_WORKSPACE;
+  char* base = static_cast<char*>(ws);
+  float* logits = logits_out ? logits_out : reinterpret_cast<float*>(base + lo.logits);
+  int32_t* ids = topk_ids_out ? topk_ids_out : reinterpret_cast<int32_t*>(base + lo.ids);
+  float* wts = topk_weights_out ? topk_weights_out : reinterpret_cast<float*>(base + lo.weights);
+  int32_t* counts = reinterpret_cast<int32_t*>(base + lo.counts);
+  int32_t* offsets = reinterpret_cast<int32_t*>(base + lo.offsets);
+  int32_t* perm = reinterpret_cast<int32_t*>(base + lo.perm);
+  int32_t* e2p = reinterpret_cast<int32_t*>(base + lo.e2p);
+  float* eo = reinterpret_cast<float*>(base + lo.expert_out);
+  hipStream_t s = as_stream(stream);
+
+  hipError_t err = moe::launch_router_logits(x, w_gate, router_bias, T, H, E, logits, s);
+  if (err == hipSuccess) err = moe::launch_route(logits, T, E, k, ids, wts, s);
+  if (err == hipSuccess)
+    err = moe::launch_permute(ids, T, k, E, first_expert, num_local, counts, offsets, perm, e2p,
+                              base + lo.permute_ws, s);
+  if (err == hipSuccess && num_local > 0)
+    err = moe::launch_grouped_ffn(x, perm, offsets, num_local, T, k, H, I, w1, w2, eo,
+                                  base + lo.ffn_ws, s);
+  if (err == hipSuccess) err = moe::launch_combine(eo, e2p, wts, T, k, H, y, s);
+  return launched(err);
+}
+
+}  // extern "C"

@@ -1,0 +1,93 @@
+// Device-side helpers shared by the libmoe kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// Round to nearest even on the fp32 bit pattern; NaN stays NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu)) return static_cast<uint16_t>((u >> 16) | 0x40u);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int mask) {
+  uint32_t lo = static_cast<uint32_t>(v), hi = static_cast<uint32_t>(v >> 32);
+  lo = __shfl_xor(lo, mask, kWave);
+  hi = __shfl_xor(hi, mask, kWave);
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    uint64_t o = shfl_xor_u64(v, m);
+    v = o > v ? o : v;
+  }
+  return v;
+}
+
+// Butterfly sum: every lane ends with the same value, summed in the same
+// fixed order on every run.
+__device__ __forceinline__ float wave_sum_f32(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
+  return v;
+}
+
+// Exclusive prefix sum over data[0, n) in shared memory by one block of
+// blockDim.x threads (a multiple of 64, at most 1024); data[n] receives the
+// total. `tmp` is shared scratch of at least blockDim.x / 64 ints. Must be
+// called by every thread of the block.
+__device__ inline void block_exclusive_scan(int* data, int n, int* tmp) {
+  const int nt = blockDim.x, tid = threadIdx.x;
+  const int per = (n + nt - 1) / nt;
+  const int b = tid * per, e = min(b + per, n);
+  int local = 0;
+  for (int i = b; i < e; ++i) local += data[i];
+  // inclusive scan of `local` across the block
+  const int lane = tid % kWave, wave = tid / kWave;
+  int v = local;
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    int o = __shfl_up(v, d, kWave);
+    if (lane >= d) v += o;
+  }
+  if (lane == kWave - 1) tmp[wave] = v;
+  __syncthreads();
+  if (wave == 0) {
+    int w = lane < nt / kWave ? tmp[lane] : 0;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+      int o = __shfl_up(w, d, kWave);
+      if (lane >= d) w += o;
+    }
+    if (lane < nt / kWave) tmp[lane] = w;
+  }
+  __syncthreads();
+  int run = v - local + (wave > 0 ? tmp[wave - 1] : 0);
+  const int total = tmp[nt / kWave - 1];
+  __syncthreads();
+  for (int i = b; i < e; ++i) {
+    int c = data[i];
+    data[i] = run;
+    run += c;
+  }
+  if (tid == 0) data[n] = total;
+  __syncthreads();
+}
+
+}  // namespace moe

@@ -1,0 +1,101 @@
+// Routing: top-k of each token's fp32 logits, then the softmax renormalised
+// over the k selected experts.
+//
+// Page "TRTLLM-Gen MoE routing optimisation in FlashInfer: relieving register
+// pressure" (flashinfer PR #3751), section 1 "Dynamic thread block size":
+// the launch shape follows the work (there, the block size follows the token
+// count so registers do not spill). Here one wave64 owns one token; the
+// kernel is instantiated per values-per-lane tier (E / 64 rounded up to a
+// power of two) so a lane keeps its share of the logits in registers
+// whatever E is, and the tier table plays the role of that page's section 2
+// (valid expert-count / block-size combinations fixed at compile time).
+//
+// Selection: k rounds of a wave-wide maximum over 64-bit keys
+//   key = (order-preserving bits of the logit) << 32 | (0xFFFFFFFF - id)
+// so the larger logit wins and, on equal logits, the lower id; -0 is folded
+// onto +0 first so the two compare equal. Weights: w_j = exp(l_j - l_0) /
+// sum_i exp(l_i - l_0) over the k selected logits (the full-softmax
+// normaliser cancels in the renormalisation).
+#include "device.h"
+
+namespace moe {
+
+namespace {
+
+__device__ __forceinline__ uint64_t make_key(float v, int id) {
+  v = v + 0.0f;  // -0 -> +0
+  uint32_t u = __float_as_uint(v);
+  uint32_t mono = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return (static_cast<uint64_t>(mono) << 32) | (0xFFFFFFFFu - static_cast<uint32_t>(id));
+}
+
+__device__ __forceinline__ float key_value(uint64_t key) {
+  uint32_t mono = static_cast<uint32_t>(key >> 32);
+  uint32_t u = (mono & 0x80000000u) ? (mono & 0x7FFFFFFFu) : ~mono;
+  return __uint_as_float(u);
+}
+
+__device__ __forceinline__ int key_id(uint64_t key) {
+  return static_cast<int>(0xFFFFFFFFu - static_cast<uint32_t>(key));
+}
+
+template <int VPL>
+__global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ logits, int T, int E,
+                                                   int k, int* __restrict__ ids,
+                                                   float* __restrict__ weights) {
+  const int lane = threadIdx.x % kWave;
+  const int t = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+  if (t >= T) return;
+  const float* l = logits + (size_t)t * E;
+  uint64_t key[VPL];
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) {
+    const int e = lane + kWave * i;
+    key[i] = e < E ? make_key(l[e], e) : 0ull;  // a valid key is never 0
+  }
+  uint64_t mine = 0;  // lane j keeps the key of selection j
+  for (int j = 0; j < k; ++j) {
+    uint64_t best = key[0];
+#pragma unroll
+    for (int i = 1; i < VPL; ++i) best = key[i] > best ? key[i] : best;
+    best = wave_max_u64(best);
+#pragma unroll
+    for (int i = 0; i < VPL; ++i)
+      if (key[i] == best) key[i] = 0ull;
+    if (lane == j) mine = best;
+  }
+  // Lane 0 holds the first (largest) selection.
+  const uint32_t top_bits = __shfl(static_cast<uint32_t>(mine >> 32), 0, kWave);
+  const float top = key_value(static_cast<uint64_t>(top_bits) << 32);
+  const float ex = lane < k ? expf(key_value(mine) - top) : 0.0f;
+  const float s = wave_sum_f32(ex);
+  if (lane < k) {
+    ids[(size_t)t * k + lane] = key_id(mine);
+    weights[(size_t)t * k + lane] = ex / s;
+  }
+}
+
+template <int VPL>
+hipError_t launch_tier(const float* logits, int T, int E, int k, int* ids, float* w,
+                       hipStream_t stream) {
+  const int waves_per_block = 4;
+  dim3 grid((T + waves_per_block - 1) / waves_per_block);
+  hipLaunchKernelGGL(route_kernel<VPL>, grid, dim3(waves_per_block * kWave), 0, stream, logits, T,
+                     E, k, ids, w);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_route(const float* logits, int T, int E, int k, int* ids, float* w,
+                        hipStream_t stream) {
+  if (E <= 64) return launch_tier<1>(logits, T, E, k, ids, w, stream);
+  if (E <= 128) return launch_tier<2>(logits, T, E, k, ids, w, stream);
+  if (E <= 256) return launch_tier<4>(logits, T, E, k, ids, w, stream);
+  if (E <= 512) return launch_tier<8>(logits, T, E, k, ids, w, stream);
+  if (E <= 1024) return launch_tier<16>(logits, T, E, k, ids, w, stream);
+  if (E <= 2048) return launch_tier<32>(logits, T, E, k, ids, w, stream);
+  return launch_tier<64>(logits, T, E, k, ids, w, stream);
+}
+
+}  // namespace moe

@@ -1,0 +1,114 @@
+"""moe_grouped_ffn and moe_combine against the oracle.
+
+Grouped FFN tolerance (derived): inputs are exact bf16, products exact in
+the MFMA, fp32 accumulation over K <= 16384 terms (relative error ~1e-6 of
+the term scale), silu in fp32, and the intermediate carried as hi + lo bf16
+(2^-17 relative). The output error stays below 1e-4 of max|ref| and the mean
+below 2e-5 of mean|ref|.
+
+Combine: one fp32 sum of at most k products, then one round to bf16: the
+result is within half a bf16 ulp of the exact value, plus fp32 slack.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import routing_grouped_expert_amd as moe
+import synth
+from gpu_util import bf16_to_f64, dev, empty, host, note, sync, torch
+
+pytestmark = pytest.mark.gpu
+
+
+def layer(seed, T, H, I, E, k, first, L):
+    x = synth.normal_bf16(seed, synth.X, (T, H), 1.0)
+    w1 = synth.normal_bf16(seed, synth.W1, (L, 2 * I, H), 0.02, first_expert=first)
+    w2 = synth.normal_bf16(seed, synth.W2, (L, H, I), 0.02, first_expert=first)
+    ids = synth.topk_ids(seed, synth.IDS, T, E, k)
+    return x, w1, w2, ids
+
+
+def run_ffn(x, perm, offsets, k, w1, w2, x_offset=0):
+    """x_offset > 0 places x at an element offset inside a larger buffer (not
+    16-byte aligned), which takes the checked element-wise path."""
+    t = torch()
+    T, H = x.shape
+    L = len(offsets) - 1
+    I = w2.shape[2]
+    xb = dev(np.concatenate([np.zeros(x_offset, np.uint16), x.reshape(-1)]))
+    xd = xb[x_offset:].view(T, H)
+    out = t.full((T * k, H), float("nan"), dtype=t.float32, device="cuda:0")
+    ws = moe.alloc_workspace(T, H, I, 1 + L, k, L)
+    pd = dev(perm if len(perm) else np.zeros(1, np.int32))
+    moe.grouped_ffn(xd, pd, dev(offsets), k, dev(w1), dev(w2), out, ws)
+    sync()
+    return host(out)
+
+
+def check_ffn(T, H, I, E, k, first, L, seed=1, x_offset=0):
+    note(f"ffn T={T} H={H} I={I} E={E} k={k} share=({first},{L}) x_offset={x_offset}")
+    x, w1, w2, ids = layer(seed, T, H, I, E, k, first, L)
+    _, offsets, perm, _ = oracle.permute(ids, E, first, L)
+    got = run_ffn(x, perm, offsets, k, w1, w2, x_offset)
+    n = offsets[-1]
+    ref = oracle.grouped_ffn(x, perm, offsets, k, w1, w2)
+    g = got[:n].astype(np.float64)
+    assert np.isfinite(g).all()
+    err = np.abs(g - ref)
+    assert err.max() <= 1e-4 * np.abs(ref).max(), err.max() / np.abs(ref).max()
+    assert err.mean() <= 2e-5 * np.abs(ref).mean(), err.mean() / np.abs(ref).mean()
+    assert np.isnan(got[n:]).all()  # rows past N_L untouched
+
+
+# one 16-token tile, two, four, eight (+ a second pass when an expert has > 128 rows)
+@pytest.mark.parametrize("T,E,k", [(12, 4, 2), (30, 8, 2), (60, 6, 2), (300, 2, 1)])
+def test_ffn_fast_path_tiles(T, E, k):
+    check_ffn(T, 256, 384, E, k, 0, E)
+
+
+def test_ffn_share_and_empty_experts():
+    check_ffn(40, 128, 256, 16, 2, 3, 9)   # several local experts get no rows
+
+
+@pytest.mark.parametrize("H,I", [(200, 72), (130, 260), (8, 24)])
+def test_ffn_checked_path_ragged(H, I):
+    check_ffn(37, H, I, 5, 2, 0, 5)
+
+
+def test_ffn_checked_path_misaligned():
+    check_ffn(20, 256, 256, 4, 2, 0, 4, x_offset=3)
+
+
+def test_ffn_no_rows():
+    x, w1, w2, ids = layer(3, 8, 128, 128, 8, 1, 0, 2)
+    offsets = np.zeros(3, np.int32)
+    got = run_ffn(x, np.zeros(0, np.int32), offsets, 1, w1, w2)
+    assert np.isnan(got).all()
+
+
+def run_combine(eo, e2p, w, H):
+    t = torch()
+    T, k = w.shape
+    y = empty((T, H), t.int16)
+    moe.combine(dev(eo), dev(e2p), dev(w), y)
+    sync()
+    return host(y, np.uint16)
+
+
+@pytest.mark.parametrize("T,E,k,H,first,L", [(16, 8, 2, 128, 0, 8), (64, 40, 8, 300, 5, 20),
+                                             (33, 12, 3, 7, 0, 0)])
+def test_combine(T, E, k, H, first, L):
+    note(f"combine T={T} k={k} H={H} share=({first},{L})")
+    ids = synth.topk_ids(9, 400, T, E, k)
+    _, offsets, perm, e2p = oracle.permute(ids, E, first, L)
+    n = max(int(offsets[-1]), 1)
+    eo = synth.normal_f32(9, synth.EXPERT_OUT, (T * k, H), 1.0)
+    w = np.abs(synth.normal_f32(9, synth.WEIGHTS, (T, k), 0.4))
+    y = run_combine(eo, e2p, w, H)
+    ref = oracle.combine(eo[:n].astype(np.float64), e2p, w.astype(np.float64), T, k, H)
+    got = bf16_to_f64(y)
+    ulp = np.spacing(np.abs(ref).astype(np.float32)).astype(np.float64) * 65536.0  # bf16 ulp
+    slack = 1e-6 * (np.abs(w).sum(1, keepdims=True) * np.abs(eo).max())
+    assert (np.abs(got - ref) <= 0.5 * ulp + slack).all()
+    if L == 0:
+        assert (got == 0).all()

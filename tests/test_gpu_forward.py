@@ -1,0 +1,86 @@
+"""moe_forward against the oracle: routing bit-exact, the bf16 output within
+max|err| <= 2e-2 max|ref| and mean|err| <= 2e-3 mean|ref| of the fp64 oracle
+on the same bf16 inputs. Reduced sizes compare every output; the full
+workload sizes compare all routing and a sample of token outputs, in the
+launch configuration the benchmark times."""
+import numpy as np
+import pytest
+
+import oracle
+import routing_grouped_expert_amd as moe
+from gpu_util import assert_layer_ok, bf16_to_f64, dev, empty, host, note, sync, torch
+from synth import configs
+
+pytestmark = pytest.mark.gpu
+W_TOL = 4e-6
+
+
+def gpu_forward(d):
+    t = torch()
+    T, H, E, k, I = d["T"], d["H"], d["E"], d["k"], d["I"]
+    first, L = d["first"], d["L"]
+    y = empty((T, H), t.int16)
+    logits = empty((T, E), t.float32)
+    ids = empty((T, k), t.int32)
+    w = empty((T, k), t.float32)
+    ws = moe.alloc_workspace(T, H, I, E, k, L)
+    moe.forward(dev(d["x"]), dev(d["wg"]), None if d["bias"] is None else dev(d["bias"]),
+                dev(d["w1"]), dev(d["w2"]), k, first, L, y, ws, logits, ids, w)
+    sync()
+    return host(y, np.uint16), host(logits), host(ids), host(w)
+
+
+def check_forward(d, sample=None, what=""):
+    note(f"forward {what} T={d['T']} H={d['H']} I={d['I']} E={d['E']} k={d['k']} "
+         f"share=({d['first']},{d['L']})")
+    y, lg, ids, w = gpu_forward(d)
+    rlg, rids, rw, ry = oracle.forward(d["x"], d["wg"], d["w1"], d["w2"], d["k"], d["first"],
+                                       d["L"], d["bias"], sample)
+    ulp = np.spacing(np.abs(rlg))
+    assert (np.abs(lg.astype(np.float64) - rlg) <= ulp).all()
+    assert np.array_equal(ids, rids), f"{what}: routing differs for tokens {np.unique(np.argwhere(ids != rids)[:, 0])[:8]}"
+    assert np.abs(w - rw).max() <= W_TOL
+    ys = y if sample is None else y[sample]
+    return assert_layer_ok(ys, ry, what)
+
+
+def test_forward_tiny():
+    check_forward(configs.layer_inputs(configs.WORKLOADS["tiny"]), what="tiny")
+
+
+@pytest.mark.parametrize("name,T,H,I", [("decode", 32, 512, 1024), ("fine", 128, 512, 256),
+                                        ("share0", 256, 512, 256)])
+def test_forward_reduced(name, T, H, I):
+    check_forward(configs.layer_inputs(configs.WORKLOADS[name], T=T, H=H, I=I), what=name)
+
+
+def test_forward_odd_shapes():
+    cfg = dict(configs.WORKLOADS["fine"], E=13, k=3, first=2, L=7)
+    check_forward(configs.layer_inputs(cfg, T=45, H=200, I=72), what="odd shapes")
+
+
+def test_forward_shares_sum_to_whole_layer():
+    """Weights are renormalised before the share mask, so the shares' outputs
+    add up to the whole layer (up to one bf16 rounding per share)."""
+    cfg = dict(configs.WORKLOADS["share0"], E=20, S=5)
+    full = configs.layer_inputs(cfg, T=64, H=256, I=128, first=0, L=20)
+    y_full = bf16_to_f64(gpu_forward(full)[0])
+    acc = np.zeros_like(y_full)
+    for s in range(5):
+        f, c = moe.partition(20, 5, s)
+        d = configs.layer_inputs(cfg, T=64, H=256, I=128, first=f, L=c)
+        acc += bf16_to_f64(gpu_forward(d)[0])
+    err = np.abs(acc - y_full)
+    assert err.max() <= 6 * 2 ** -8 * np.abs(y_full).max()
+    assert err.mean() <= 2e-3 * np.abs(y_full).mean() * 3
+
+
+@pytest.mark.parametrize("name", ["decode", "fine", "share0"])
+def test_forward_full_size_sampled(name):
+    cfg = configs.WORKLOADS[name]
+    assert moe.partition(cfg["E"], cfg["S"], cfg["s"]) == (cfg["first"], cfg["L"])
+    d = configs.layer_inputs(cfg)
+    T = d["T"]
+    sample = np.unique(np.array([0, 1, T // 3, T // 2, T - 2, T - 1, 7 % T, (5 * T) // 7],
+                                np.int32))
+    check_forward(d, sample=sample, what=name + " full size")

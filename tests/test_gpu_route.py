@@ -1,0 +1,121 @@
+"""moe_route and moe_permute against the oracle, bit-exact for ids, counts,
+offsets and the permutation; weights within the fp32 bound below.
+
+Weight tolerance (derived): the GPU forms exp(l_j - l_0) in fp32 (the
+difference rounds with |l_j - l_0| <= ~12, an absolute error <= 1e-6, and
+expf adds ~1 ulp), sums at most 32 terms and divides; the relative error of
+w_j is below 3e-6, and w_j <= 1, so |w_gpu - w_oracle| <= 4e-6.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import routing_grouped_expert_amd as moe
+import synth
+from gpu_util import dev, empty, host, note, sync, torch
+from synth import configs
+
+pytestmark = pytest.mark.gpu
+W_TOL = 4e-6
+
+
+def gpu_route(logits, k):
+    t = torch()
+    T, E = logits.shape
+    ids = empty((T, k), t.int32)
+    w = empty((T, k), t.float32)
+    moe.route(dev(logits), k, ids, w)
+    sync()
+    return host(ids), host(w)
+
+
+def check_route(logits, k, what):
+    note(f"route {what} T={logits.shape[0]} E={logits.shape[1]} k={k}")
+    ids, w = gpu_route(logits, k)
+    rid, rw = oracle.route(logits, k)
+    assert np.array_equal(ids, rid), f"{what}: ids differ at {np.argwhere(ids != rid)[:5]}"
+    assert np.abs(w - rw).max() <= W_TOL, f"{what}: weights off by {np.abs(w - rw).max():.2e}"
+    assert np.abs(w.astype(np.float64).sum(1) - 1.0).max() <= W_TOL
+
+
+@pytest.mark.parametrize("T", configs.ROUTING["T"])
+def test_routing_workload(T):
+    check_route(configs.routing_logits(T), configs.ROUTING["k"], "normal logits")
+
+
+@pytest.mark.parametrize("T", configs.ROUTING["T"])
+def test_routing_workload_ties(T):
+    lg = configs.routing_logits(T, ties=True)
+    check_route(lg, configs.ROUTING["k"], "eight-level logits")
+
+
+@pytest.mark.parametrize("E,k", [(1, 1), (5, 5), (8, 2), (63, 7), (64, 8), (65, 8), (300, 32),
+                                 (1024, 1), (2049, 8), (4096, 32)])
+def test_routing_edges(E, k):
+    lg = synth.normal_f32(77, 200 + E, (37, E), 1.0)
+    check_route(lg, k, "edge")
+
+
+def test_routing_special_values():
+    lg = np.full((3, 100), 0.5, np.float32)
+    ids, w = gpu_route(lg, 8)
+    assert (ids == np.arange(8)).all() and np.abs(w - 0.125).max() == 0
+    lg = np.array([[0.0, -0.0, -1.0, -0.0], [-0.0, 0.0, 0.0, -3.0]], np.float32)
+    check_route(lg, 3, "signed zeros")
+
+
+def gpu_permute(ids, E, first, L):
+    t = torch()
+    T, k = ids.shape
+    counts = empty((E,), t.int32)
+    offsets = empty((L + 1,), t.int32)
+    perm = t.full((T * k,), -5, dtype=t.int32, device="cuda:0")
+    e2p = empty((T * k,), t.int32)
+    ws = moe.alloc_workspace(T, 128, 128, E, k, L)
+    moe.permute(dev(ids), E, first, L, counts, offsets, perm, e2p, ws)
+    sync()
+    return host(counts), host(offsets), host(perm), host(e2p)
+
+
+CASES = [(1, 8, 2, 0, 8), (32, 8, 2, 0, 8), (16, 8, 2, 2, 3), (64, 1024, 8, 0, 1024),
+         (65, 8, 2, 0, 8), (200, 40, 4, 13, 9), (512, 256, 8, 0, 256), (4096, 1024, 8, 0, 1024),
+         (4096, 384, 8, 0, 77), (4096, 384, 8, 308, 76), (100, 4096, 32, 1000, 2000),
+         (129, 16, 4, 5, 0), (3000, 1, 1, 0, 1)]
+
+
+@pytest.mark.parametrize("T,E,k,first,L", CASES)
+def test_permute(T, E, k, first, L):
+    note(f"permute T={T} E={E} k={k} share=({first},{L})")
+    ids = synth.topk_ids(31, 300 + T, T, E, k)
+    c, o, p, e = gpu_permute(ids, E, first, L)
+    rc, ro, rp, re = oracle.permute(ids, E, first, L)
+    assert np.array_equal(c, rc)
+    assert np.array_equal(o, ro)
+    n = ro[-1]
+    assert np.array_equal(p[:n], rp)
+    assert (p[n:] == -5).all()  # positions past N_L are not written
+    assert np.array_equal(e, re)
+
+
+def test_permute_structured():
+    T, E, k = 300, 16, 4
+    shared = np.tile(np.array([3, 9, 0, 5], np.int32), (T, 1))
+    disjoint = ((np.arange(T)[:, None] * k + np.arange(k)[None, :]) % E).astype(np.int32)
+    for ids in (shared, disjoint):
+        for first, L in [(0, 16), (4, 6)]:
+            got = gpu_permute(ids, E, first, L)
+            want = oracle.permute(ids, E, first, L)
+            for g, w_ in zip(got, want):
+                assert np.array_equal(g[: len(w_)], w_)
+
+
+def test_route_then_permute_repeatable():
+    lg = configs.routing_logits(4096)
+    a = gpu_route(lg, 8)
+    for _ in range(3):
+        b = gpu_route(lg, 8)
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    p1 = gpu_permute(a[0], 1024, 0, 1024)
+    p2 = gpu_permute(a[0], 1024, 0, 1024)
+    for x, y in zip(p1, p2):
+        assert np.array_equal(x, y)
