@@ -63,6 +63,10 @@ typedef enum moe_status {
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* moe_status_string(moe_status status);
 
+/* Name of the HIP error behind the last MOE_ERROR_LAUNCH returned on the
+ * calling host thread ("hipSuccess" if there was none). Diagnostic only. */
+const char* moe_last_launch_error(void);
+
 /*
  * moe_partition -- contiguous ceil/floor split of E experts over S shares.
  * [P-A2A] section 1, "Flexible expert-to-rank mapping": base = E / S,

@@ -18,8 +18,8 @@ STATUS = {0: "MOE_SUCCESS", 1: "MOE_ERROR_INVALID_VALUE", 2: "MOE_ERROR_UNSUPPOR
 
 
 class MoeError(RuntimeError):
-    def __init__(self, fn, status):
-        super().__init__(f"{fn} returned {STATUS.get(status, status)}")
+    def __init__(self, fn, status, detail=""):
+        super().__init__(f"{fn} returned {STATUS.get(status, status)}{detail}")
         self.status = status
 
 
@@ -30,6 +30,7 @@ _SZ = ctypes.c_size_t
 
 _SIGS = {
     "moe_status_string": ([ctypes.c_int], ctypes.c_char_p),
+    "moe_last_launch_error": ([], ctypes.c_char_p),
     "moe_partition": ([_I32, _I32, _I32, ctypes.POINTER(_I32), ctypes.POINTER(_I32)], ctypes.c_int),
     "moe_workspace_size": ([_I32] * 6 + [ctypes.POINTER(_SZ)], ctypes.c_int),
     "moe_router_logits": ([_VP, _VP, _VP, _I32, _I32, _I32, _VP, _VP], ctypes.c_int),
@@ -62,7 +63,10 @@ def lib():
 
 def _check(fn, st):
     if st != 0:
-        raise MoeError(fn, st)
+        detail = ""
+        if st == 4:
+            detail = f" ({lib().moe_last_launch_error().decode()})"
+        raise MoeError(fn, st, detail)
 
 
 def _ptr(t):

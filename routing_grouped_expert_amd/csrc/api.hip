@@ -15,7 +15,7 @@ hipError_t launch_route(const float* logits, int T, int E, int k, int* ids, floa
 size_t permute_workspace_bytes(int T, int E, int L);
 hipError_t launch_permute(const int* ids, int T, int k, int E, int first, int L, int* counts,
                           int* offsets, int* perm, int* e2p, void* ws, hipStream_t stream);
-size_t ffn_workspace_bytes(int T, int k, int I);
+size_t ffn_workspace_bytes(int T, int k, int I, int L);
 hipError_t launch_grouped_ffn(const uint16_t* x, const int* perm, const int* offsets, int L, int T,
                               int k, int H, int I, const uint16_t* w1, const uint16_t* w2,
                               float* out, void* ws, hipStream_t stream);
@@ -33,7 +33,19 @@ size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 
 hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 
-moe_status launched(hipError_t e) { return e == hipSuccess ? MOE_SUCCESS : MOE_ERROR_LAUNCH; }
+// HIP error of the last failed launch on this host thread (for diagnostics).
+thread_local hipError_t t_last_launch_error = hipSuccess;
+
+// hipGetLastError reports the last failing HIP call of the thread, whoever
+// made it (a query that returned hipErrorNotReady counts). Clear it before a
+// call's launches so the status reflects this call's launches only.
+void clear_stale_error() { (void)hipGetLastError(); }
+
+moe_status launched(hipError_t e) {
+  if (e == hipSuccess) return MOE_SUCCESS;
+  t_last_launch_error = e;
+  return MOE_ERROR_LAUNCH;
+}
 
 // Sizes shared by every call; returns the status for invalid/unsupported.
 moe_status check_common(int64_t T, int64_t E, int64_t k) {
@@ -78,7 +90,7 @@ Layout layout(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k, int64_t L) 
   o.perm = take(n * 4);
   o.e2p = take(n * 4);
   o.permute_ws = take(moe::permute_workspace_bytes((int)T, (int)E, (int)L));
-  o.ffn_ws = take(moe::ffn_workspace_bytes((int)T, (int)k, (int)I));
+  o.ffn_ws = take(moe::ffn_workspace_bytes((int)T, (int)k, (int)I, (int)L));
   o.expert_out = take(n * (size_t)H * 4);
   o.total = at;
   return o;
@@ -100,6 +112,8 @@ const char* moe_status_string(moe_status s) {
   }
   return "MOE_ERROR_UNKNOWN";
 }
+
+const char* moe_last_launch_error(void) { return hipGetErrorName(t_last_launch_error); }
 
 moe_status moe_partition(int32_t E, int32_t S, int32_t s, int32_t* first_expert,
                          int32_t* num_local) {
@@ -132,6 +146,7 @@ moe_status moe_router_logits(const uint16_t* x, const float* w_gate, const float
     return MOE_ERROR_UNSUPPORTED;
   if (T == 0) return MOE_SUCCESS;
   if (!x || !w_gate || !logits) return MOE_ERROR_INVALID_VALUE;
+  clear_stale_error();
   return launched(moe::launch_router_logits(x, w_gate, bias, T, H, E, logits, as_stream(stream)));
 }
 
@@ -142,6 +157,7 @@ moe_status moe_route(const float* logits, int32_t T, int32_t E, int32_t k, int32
   if ((int64_t)T * E >= kMaxIndex) return MOE_ERROR_UNSUPPORTED;
   if (T == 0) return MOE_SUCCESS;
   if (!logits || !topk_ids || !topk_weights) return MOE_ERROR_INVALID_VALUE;
+  clear_stale_error();
   return launched(moe::launch_route(logits, T, E, k, topk_ids, topk_weights, as_stream(stream)));
 }
 
@@ -157,6 +173,7 @@ moe_status moe_permute(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E,
     return MOE_ERROR_INVALID_VALUE;
   const size_t need = moe::permute_workspace_bytes(T, E, num_local);
   if (need > 0 && (!ws || ws_bytes < need || !aligned256(ws))) return MOE_ERROR_WORKSPACE;
+  clear_stale_error();
   return launched(moe::launch_permute(topk_ids, T, k, E, first_expert, num_local, expert_counts,
                                       expert_offsets, permuted_rows, expanded_to_permuted, ws,
                                       as_stream(stream)));
@@ -174,8 +191,9 @@ moe_status moe_grouped_ffn(const uint16_t* x, const int32_t* permuted_rows,
   if (T == 0 || num_local == 0) return MOE_SUCCESS;
   if (!x || !permuted_rows || !expert_offsets || !w1 || !w2 || !expert_out)
     return MOE_ERROR_INVALID_VALUE;
-  const size_t need = moe::ffn_workspace_bytes(T, k, I);
+  const size_t need = moe::ffn_workspace_bytes(T, k, I, num_local);
   if (!ws || ws_bytes < need || !aligned256(ws)) return MOE_ERROR_WORKSPACE;
+  clear_stale_error();
   return launched(moe::launch_grouped_ffn(x, permuted_rows, expert_offsets, num_local, T, k, H, I,
                                           w1, w2, expert_out, ws, as_stream(stream)));
 }
@@ -187,6 +205,7 @@ moe_status moe_combine(const float* expert_out, const int32_t* expanded_to_permu
   if (k > kMaxTopK || (int64_t)T * k * H >= kMaxIndex) return MOE_ERROR_UNSUPPORTED;
   if (T == 0) return MOE_SUCCESS;
   if (!expert_out || !expanded_to_permuted || !topk_weights || !y) return MOE_ERROR_INVALID_VALUE;
+  clear_stale_error();
   return launched(moe::launch_combine(expert_out, expanded_to_permuted, topk_weights, T, k, H, y,
                                       as_stream(stream)));
 }
@@ -216,6 +235,7 @@ moe_status moe_forward(const uint16_t* x, const float* w_gate, const float* rout
   float* eo = reinterpret_cast<float*>(base + lo.expert_out);
   hipStream_t s = as_stream(stream);
 
+  clear_stale_error();
   hipError_t err = moe::launch_router_logits(x, w_gate, router_bias, T, H, E, logits, s);
   if (err == hipSuccess) err = moe::launch_route(logits, T, E, k, ids, wts, s);
   if (err == hipSuccess)

@@ -321,9 +321,24 @@ hipError_t launch_nt(const uint16_t* x, const int* perm, const int* offsets, int
 }
 }  // namespace
 
-size_t ffn_workspace_bytes(int T, int k, int I) {
+bool ffn_sk_applies(const void* x, const void* w1, const void* w2, int T, int k, int L, int H,
+                    int I);
+size_t ffn_sk_workspace_bytes(int T, int k, int L);
+hipError_t launch_grouped_ffn_sk(const uint16_t* x, const int* perm, const int* offsets, int L,
+                                 int T, int k, int H, int I, const uint16_t* w1,
+                                 const uint16_t* w2, uint16_t* h_hi, uint16_t* h_lo, float* out,
+                                 void* ws, hipStream_t stream);
+
+namespace {
+size_t h_array_bytes(int T, int k, int I) {
   const size_t n = (size_t)T * k * I * 2;  // one bf16 array
-  return 2 * ((n + 255) & ~(size_t)255);
+  return (n + 255) & ~(size_t)255;
+}
+}  // namespace
+
+// Workspace: h_hi, h_lo ([T*k, I] bf16 each), then the stream-K plan / slots.
+size_t ffn_workspace_bytes(int T, int k, int I, int L) {
+  return 2 * h_array_bytes(T, k, I) + ffn_sk_workspace_bytes(T, k, L);
 }
 
 bool ffn_vector_path(const void* x, const void* w1, const void* w2, const void* ws, int H, int I) {
@@ -336,9 +351,12 @@ hipError_t launch_grouped_ffn(const uint16_t* x, const int* perm, const int* off
                               int k, int H, int I, const uint16_t* w1, const uint16_t* w2,
                               float* out, void* ws, hipStream_t stream) {
   const int nmax = T * k;
-  const size_t half = ffn_workspace_bytes(T, k, I) / 2;
+  const size_t half = h_array_bytes(T, k, I);
   uint16_t* h_hi = static_cast<uint16_t*>(ws);
   uint16_t* h_lo = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + half);
+  if (ffn_sk_applies(x, w1, w2, T, k, L, H, I))
+    return launch_grouped_ffn_sk(x, perm, offsets, L, T, k, H, I, w1, w2, h_hi, h_lo, out,
+                                 static_cast<char*>(ws) + 2 * half, stream);
   const bool vec = ffn_vector_path(x, w1, w2, ws, H, I);
   // A token picks an expert at most once, so an expert has at most T entries.
   const int bound = T < nmax ? T : nmax;

@@ -1,0 +1,525 @@
+// Grouped expert FFN, persistent "stream-K" schedule for the 16-byte /
+// 256-element fast path.
+//
+// Why: the expert weights are streamed once and every config is HBM-bound, so
+// the kernel time is (weight bytes) / (bandwidth actually sustained). A grid
+// of equal blocks that does not divide evenly into the resident block slots
+// leaves a last partial round with too few loads in flight. Here exactly the
+// resident number of blocks NB is launched and the work is cut into equal
+// contiguous ranges of units:
+//   tile = (pass, row group)   pass = up to NT*16 tokens of one expert
+//   unit = (tile, 256-wide K chunk); the 4 waves of a block take 64 each.
+// (With fewer units than resident blocks only the first U blocks take part,
+// so every participating block owns at least one unit.)
+// A block runs its units in order, adding its waves' partial sums in LDS in a
+// fixed order (wave 0, 1, 2, 3) at the end of each tile. A tile covered by
+// one block is finished directly; a tile cut between blocks leaves one
+// partial per block in a slot, and the block that arrives last (atomic
+// counter) adds the slots in block order and finishes the tile. The order of
+// every sum is fixed by the schedule, so results do not depend on timing.
+//
+// Operands: weight rows are the MFMA A operand and stream from HBM straight
+// into VGPRs (16 rows x 64 B per load instruction); the gathered token rows
+// (page "FlashInfer MoE optimisation: overlapping grouped activation staging
+// on Ampere and Hopper", flashinfer PR #7368, section 1: route index divided
+// by the route divisor, 128-bit loads, absent members read as zero) are the B
+// operand, loaded per lane from L2 with 16-byte loads. Weight loads of the
+// next chunk are issued before the current chunk's MFMAs (section 2 of the
+// same page: the weight stream starts first and overlaps the activation
+// gather).
+//
+// up:   tile rows = 16 gate rows + the 16 matching up rows; the finished tile
+//       applies SwiGLU and writes a = silu(g) * u as hi = bf16(a),
+//       lo = bf16(a - hi) (a is never rounded to bf16 alone).
+// down: tile rows = 64 rows of W2 (4 groups of 16 sharing each B fragment);
+//       B = hi and lo, two MFMAs into one fp32 accumulator; the finished tile
+//       writes fp32 expert_out.
+#include "device.h"
+
+namespace moe {
+
+namespace {
+constexpr int KSUB = 64;          // K per wave per unit
+constexpr int KUNIT = 4 * KSUB;   // K per unit (4 waves)
+constexpr int STEPS = KSUB / 32;  // MFMA K-steps per wave per unit
+constexpr int UP_ROWS = 16;       // gate rows (and as many up rows) per up tile
+constexpr int DOWN_GROUPS = 4;    // 16-row groups per down tile
+constexpr int DOWN_ROWS = 16 * DOWN_GROUPS;
+
+// Plan layout (ints): [0] passes P, then pass_expert[Pmax], pass_beg[Pmax],
+// pass_cnt[Pmax]; counters follow at a 256-byte boundary.
+struct PlanView {
+  int* hdr;
+  int* expert;
+  int* beg;
+  int* cnt;
+};
+
+__device__ __forceinline__ PlanView plan_view(int* plan, int pmax) {
+  return PlanView{plan, plan + 4, plan + 4 + pmax, plan + 4 + 2 * pmax};
+}
+
+// One block of 1024 threads: list the passes (expert, first entry, entries)
+// of every local expert with entries, and zero the fixup counters.
+__global__ __launch_bounds__(1024) void ffn_plan_kernel(const int* __restrict__ offsets, int L,
+                                                        int nmax, int nr, int* plan, int pmax,
+                                                        int* counters, int ncounters) {
+  extern __shared__ __attribute__((aligned(16))) int s_pass[];  // L + 1, then 16 scratch
+  const int tid = threadIdx.x;
+  for (int i = tid; i < ncounters; i += blockDim.x) counters[i] = 0;
+  for (int i = tid; i < L; i += blockDim.x) {
+    int b = max(0, min(offsets[i], nmax));
+    int e = max(b, min(offsets[i + 1], nmax));
+    s_pass[i] = (e - b + nr - 1) / nr;
+  }
+  __syncthreads();
+  block_exclusive_scan(s_pass, L, s_pass + L + 1);
+  PlanView pv = plan_view(plan, pmax);
+  for (int i = tid; i < L; i += blockDim.x) {
+    int b = max(0, min(offsets[i], nmax));
+    int e = max(b, min(offsets[i + 1], nmax));
+    for (int q = s_pass[i], t = b; t < e; ++q, t += nr) {
+      pv.expert[q] = i;
+      pv.beg[q] = t;
+      pv.cnt[q] = min(nr, e - t);
+    }
+  }
+  if (tid == 0) pv.hdr[0] = s_pass[L];
+}
+
+__device__ __forceinline__ bf16x8 ld8(const uint16_t* p) {
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(p));
+}
+
+__device__ __forceinline__ bf16x8 ld8_or_zero(const uint16_t* p, bool ok) {
+  u16x8 v = {0, 0, 0, 0, 0, 0, 0, 0};
+  if (ok) v = *reinterpret_cast<const u16x8*>(p);
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// Block containing unit u when U units are cut into NB equal ranges
+// [floor(b U / NB), floor((b + 1) U / NB)).
+__device__ __forceinline__ int block_of_unit(long u, long U, int NB) {
+  return (int)(((u + 1) * NB + U - 1) / U) - 1;
+}
+__device__ __forceinline__ long first_unit(int b, long U, int NB) { return (long)b * U / NB; }
+
+// Sum the four waves' accumulators of one tile in LDS, wave order 0..3.
+// Afterwards `red` holds the block's partial; every thread must call it.
+template <int N>
+__device__ __forceinline__ void block_reduce(f32x4 (&acc)[N], f32x4 (*red)[kWave], int wave,
+                                             int lane) {
+  for (int w = 0; w < 4; ++w) {
+    if (wave == w) {
+#pragma unroll
+      for (int i = 0; i < N; ++i) red[i][lane] = (w == 0) ? acc[i] : red[i][lane] + acc[i];
+    }
+    __syncthreads();
+  }
+}
+
+// Cross-block fixup of a tile cut between blocks. Wave 0 stores the block's
+// partial (`part`, N f32x4 per lane) into its slot, then the last block to
+// arrive adds all slots in block order into `part` and returns true.
+template <int N>
+__device__ bool fixup(f32x4 (&part)[N], f32x4* slots, int* counters, long tile, long C, long U,
+                      int NB, int b, int lane) {
+  const long t0 = tile * C;
+  const int bf = block_of_unit(t0, U, NB), bl = block_of_unit(t0 + C - 1, U, NB);
+  const int my_slot = 2 * b + (first_unit(b, U, NB) < t0 ? 1 : 0);
+  f32x4* mine = slots + (size_t)my_slot * N * kWave;
+#pragma unroll
+  for (int i = 0; i < N; ++i) mine[i * kWave + lane] = part[i];
+  __threadfence();
+  int last = 0;
+  if (lane == 0) last = atomicAdd(&counters[bf], 1) == (bl - bf);
+  last = __shfl(last, 0, kWave);
+  if (!last) return false;
+  __threadfence();
+#pragma unroll
+  for (int i = 0; i < N; ++i) part[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int pb = bf; pb <= bl; ++pb) {
+    const int slot = 2 * pb + (first_unit(pb, U, NB) < t0 ? 1 : 0);
+    const f32x4* src = slots + (size_t)slot * N * kWave;
+#pragma unroll
+    for (int i = 0; i < N; ++i) part[i] = part[i] + src[i * kWave + lane];
+  }
+  return true;
+}
+
+// ----------------------------------------------------------------- up
+template <int NTILES>
+__device__ __forceinline__ void up_mma(const bf16x8 (&ag)[STEPS], const bf16x8 (&au)[STEPS],
+                                       const bf16x8 (*bx)[STEPS], f32x4* accg, f32x4* accu) {
+#pragma unroll
+  for (int s = 0; s < STEPS; ++s) {
+#pragma unroll
+    for (int nt = 0; nt < NTILES; ++nt) {
+      accg[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ag[s], bx[nt][s], accg[nt], 0, 0, 0);
+      accu[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(au[s], bx[nt][s], accu[nt], 0, 0, 0);
+    }
+  }
+}
+
+template <int NT>
+__global__ __launch_bounds__(256) void ffn_up_sk_kernel(
+    const uint16_t* __restrict__ x, const int* __restrict__ perm, int k, int H, int I, int nmax,
+    const uint16_t* __restrict__ w1, int* plan, int pmax, f32x4* slots, int* counters,
+    uint16_t* __restrict__ h_hi, uint16_t* __restrict__ h_lo, int NB) {
+  __shared__ f32x4 red[2 * NT][kWave];
+  const PlanView pv = plan_view(plan, pmax);
+  const long P = pv.hdr[0];
+  const long G = I / UP_ROWS, C = H / KUNIT;
+  const long U = P * G * C;
+  const int nb = (int)min((long)NB, U);
+  const int b = blockIdx.x;
+  if (b >= nb) return;
+  const long s = first_unit(b, U, nb), e = first_unit(b + 1, U, nb);
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int kq = (lane >> 4) * 8 + wave * KSUB;
+  for (long u = s; u < e;) {
+    const long tile = u / C;
+    const int c0 = (int)(u % C);
+    const int c1 = (int)min(C, c0 + (e - u));
+    const int pass = (int)(tile / G), g = (int)(tile % G);
+    const int ex = pv.expert[pass], tb = pv.beg[pass], tc = pv.cnt[pass];
+    const int ntiles = (tc + 15) >> 4;
+    size_t xoff[NT];
+    bool xok[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const int n = nt * 16 + (lane & 15);
+      int tok = -1;
+      if (n < tc) {
+        const int r = perm[tb + n];
+        if (r >= 0 && r < nmax) tok = r / k;
+      }
+      xok[nt] = tok >= 0 && nt < ntiles;
+      xoff[nt] = (size_t)(tok >= 0 ? tok : 0) * H + kq;
+    }
+    const uint16_t* wg = w1 + ((size_t)ex * 2 * I + g * UP_ROWS + (lane & 15)) * H + kq;
+    const uint16_t* wu = wg + (size_t)I * H;
+    f32x4 acc[2 * NT];
+#pragma unroll
+    for (int i = 0; i < 2 * NT; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // operands of chunk c (cur) and c + 1 (next): the loads for c + 1 are in
+    // flight while chunk c is multiplied
+    bf16x8 ag[STEPS], au[STEPS], bx[NT][STEPS];
+    {
+      const size_t kb = (size_t)c0 * KUNIT;
+#pragma unroll
+      for (int st = 0; st < STEPS; ++st) {
+        ag[st] = ld8(wg + kb + 32 * st);
+        au[st] = ld8(wu + kb + 32 * st);
+      }
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int st = 0; st < STEPS; ++st) bx[nt][st] = ld8_or_zero(x + xoff[nt] + kb + 32 * st, xok[nt]);
+    }
+    for (int c = c0; c < c1; ++c) {
+      bf16x8 ng[STEPS], nu[STEPS], nx[NT][STEPS];
+      if (c + 1 < c1) {
+        const size_t kb = (size_t)(c + 1) * KUNIT;
+#pragma unroll
+        for (int st = 0; st < STEPS; ++st) {
+          ng[st] = ld8(wg + kb + 32 * st);
+          nu[st] = ld8(wu + kb + 32 * st);
+        }
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+          for (int st = 0; st < STEPS; ++st)
+            nx[nt][st] = ld8_or_zero(x + xoff[nt] + kb + 32 * st, xok[nt]);
+      }
+      switch (ntiles) {
+#define MOE_UPSK(n) \
+  case n:           \
+    if (n <= NT) up_mma<n>(ag, au, bx, acc, acc + NT); \
+    break;
+        MOE_UPSK(1) MOE_UPSK(2) MOE_UPSK(3) MOE_UPSK(4) MOE_UPSK(5) MOE_UPSK(6) MOE_UPSK(7)
+        MOE_UPSK(8)
+#undef MOE_UPSK
+      }
+#pragma unroll
+      for (int st = 0; st < STEPS; ++st) {
+        ag[st] = ng[st];
+        au[st] = nu[st];
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) bx[nt][st] = nx[nt][st];
+      }
+    }
+    block_reduce(acc, red, wave, lane);
+    if (wave == 0) {
+      bool done = true;
+#pragma unroll
+      for (int i = 0; i < 2 * NT; ++i) acc[i] = red[i][lane];
+      if (!(c0 == 0 && c1 == C)) done = fixup(acc, slots, counters, tile, C, U, nb, b, lane);
+      if (done) {
+        // lane l: rows g*16 + 4*(l/16) + j of token slot l % 16 of each N-tile
+        const int ir = g * UP_ROWS + (lane >> 4) * 4;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          const int n = nt * 16 + (lane & 15);
+          if (n >= tc) continue;
+          typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
+          u16x4 hi, lo;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float gg = acc[nt][j], uu = acc[NT + nt][j];
+            const float a = gg / (1.0f + expf(-gg)) * uu;
+            hi[j] = f32_to_bf16_bits(a);
+            lo[j] = f32_to_bf16_bits(a - bf16_bits_to_f32(hi[j]));
+          }
+          const size_t o = (size_t)(tb + n) * I + ir;
+          *reinterpret_cast<u16x4*>(h_hi + o) = hi;
+          *reinterpret_cast<u16x4*>(h_lo + o) = lo;
+        }
+      }
+    }
+    __syncthreads();  // red is reused by the next tile
+    u += c1 - c0;
+  }
+}
+
+// --------------------------------------------------------------- down
+template <int NTILES>
+__device__ __forceinline__ void down_mma(const bf16x8 (&a)[DOWN_GROUPS][STEPS],
+                                         const bf16x8 (*bh)[STEPS], const bf16x8 (*bl)[STEPS],
+                                         f32x4* acc) {
+#pragma unroll
+  for (int st = 0; st < STEPS; ++st) {
+#pragma unroll
+    for (int nt = 0; nt < NTILES; ++nt) {
+#pragma unroll
+      for (int rg = 0; rg < DOWN_GROUPS; ++rg) {
+        f32x4& c = acc[nt * DOWN_GROUPS + rg];
+        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[rg][st], bh[nt][st], c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[rg][st], bl[nt][st], c, 0, 0, 0);
+      }
+    }
+  }
+}
+
+template <int NT>
+__global__ __launch_bounds__(256) void ffn_down_sk_kernel(
+    const uint16_t* __restrict__ h_hi, const uint16_t* __restrict__ h_lo, int H, int I,
+    const uint16_t* __restrict__ w2, int* plan, int pmax, f32x4* slots, int* counters,
+    float* __restrict__ out, int NB) {
+  constexpr int NACC = NT * DOWN_GROUPS;
+  __shared__ f32x4 red[NACC][kWave];
+  const PlanView pv = plan_view(plan, pmax);
+  const long P = pv.hdr[0];
+  const long G = H / DOWN_ROWS, C = I / KUNIT;
+  const long U = P * G * C;
+  const int nb = (int)min((long)NB, U);
+  const int b = blockIdx.x;
+  if (b >= nb) return;
+  const long s = first_unit(b, U, nb), e = first_unit(b + 1, U, nb);
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int kq = (lane >> 4) * 8 + wave * KSUB;
+  for (long u = s; u < e;) {
+    const long tile = u / C;
+    const int c0 = (int)(u % C);
+    const int c1 = (int)min(C, c0 + (e - u));
+    const int pass = (int)(tile / G), g = (int)(tile % G);
+    const int ex = pv.expert[pass], tb = pv.beg[pass], tc = pv.cnt[pass];
+    const int ntiles = (tc + 15) >> 4;
+    const uint16_t* w = w2 + ((size_t)ex * H + g * DOWN_ROWS + (lane & 15)) * I + kq;
+    size_t hrow[NT];
+    bool hok[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const int n = nt * 16 + (lane & 15);
+      hok[nt] = n < tc && nt < ntiles;
+      hrow[nt] = (size_t)(tb + (n < tc ? n : 0)) * I + kq;
+    }
+    f32x4 acc[NACC];
+#pragma unroll
+    for (int i = 0; i < NACC; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    bf16x8 a[DOWN_GROUPS][STEPS], bh[NT][STEPS], bl[NT][STEPS];
+    {
+      const size_t kb = (size_t)c0 * KUNIT;
+#pragma unroll
+      for (int rg = 0; rg < DOWN_GROUPS; ++rg)
+#pragma unroll
+        for (int st = 0; st < STEPS; ++st) a[rg][st] = ld8(w + (size_t)rg * 16 * I + kb + 32 * st);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int st = 0; st < STEPS; ++st) {
+          bh[nt][st] = ld8_or_zero(h_hi + hrow[nt] + kb + 32 * st, hok[nt]);
+          bl[nt][st] = ld8_or_zero(h_lo + hrow[nt] + kb + 32 * st, hok[nt]);
+        }
+    }
+    for (int c = c0; c < c1; ++c) {
+      bf16x8 na[DOWN_GROUPS][STEPS], nh[NT][STEPS], nl[NT][STEPS];
+      if (c + 1 < c1) {
+        const size_t kb = (size_t)(c + 1) * KUNIT;
+#pragma unroll
+        for (int rg = 0; rg < DOWN_GROUPS; ++rg)
+#pragma unroll
+          for (int st = 0; st < STEPS; ++st)
+            na[rg][st] = ld8(w + (size_t)rg * 16 * I + kb + 32 * st);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+          for (int st = 0; st < STEPS; ++st) {
+            nh[nt][st] = ld8_or_zero(h_hi + hrow[nt] + kb + 32 * st, hok[nt]);
+            nl[nt][st] = ld8_or_zero(h_lo + hrow[nt] + kb + 32 * st, hok[nt]);
+          }
+      }
+      switch (ntiles) {
+#define MOE_DNSK(n) \
+  case n:           \
+    if (n <= NT) down_mma<n>(a, bh, bl, acc); \
+    break;
+        MOE_DNSK(1) MOE_DNSK(2) MOE_DNSK(3) MOE_DNSK(4) MOE_DNSK(5) MOE_DNSK(6) MOE_DNSK(7)
+        MOE_DNSK(8)
+#undef MOE_DNSK
+      }
+#pragma unroll
+      for (int st = 0; st < STEPS; ++st) {
+#pragma unroll
+        for (int rg = 0; rg < DOWN_GROUPS; ++rg) a[rg][st] = na[rg][st];
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          bh[nt][st] = nh[nt][st];
+          bl[nt][st] = nl[nt][st];
+        }
+      }
+    }
+    block_reduce(acc, red, wave, lane);
+    if (wave == 0) {
+      bool done = true;
+#pragma unroll
+      for (int i = 0; i < NACC; ++i) acc[i] = red[i][lane];
+      if (!(c0 == 0 && c1 == C)) done = fixup(acc, slots, counters, tile, C, U, nb, b, lane);
+      if (done) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          const int n = nt * 16 + (lane & 15);
+          if (n >= tc) continue;
+          float* o = out + (size_t)(tb + n) * H + g * DOWN_ROWS + (lane >> 4) * 4;
+#pragma unroll
+          for (int rg = 0; rg < DOWN_GROUPS; ++rg)
+            *reinterpret_cast<f32x4*>(o + rg * 16) = acc[nt * DOWN_GROUPS + rg];
+        }
+      }
+    }
+    __syncthreads();
+    u += c1 - c0;
+  }
+}
+
+int device_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+// Resident 256-thread blocks of `kernel` on the current device (cached).
+template <typename K>
+int resident_blocks(K kernel) {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  if (cached[dev] == 0) {
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, 0) != hipSuccess ||
+        per_cu <= 0)
+      per_cu = 1;
+    if (per_cu > 8) per_cu = 8;  // the workspace holds slots for 8 blocks per CU
+    cached[dev] = per_cu * device_cus();
+  }
+  return cached[dev];
+}
+
+// Token tiles per pass, from twice the mean entries per local expert (an
+// expert with more entries takes further passes); 0 = use the LDS-tiled
+// kernels instead (many tokens per expert: prefill shapes).
+int pick_nt(int T, int k, int L) {
+  const long bound = T;  // a token picks an expert at most once
+  const long twice_mean = L > 0 ? (2L * T * k + L - 1) / L : bound;
+  const long want = twice_mean < bound ? twice_mean : bound;
+  return want <= 16 ? 1 : want <= 32 ? 2 : 0;
+}
+
+size_t a256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+// Upper bound of resident 256-thread blocks: 8 per CU.
+int max_blocks() { return 8 * device_cus(); }
+
+struct SkLayout {
+  size_t plan, counters, slots, total;
+  int pmax, ncounters, slot_f32x4;
+};
+
+SkLayout sk_layout(int T, int k, int L, int NT) {
+  SkLayout o{};
+  const int nmax = T * k, nr = NT * 16;
+  o.pmax = L + (nmax + nr - 1) / nr + 1;
+  o.ncounters = 2 * max_blocks();
+  // a slot holds the larger of an up piece (2 NT) and a down piece (4 NT) f32x4 per lane
+  o.slot_f32x4 = NT * DOWN_GROUPS * kWave;
+  o.plan = 0;
+  o.counters = a256((size_t)(4 + 3 * o.pmax) * 4);
+  o.slots = o.counters + a256((size_t)o.ncounters * 4);
+  o.total = o.slots + a256((size_t)2 * max_blocks() * o.slot_f32x4 * 16);
+  return o;
+}
+
+template <int NT>
+hipError_t launch_sk_nt(const uint16_t* x, const int* perm, const int* offsets, int L, int T,
+                        int k, int H, int I, const uint16_t* w1, const uint16_t* w2,
+                        uint16_t* h_hi, uint16_t* h_lo, float* out, char* ws, hipStream_t stream) {
+  const SkLayout lo = sk_layout(T, k, L, NT);
+  int* plan = reinterpret_cast<int*>(ws + lo.plan);
+  int* counters = reinterpret_cast<int*>(ws + lo.counters);
+  f32x4* slots = reinterpret_cast<f32x4*>(ws + lo.slots);
+  const int nmax = T * k;
+  hipLaunchKernelGGL(ffn_plan_kernel, dim3(1), dim3(1024), (size_t)(L + 1 + 16) * 4, stream,
+                     offsets, L, nmax, NT * 16, plan, lo.pmax, counters, lo.ncounters);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  const int nb_up = resident_blocks(ffn_up_sk_kernel<NT>);
+  hipLaunchKernelGGL(ffn_up_sk_kernel<NT>, dim3(nb_up), dim3(256), 0, stream, x, perm, k, H, I,
+                     nmax, w1, plan, lo.pmax, slots, counters, h_hi, h_lo, nb_up);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  const int nb_down = resident_blocks(ffn_down_sk_kernel<NT>);
+  hipLaunchKernelGGL(ffn_down_sk_kernel<NT>, dim3(nb_down), dim3(256), 0, stream, h_hi, h_lo, H,
+                     I, w2, plan, lo.pmax, slots, counters + max_blocks(), out, nb_down);
+  return hipGetLastError();
+}
+}  // namespace
+
+bool ffn_sk_applies(const void* x, const void* w1, const void* w2, int T, int k, int L, int H,
+                    int I) {
+  auto al = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
+  return al(x) && al(w1) && al(w2) && H % KUNIT == 0 && I % KUNIT == 0 && pick_nt(T, k, L) > 0;
+}
+
+size_t ffn_sk_workspace_bytes(int T, int k, int L) {
+  const int nt = pick_nt(T, k, L);
+  return sk_layout(T, k, L, nt > 0 ? nt : 1).total;
+}
+
+hipError_t launch_grouped_ffn_sk(const uint16_t* x, const int* perm, const int* offsets, int L,
+                                 int T, int k, int H, int I, const uint16_t* w1,
+                                 const uint16_t* w2, uint16_t* h_hi, uint16_t* h_lo, float* out,
+                                 void* ws, hipStream_t stream) {
+  char* w = static_cast<char*>(ws);
+  if (pick_nt(T, k, L) == 1)
+    return launch_sk_nt<1>(x, perm, offsets, L, T, k, H, I, w1, w2, h_hi, h_lo, out, w, stream);
+  return launch_sk_nt<2>(x, perm, offsets, L, T, k, H, I, w1, w2, h_hi, h_lo, out, w, stream);
+}
+
+}  // namespace moe

@@ -19,7 +19,7 @@ def test_exports_every_declared_symbol():
     names = _declared()
     assert {"moe_partition", "moe_workspace_size", "moe_router_logits", "moe_route",
             "moe_permute", "moe_grouped_ffn", "moe_combine", "moe_forward",
-            "moe_status_string"} <= names
+            "moe_status_string", "moe_last_launch_error"} <= names
     L = ctypes.CDLL(moe.LIB_PATH)
     for n in sorted(names):
         assert hasattr(L, n), n
@@ -33,6 +33,7 @@ def test_status_strings():
     L = moe.lib()
     for code, name in moe.STATUS.items():
         assert L.moe_status_string(code).decode() == name
+    assert L.moe_last_launch_error().decode() == "hipSuccess"
 
 
 def test_partition_matches_worked_examples():

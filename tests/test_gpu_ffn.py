@@ -45,9 +45,10 @@ def run_ffn(x, perm, offsets, k, w1, w2, x_offset=0):
     return host(out)
 
 
-def check_ffn(T, H, I, E, k, first, L, seed=1, x_offset=0):
+def check_ffn(T, H, I, E, k, first, L, seed=1, x_offset=0, ids=None):
     note(f"ffn T={T} H={H} I={I} E={E} k={k} share=({first},{L}) x_offset={x_offset}")
-    x, w1, w2, ids = layer(seed, T, H, I, E, k, first, L)
+    x, w1, w2, rnd = layer(seed, T, H, I, E, k, first, L)
+    ids = rnd if ids is None else ids
     _, offsets, perm, _ = oracle.permute(ids, E, first, L)
     got = run_ffn(x, perm, offsets, k, w1, w2, x_offset)
     n = offsets[-1]
@@ -64,6 +65,27 @@ def check_ffn(T, H, I, E, k, first, L, seed=1, x_offset=0):
 @pytest.mark.parametrize("T,E,k", [(12, 4, 2), (30, 8, 2), (60, 6, 2), (300, 2, 1)])
 def test_ffn_fast_path_tiles(T, E, k):
     check_ffn(T, 256, 384, E, k, 0, E)
+
+
+# Persistent stream-K path (H, I multiples of 256; at most 32 mean-doubled
+# entries per expert): every tile cut between blocks when there are fewer
+# units than blocks, long K ranges, NT = 1 and 2, several passes per expert.
+@pytest.mark.parametrize("T,H,I,E,k", [(24, 512, 512, 8, 2), (60, 512, 768, 8, 2),
+                                       (32, 4096, 512, 8, 2), (16, 256, 4096, 4, 1),
+                                       (200, 1024, 512, 64, 2)])
+def test_ffn_stream_k(T, H, I, E, k):
+    check_ffn(T, H, I, E, k, 0, E)
+
+
+def test_ffn_stream_k_skewed_passes():
+    """One expert takes every token (three 16-token passes), others few."""
+    T, E, k = 40, 8, 2
+    ids = np.stack([np.zeros(T, np.int32), 1 + np.arange(T, dtype=np.int32) % 7], 1)
+    check_ffn(T, 512, 512, E, k, 0, E, ids=ids)
+
+
+def test_ffn_stream_k_share():
+    check_ffn(48, 512, 512, 12, 2, 4, 5)
 
 
 def test_ffn_share_and_empty_experts():

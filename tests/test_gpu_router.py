@@ -58,3 +58,14 @@ def test_router_exact_sums():
     wg = (m / float(1 << 20)).astype(np.float32)
     x = synth.f32_to_bf16(xv.astype(np.float32))
     assert np.array_equal(gpu_logits(x, wg, None), oracle.router_logits(x, wg, None))
+
+
+@pytest.mark.parametrize("T,H,E", [(5, 130, 13), (40, 256, 21), (64, 7168, 384), (1, 4, 1)])
+def test_router_few_tokens(T, H, E):
+    """The few-token kernel (T <= 64): vector and element-wise loads, E not a
+    multiple of its 8-expert groups."""
+    x = synth.normal_bf16(6, 93, (T, H), 1.0)
+    wg = synth.normal_f32(6, 94, (E, H), 0.1)
+    b = synth.normal_f32(6, 95, (E,), 1.0)
+    check(x, wg, b, "few tokens")
+    check(x, wg, None, "few tokens, no bias")
