@@ -41,7 +41,8 @@ def parse_args():
                     help="skip the oracle timing (profiling runs)")
     ap.add_argument("--no-routing", action="store_true", help="skip the routing-only timings")
     ap.add_argument("--calibrate-copy", action="store_true",
-                    help="also run one plain device copy of 256 MiB (counter calibration)")
+                    help="also run one elementwise kernel that reads 256 MiB and writes 256 MiB "
+                         "(calibrates the HBM byte counters)")
     return ap.parse_args()
 
 
@@ -152,7 +153,8 @@ def main():
     if args.calibrate_copy:
         src = torch.ones(64 << 20, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
-        dst.copy_(src)
+        torch.cuda.synchronize()
+        torch.add(src, 1.0, out=dst)  # reads 256 MiB, writes 256 MiB
         torch.cuda.synchronize()
 
     routing = None
