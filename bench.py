@@ -48,7 +48,7 @@ def parse_args():
 
 def ffn_source_digest():
     h = hashlib.sha256()
-    for name in ("ffn.hip", "device.h"):
+    for name in ("ffn.hip", "ffn_sk.hip", "device.h"):
         with open(os.path.join(ROOT, "routing_grouped_expert_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -104,7 +104,7 @@ def main():
     del d
 
     def step(ev0=None, ev1=None):
-        moe.router_logits(x, wg, bias, logits, stream)
+        moe.router_logits(x, wg, bias, logits, ws, stream)
         moe.route(logits, k, ids, wts, stream)
         moe.permute(ids, E, first, L, counts, offsets, perm, e2p, ws, stream)
         if ev0 is not None:

@@ -80,8 +80,9 @@ moe_status moe_partition(int32_t num_experts, int32_t num_shares, int32_t share,
 
 /*
  * moe_workspace_size -- bytes of device workspace that moe_forward needs
- * (*bytes, HOST pointer). moe_permute and moe_grouped_ffn need no more than
- * this for the same sizes, so one workspace serves every call. The workspace
+ * (*bytes, HOST pointer). moe_router_logits, moe_permute and moe_grouped_ffn
+ * need no more than this for the same sizes, so one workspace serves every
+ * call. The workspace
  * must be 256-byte aligned. Its contents need no initialisation and are
  * scratch after the call.
  */
@@ -95,9 +96,12 @@ moe_status moe_workspace_size(int32_t T, int32_t H, int32_t I, int32_t E, int32_
  * carried in fp64 and rounded once to fp32.
  *   x       [T, H] bf16;  w_gate [E, H] fp32;  bias [E] fp32 or NULL
  *   logits  [T, E] fp32 (output)
+ *   ws / ws_bytes  workspace (moe_workspace_size with the same T, H, E; it
+ *                  holds fp64 partial sums when T > 64, unused otherwise)
  */
 moe_status moe_router_logits(const uint16_t* x, const float* w_gate, const float* bias, int32_t T,
-                             int32_t H, int32_t E, float* logits, void* stream);
+                             int32_t H, int32_t E, float* logits, void* ws, size_t ws_bytes,
+                             void* stream);
 
 /*
  * moe_route -- softmax over the E logits, top-k, renormalise over the k.

@@ -33,7 +33,7 @@ _SIGS = {
     "moe_last_launch_error": ([], ctypes.c_char_p),
     "moe_partition": ([_I32, _I32, _I32, ctypes.POINTER(_I32), ctypes.POINTER(_I32)], ctypes.c_int),
     "moe_workspace_size": ([_I32] * 6 + [ctypes.POINTER(_SZ)], ctypes.c_int),
-    "moe_router_logits": ([_VP, _VP, _VP, _I32, _I32, _I32, _VP, _VP], ctypes.c_int),
+    "moe_router_logits": ([_VP, _VP, _VP, _I32, _I32, _I32, _VP, _VP, _SZ, _VP], ctypes.c_int),
     "moe_route": ([_VP, _I32, _I32, _I32, _VP, _VP, _VP], ctypes.c_int),
     "moe_permute": ([_VP, _I32, _I32, _I32, _I32, _I32, _VP, _VP, _VP, _VP, _VP, _SZ, _VP],
                     ctypes.c_int),
@@ -95,11 +95,12 @@ def workspace_size(T, H, I, E, k, num_local):
     return n.value
 
 
-def router_logits(x, w_gate, bias, logits, stream=None):
+def router_logits(x, w_gate, bias, logits, ws, stream=None):
     T, H = x.shape
     E = w_gate.shape[0]
-    _check("moe_router_logits", lib().moe_router_logits(_ptr(x), _ptr(w_gate), _ptr(bias), T, H,
-                                                        E, _ptr(logits), _stream(stream)))
+    _check("moe_router_logits", lib().moe_router_logits(
+        _ptr(x), _ptr(w_gate), _ptr(bias), T, H, E, _ptr(logits), _ptr(ws),
+        0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def route(logits, k, topk_ids, topk_weights, stream=None):

@@ -8,8 +8,9 @@
 #include <cstdint>
 
 namespace moe {
+size_t router_workspace_bytes(int T, int H, int E);
 hipError_t launch_router_logits(const uint16_t* x, const float* wg, const float* bias, int T, int H,
-                                int E, float* logits, hipStream_t stream);
+                                int E, float* logits, void* ws, hipStream_t stream);
 hipError_t launch_route(const float* logits, int T, int E, int k, int* ids, float* w,
                         hipStream_t stream);
 size_t permute_workspace_bytes(int T, int E, int L);
@@ -70,7 +71,8 @@ moe_status check_dims(int64_t T, int64_t k, int64_t H, int64_t I) {
 
 // Workspace layout of moe_forward; every region starts 256-byte aligned.
 struct Layout {
-  size_t logits, ids, weights, counts, offsets, perm, e2p, permute_ws, ffn_ws, expert_out, total;
+  size_t logits, ids, weights, counts, offsets, perm, e2p, router_ws, permute_ws, ffn_ws, expert_out,
+      total;
 };
 
 Layout layout(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k, int64_t L) {
@@ -89,6 +91,7 @@ Layout layout(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k, int64_t L) 
   o.offsets = take((size_t)(L + 1) * 4);
   o.perm = take(n * 4);
   o.e2p = take(n * 4);
+  o.router_ws = take(moe::router_workspace_bytes((int)T, (int)H, (int)E));
   o.permute_ws = take(moe::permute_workspace_bytes((int)T, (int)E, (int)L));
   o.ffn_ws = take(moe::ffn_workspace_bytes((int)T, (int)k, (int)I, (int)L));
   o.expert_out = take(n * (size_t)H * 4);
@@ -139,15 +142,19 @@ moe_status moe_workspace_size(int32_t T, int32_t H, int32_t I, int32_t E, int32_
 }
 
 moe_status moe_router_logits(const uint16_t* x, const float* w_gate, const float* bias, int32_t T,
-                             int32_t H, int32_t E, float* logits, void* stream) {
+                             int32_t H, int32_t E, float* logits, void* ws, size_t ws_bytes,
+                             void* stream) {
   if (T < 0 || H < 1 || E < 1) return MOE_ERROR_INVALID_VALUE;
   if (E > kMaxExperts || (int64_t)T * H >= kMaxIndex || (int64_t)E * H >= kMaxIndex ||
       (int64_t)T * E >= kMaxIndex)
     return MOE_ERROR_UNSUPPORTED;
   if (T == 0) return MOE_SUCCESS;
   if (!x || !w_gate || !logits) return MOE_ERROR_INVALID_VALUE;
+  const size_t need = moe::router_workspace_bytes(T, H, E);
+  if (need > 0 && (!ws || ws_bytes < need || !aligned256(ws))) return MOE_ERROR_WORKSPACE;
   clear_stale_error();
-  return launched(moe::launch_router_logits(x, w_gate, bias, T, H, E, logits, as_stream(stream)));
+  return launched(
+      moe::launch_router_logits(x, w_gate, bias, T, H, E, logits, ws, as_stream(stream)));
 }
 
 moe_status moe_route(const float* logits, int32_t T, int32_t E, int32_t k, int32_t* topk_ids,
@@ -236,7 +243,8 @@ moe_status moe_forward(const uint16_t* x, const float* w_gate, const float* rout
   hipStream_t s = as_stream(stream);
 
   clear_stale_error();
-  hipError_t err = moe::launch_router_logits(x, w_gate, router_bias, T, H, E, logits, s);
+  hipError_t err =
+      moe::launch_router_logits(x, w_gate, router_bias, T, H, E, logits, base + lo.router_ws, s);
   if (err == hipSuccess) err = moe::launch_route(logits, T, E, k, ids, wts, s);
   if (err == hipSuccess)
     err = moe::launch_permute(ids, T, k, E, first_expert, num_local, counts, offsets, perm, e2p,

@@ -39,9 +39,11 @@
 namespace moe {
 
 namespace {
-constexpr int KSUB = 64;          // K per wave per unit
-constexpr int KUNIT = 4 * KSUB;   // K per unit (4 waves)
-constexpr int STEPS = KSUB / 32;  // MFMA K-steps per wave per unit
+// MFMA K-steps (of 32) per wave per unit; a unit spans 4 waves.
+constexpr int UP_STEPS = 2;
+constexpr int DOWN_STEPS = 4;
+constexpr int UP_KUNIT = 4 * 32 * UP_STEPS;
+constexpr int DOWN_KUNIT = 4 * 32 * DOWN_STEPS;
 constexpr int UP_ROWS = 16;       // gate rows (and as many up rows) per up tile
 constexpr int DOWN_GROUPS = 4;    // 16-row groups per down tile
 constexpr int DOWN_ROWS = 16 * DOWN_GROUPS;
@@ -57,6 +59,19 @@ struct PlanView {
 
 __device__ __forceinline__ PlanView plan_view(int* plan, int pmax) {
   return PlanView{plan, plan + 4, plan + 4 + pmax, plan + 4 + 2 * pmax};
+}
+
+// Read-only view for the FFN kernels (the plan is written by an earlier
+// kernel), so its wave-uniform entries are fetched with scalar loads.
+struct PlanRO {
+  const int* __restrict__ hdr;
+  const int* __restrict__ expert;
+  const int* __restrict__ beg;
+  const int* __restrict__ cnt;
+};
+
+__device__ __forceinline__ PlanRO plan_ro(const int* __restrict__ plan, int pmax) {
+  return PlanRO{plan, plan + 4, plan + 4 + pmax, plan + 4 + 2 * pmax};
 }
 
 // One block of 1024 threads: list the passes (expert, first entry, entries)
@@ -91,12 +106,6 @@ __device__ __forceinline__ bf16x8 ld8(const uint16_t* p) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(p));
 }
 
-__device__ __forceinline__ bf16x8 ld8_or_zero(const uint16_t* p, bool ok) {
-  u16x8 v = {0, 0, 0, 0, 0, 0, 0, 0};
-  if (ok) v = *reinterpret_cast<const u16x8*>(p);
-  return __builtin_bit_cast(bf16x8, v);
-}
-
 // Block containing unit u when U units are cut into NB equal ranges
 // [floor(b U / NB), floor((b + 1) U / NB)).
 __device__ __forceinline__ int block_of_unit(long u, long U, int NB) {
@@ -104,17 +113,31 @@ __device__ __forceinline__ int block_of_unit(long u, long U, int NB) {
 }
 __device__ __forceinline__ long first_unit(int b, long U, int NB) { return (long)b * U / NB; }
 
-// Sum the four waves' accumulators of one tile in LDS, wave order 0..3.
-// Afterwards `red` holds the block's partial; every thread must call it.
+// Workgroups are dispatched to the 8 XCDs round-robin (block b to XCD b % 8),
+// and each XCD has its own L2. Renumber blocks so that consecutive unit
+// ranges -- the same experts, hence the same activation rows -- run on the
+// same XCD: physical block b becomes (b % 8) * (NB / 8) + b / 8.
+constexpr int kXcds = 8;
+__device__ __forceinline__ int xcd_block(int b, int NB) {
+  return NB % kXcds == 0 ? (b % kXcds) * (NB / kXcds) + b / kXcds : b;
+}
+
+// Sum the four waves' accumulators of one tile through LDS with one barrier:
+// every wave writes its own region, then wave 0 adds them in wave order
+// 0, 1, 2, 3 into `acc`. Regions alternate between two sets (`parity`), so a
+// region is rewritten only after the next tile's barrier, by which time wave 0
+// has read it. Every thread must call this.
 template <int N>
-__device__ __forceinline__ void block_reduce(f32x4 (&acc)[N], f32x4 (*red)[kWave], int wave,
-                                             int lane) {
-  for (int w = 0; w < 4; ++w) {
-    if (wave == w) {
+__device__ __forceinline__ void block_reduce(f32x4 (&acc)[N], f32x4 (*red)[4][N][kWave],
+                                             int parity, int wave, int lane) {
 #pragma unroll
-      for (int i = 0; i < N; ++i) red[i][lane] = (w == 0) ? acc[i] : red[i][lane] + acc[i];
-    }
-    __syncthreads();
+  for (int i = 0; i < N; ++i) red[parity][wave][i][lane] = acc[i];
+  __syncthreads();
+  if (wave == 0) {
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+      acc[i] = ((red[parity][0][i][lane] + red[parity][1][i][lane]) + red[parity][2][i][lane]) +
+               red[parity][3][i][lane];
   }
 }
 
@@ -148,11 +171,11 @@ __device__ bool fixup(f32x4 (&part)[N], f32x4* slots, int* counters, long tile, 
 }
 
 // ----------------------------------------------------------------- up
-template <int NTILES>
-__device__ __forceinline__ void up_mma(const bf16x8 (&ag)[STEPS], const bf16x8 (&au)[STEPS],
-                                       const bf16x8 (*bx)[STEPS], f32x4* accg, f32x4* accu) {
+template <int NTILES, int S>
+__device__ __forceinline__ void up_mma(const bf16x8 (&ag)[S], const bf16x8 (&au)[S],
+                                       const bf16x8 (*bx)[S], f32x4* accg, f32x4* accu) {
 #pragma unroll
-  for (int s = 0; s < STEPS; ++s) {
+  for (int s = 0; s < S; ++s) {
 #pragma unroll
     for (int nt = 0; nt < NTILES; ++nt) {
       accg[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ag[s], bx[nt][s], accg[nt], 0, 0, 0);
@@ -161,107 +184,138 @@ __device__ __forceinline__ void up_mma(const bf16x8 (&ag)[STEPS], const bf16x8 (
   }
 }
 
+// Operands of one K chunk for one wave (up projection).
+template <int NT, int S>
+struct UpOps {
+  bf16x8 g[S], u[S], x[NT][S];
+};
+
+template <int NT, int S>
+__device__ __forceinline__ void up_load(UpOps<NT, S>& r, const uint16_t* wg, const uint16_t* wu,
+                                        const uint16_t* x, const size_t (&xoff)[NT], size_t kb) {
+#pragma unroll
+  for (int st = 0; st < S; ++st) {
+    r.g[st] = ld8(wg + kb + 32 * st);
+    r.u[st] = ld8(wu + kb + 32 * st);
+  }
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+    for (int st = 0; st < S; ++st) r.x[nt][st] = ld8(x + xoff[nt] + kb + 32 * st);
+}
+
+template <int NT, int S>
+__device__ __forceinline__ void up_compute(const UpOps<NT, S>& r, int ntiles, f32x4* acc) {
+  switch (ntiles) {
+#define MOE_UPSK(n) \
+  case n:           \
+    if (n <= NT) up_mma<n, S>(r.g, r.u, r.x, acc, acc + NT); \
+    break;
+    MOE_UPSK(1) MOE_UPSK(2) MOE_UPSK(3) MOE_UPSK(4) MOE_UPSK(5) MOE_UPSK(6) MOE_UPSK(7) MOE_UPSK(8)
+#undef MOE_UPSK
+  }
+}
+
+// Per-tile state of the up projection, in two stages: `issue` loads the plan
+// entries and the permutation rows of a tile early (one tile ahead); `finish`
+// turns them into addresses when the tile is reached, so those loads never
+// stall the weight stream.
 template <int NT>
+struct UpRaw {
+  int g, ex, tb, tc;
+  int r[NT];
+};
+template <int NT>
+struct UpTile {
+  int g, tb, tc, ntiles;
+  size_t wrow;       // lane's gate row (+ its K offset) in W1
+  size_t xoff[NT];   // lane's token row (+ its K offset) in x, per N-tile
+};
+
+template <int NT>
+__device__ __forceinline__ void up_issue(UpRaw<NT>& raw, long tile, long G, const PlanRO& pv,
+                                         const int* perm, int lane) {
+  const int pass = (int)(tile / G);
+  raw.g = (int)(tile % G);
+  raw.ex = pv.expert[pass];
+  raw.tb = pv.beg[pass];
+  raw.tc = pv.cnt[pass];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int n = nt * 16 + (lane & 15);
+    raw.r[nt] = perm[raw.tb + (n < raw.tc ? n : 0)];
+  }
+}
+
+// Token slots past the pass's entries read a valid row (the first entry's):
+// MFMA output column n depends only on B column n and those columns are never
+// stored, so every load of the main loop is unconditional.
+template <int NT>
+__device__ __forceinline__ void up_finish(UpTile<NT>& st, const UpRaw<NT>& raw, int k, int H,
+                                          int I, int nmax, int lane, int kq) {
+  st.g = raw.g;
+  st.tb = raw.tb;
+  st.tc = raw.tc;
+  st.ntiles = (raw.tc + 15) >> 4;
+  st.wrow = ((size_t)raw.ex * 2 * I + raw.g * UP_ROWS + (lane & 15)) * H + kq;
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int r = (raw.r[nt] >= 0 && raw.r[nt] < nmax) ? raw.r[nt] : 0;
+    st.xoff[nt] = (size_t)(r / k) * H + kq;
+  }
+}
+
+template <int NT, int S>
 __global__ __launch_bounds__(256) void ffn_up_sk_kernel(
     const uint16_t* __restrict__ x, const int* __restrict__ perm, int k, int H, int I, int nmax,
-    const uint16_t* __restrict__ w1, int* plan, int pmax, f32x4* slots, int* counters,
-    uint16_t* __restrict__ h_hi, uint16_t* __restrict__ h_lo, int NB) {
-  __shared__ f32x4 red[2 * NT][kWave];
-  const PlanView pv = plan_view(plan, pmax);
+    const uint16_t* __restrict__ w1, const int* __restrict__ plan, int pmax, f32x4* slots,
+    int* counters, uint16_t* __restrict__ h_hi, uint16_t* __restrict__ h_lo, int NB) {
+  constexpr int KUNIT = 4 * 32 * S;
+  __shared__ f32x4 red[2][4][2 * NT][kWave];
+  const PlanRO pv = plan_ro(plan, pmax);
   const long P = pv.hdr[0];
   const long G = I / UP_ROWS, C = H / KUNIT;
   const long U = P * G * C;
   const int nb = (int)min((long)NB, U);
-  const int b = blockIdx.x;
+  const int b = xcd_block(blockIdx.x, NB);
   if (b >= nb) return;
   const long s = first_unit(b, U, nb), e = first_unit(b + 1, U, nb);
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-  const int kq = (lane >> 4) * 8 + wave * KSUB;
-  for (long u = s; u < e;) {
+  const int kq = (lane >> 4) * 8 + wave * 32 * S;
+  const size_t I_H = (size_t)I * H;
+  const long last_tile = (e - 1) / C;
+
+  UpTile<NT> ts, tn;
+  UpRaw<NT> rn;
+  {
+    UpRaw<NT> r0;
+    up_issue(r0, s / C, G, pv, perm, lane);
+    up_finish(ts, r0, k, H, I, nmax, lane, kq);
+  }
+  up_issue(rn, min(s / C + 1, last_tile), G, pv, perm, lane);
+
+  f32x4 acc[2 * NT];
+#pragma unroll
+  for (int i = 0; i < 2 * NT; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // End of the tile of unit u: add the waves' partials, complete the tile
+  // (directly, or through the cross-block fixup) and write a = silu(g) * u.
+  int parity = 0;
+  auto tile_end = [&](long u) {
     const long tile = u / C;
-    const int c0 = (int)(u % C);
-    const int c1 = (int)min(C, c0 + (e - u));
-    const int pass = (int)(tile / G), g = (int)(tile % G);
-    const int ex = pv.expert[pass], tb = pv.beg[pass], tc = pv.cnt[pass];
-    const int ntiles = (tc + 15) >> 4;
-    size_t xoff[NT];
-    bool xok[NT];
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      const int n = nt * 16 + (lane & 15);
-      int tok = -1;
-      if (n < tc) {
-        const int r = perm[tb + n];
-        if (r >= 0 && r < nmax) tok = r / k;
-      }
-      xok[nt] = tok >= 0 && nt < ntiles;
-      xoff[nt] = (size_t)(tok >= 0 ? tok : 0) * H + kq;
-    }
-    const uint16_t* wg = w1 + ((size_t)ex * 2 * I + g * UP_ROWS + (lane & 15)) * H + kq;
-    const uint16_t* wu = wg + (size_t)I * H;
-    f32x4 acc[2 * NT];
-#pragma unroll
-    for (int i = 0; i < 2 * NT; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // operands of chunk c (cur) and c + 1 (next): the loads for c + 1 are in
-    // flight while chunk c is multiplied
-    bf16x8 ag[STEPS], au[STEPS], bx[NT][STEPS];
-    {
-      const size_t kb = (size_t)c0 * KUNIT;
-#pragma unroll
-      for (int st = 0; st < STEPS; ++st) {
-        ag[st] = ld8(wg + kb + 32 * st);
-        au[st] = ld8(wu + kb + 32 * st);
-      }
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-        for (int st = 0; st < STEPS; ++st) bx[nt][st] = ld8_or_zero(x + xoff[nt] + kb + 32 * st, xok[nt]);
-    }
-    for (int c = c0; c < c1; ++c) {
-      bf16x8 ng[STEPS], nu[STEPS], nx[NT][STEPS];
-      if (c + 1 < c1) {
-        const size_t kb = (size_t)(c + 1) * KUNIT;
-#pragma unroll
-        for (int st = 0; st < STEPS; ++st) {
-          ng[st] = ld8(wg + kb + 32 * st);
-          nu[st] = ld8(wu + kb + 32 * st);
-        }
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-          for (int st = 0; st < STEPS; ++st)
-            nx[nt][st] = ld8_or_zero(x + xoff[nt] + kb + 32 * st, xok[nt]);
-      }
-      switch (ntiles) {
-#define MOE_UPSK(n) \
-  case n:           \
-    if (n <= NT) up_mma<n>(ag, au, bx, acc, acc + NT); \
-    break;
-        MOE_UPSK(1) MOE_UPSK(2) MOE_UPSK(3) MOE_UPSK(4) MOE_UPSK(5) MOE_UPSK(6) MOE_UPSK(7)
-        MOE_UPSK(8)
-#undef MOE_UPSK
-      }
-#pragma unroll
-      for (int st = 0; st < STEPS; ++st) {
-        ag[st] = ng[st];
-        au[st] = nu[st];
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) bx[nt][st] = nx[nt][st];
-      }
-    }
-    block_reduce(acc, red, wave, lane);
+    block_reduce(acc, red, parity, wave, lane);
+    parity ^= 1;
     if (wave == 0) {
+      const bool split = tile * C < s || tile * C + C > e;
       bool done = true;
-#pragma unroll
-      for (int i = 0; i < 2 * NT; ++i) acc[i] = red[i][lane];
-      if (!(c0 == 0 && c1 == C)) done = fixup(acc, slots, counters, tile, C, U, nb, b, lane);
+      if (split) done = fixup(acc, slots, counters, tile, C, U, nb, b, lane);
       if (done) {
         // lane l: rows g*16 + 4*(l/16) + j of token slot l % 16 of each N-tile
-        const int ir = g * UP_ROWS + (lane >> 4) * 4;
+        const int ir = ts.g * UP_ROWS + (lane >> 4) * 4;
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
           const int n = nt * 16 + (lane & 15);
-          if (n >= tc) continue;
+          if (n >= ts.tc) continue;
           typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
           u16x4 hi, lo;
 #pragma unroll
@@ -271,24 +325,51 @@ __global__ __launch_bounds__(256) void ffn_up_sk_kernel(
             hi[j] = f32_to_bf16_bits(a);
             lo[j] = f32_to_bf16_bits(a - bf16_bits_to_f32(hi[j]));
           }
-          const size_t o = (size_t)(tb + n) * I + ir;
+          const size_t o = (size_t)(ts.tb + n) * I + ir;
           *reinterpret_cast<u16x4*>(h_hi + o) = hi;
           *reinterpret_cast<u16x4*>(h_lo + o) = lo;
         }
       }
     }
-    __syncthreads();  // red is reused by the next tile
-    u += c1 - c0;
+#pragma unroll
+    for (int i = 0; i < 2 * NT; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  };
+
+  // One unit: start the loads of unit u + 1 (in the next tile when u ends
+  // one), multiply unit u, and finish its tile when u is the tile's last unit
+  // in this block. Returns false after the block's last unit.
+  auto step = [&](UpOps<NT, S>& cur, UpOps<NT, S>& nxt, long& u) -> bool {
+    const long un = u + 1 < e ? u + 1 : u;  // past the end: reload u (unused)
+    const bool crosses = un != u && un % C == 0;
+    if (crosses) {
+      up_finish(tn, rn, k, H, I, nmax, lane, kq);
+      up_issue(rn, min(un / C + 1, last_tile), G, pv, perm, lane);  // the tile after
+    } else {
+      tn = ts;
+    }
+    const size_t kb = (size_t)(un % C) * KUNIT;
+    up_load(nxt, w1 + tn.wrow, w1 + tn.wrow + I_H, x, tn.xoff, kb);
+    up_compute<NT, S>(cur, ts.ntiles, acc);
+    if (u % C == C - 1 || u == e - 1) tile_end(u);
+    if (u + 1 >= e) return false;
+    ts = tn;
+    u = un;
+    return true;
+  };
+
+  UpOps<NT, S> b0, b1;
+  up_load(b0, w1 + ts.wrow, w1 + ts.wrow + I_H, x, ts.xoff, (size_t)(s % C) * KUNIT);
+  long u = s;
+  while (step(b0, b1, u) && step(b1, b0, u)) {
   }
 }
 
 // --------------------------------------------------------------- down
-template <int NTILES>
-__device__ __forceinline__ void down_mma(const bf16x8 (&a)[DOWN_GROUPS][STEPS],
-                                         const bf16x8 (*bh)[STEPS], const bf16x8 (*bl)[STEPS],
-                                         f32x4* acc) {
+template <int NTILES, int S>
+__device__ __forceinline__ void down_mma(const bf16x8 (&a)[DOWN_GROUPS][S], const bf16x8 (*bh)[S],
+                                         const bf16x8 (*bl)[S], f32x4* acc) {
 #pragma unroll
-  for (int st = 0; st < STEPS; ++st) {
+  for (int st = 0; st < S; ++st) {
 #pragma unroll
     for (int nt = 0; nt < NTILES; ++nt) {
 #pragma unroll
@@ -301,114 +382,156 @@ __device__ __forceinline__ void down_mma(const bf16x8 (&a)[DOWN_GROUPS][STEPS],
   }
 }
 
+// Operands of one K chunk for one wave (down projection).
+template <int NT, int S>
+struct DownOps {
+  bf16x8 a[DOWN_GROUPS][S], h[NT][S], l[NT][S];
+};
+
+template <int NT, int S>
+__device__ __forceinline__ void down_load(DownOps<NT, S>& r, const uint16_t* w, int I,
+                                          const uint16_t* h_hi, const uint16_t* h_lo,
+                                          const size_t (&hrow)[NT], size_t kb) {
+#pragma unroll
+  for (int rg = 0; rg < DOWN_GROUPS; ++rg)
+#pragma unroll
+    for (int st = 0; st < S; ++st) r.a[rg][st] = ld8(w + (size_t)rg * 16 * I + kb + 32 * st);
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+    for (int st = 0; st < S; ++st) {
+      r.h[nt][st] = ld8(h_hi + hrow[nt] + kb + 32 * st);
+      r.l[nt][st] = ld8(h_lo + hrow[nt] + kb + 32 * st);
+    }
+}
+
+template <int NT, int S>
+__device__ __forceinline__ void down_compute(const DownOps<NT, S>& r, int ntiles, f32x4* acc) {
+  switch (ntiles) {
+#define MOE_DNSK(n) \
+  case n:           \
+    if (n <= NT) down_mma<n, S>(r.a, r.h, r.l, acc); \
+    break;
+    MOE_DNSK(1) MOE_DNSK(2) MOE_DNSK(3) MOE_DNSK(4) MOE_DNSK(5) MOE_DNSK(6) MOE_DNSK(7) MOE_DNSK(8)
+#undef MOE_DNSK
+  }
+}
+
+// Per-tile state of the down projection (plan entries loaded a tile ahead).
+struct DownRaw {
+  int g, ex, tb, tc;
+};
 template <int NT>
+struct DownTile {
+  int g, tb, tc, ntiles;
+  size_t wrow;       // lane's first W2 row (+ its K offset)
+  size_t hrow[NT];   // lane's row of h (+ its K offset), per N-tile
+};
+
+__device__ __forceinline__ void down_issue(DownRaw& raw, long tile, long G, const PlanRO& pv) {
+  const int pass = (int)(tile / G);
+  raw.g = (int)(tile % G);
+  raw.ex = pv.expert[pass];
+  raw.tb = pv.beg[pass];
+  raw.tc = pv.cnt[pass];
+}
+
+template <int NT>
+__device__ __forceinline__ void down_finish(DownTile<NT>& st, const DownRaw& raw, int H, int I,
+                                            int lane, int kq) {
+  st.g = raw.g;
+  st.tb = raw.tb;
+  st.tc = raw.tc;
+  st.ntiles = (raw.tc + 15) >> 4;
+  st.wrow = ((size_t)raw.ex * H + raw.g * DOWN_ROWS + (lane & 15)) * I + kq;
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int n = nt * 16 + (lane & 15);  // slots past the entries read the first entry's row
+    st.hrow[nt] = (size_t)(raw.tb + (n < raw.tc ? n : 0)) * I + kq;
+  }
+}
+
+template <int NT, int S>
 __global__ __launch_bounds__(256) void ffn_down_sk_kernel(
     const uint16_t* __restrict__ h_hi, const uint16_t* __restrict__ h_lo, int H, int I,
-    const uint16_t* __restrict__ w2, int* plan, int pmax, f32x4* slots, int* counters,
-    float* __restrict__ out, int NB) {
+    const uint16_t* __restrict__ w2, const int* __restrict__ plan, int pmax, f32x4* slots,
+    int* counters, float* __restrict__ out, int NB) {
+  constexpr int KUNIT = 4 * 32 * S;
   constexpr int NACC = NT * DOWN_GROUPS;
-  __shared__ f32x4 red[NACC][kWave];
-  const PlanView pv = plan_view(plan, pmax);
+  __shared__ f32x4 red[2][4][NACC][kWave];
+  const PlanRO pv = plan_ro(plan, pmax);
   const long P = pv.hdr[0];
   const long G = H / DOWN_ROWS, C = I / KUNIT;
   const long U = P * G * C;
   const int nb = (int)min((long)NB, U);
-  const int b = blockIdx.x;
+  const int b = xcd_block(blockIdx.x, NB);
   if (b >= nb) return;
   const long s = first_unit(b, U, nb), e = first_unit(b + 1, U, nb);
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-  const int kq = (lane >> 4) * 8 + wave * KSUB;
-  for (long u = s; u < e;) {
+  const int kq = (lane >> 4) * 8 + wave * 32 * S;
+  const long last_tile = (e - 1) / C;
+
+  DownTile<NT> ts, tn;
+  DownRaw rn;
+  {
+    DownRaw r0;
+    down_issue(r0, s / C, G, pv);
+    down_finish(ts, r0, H, I, lane, kq);
+  }
+  down_issue(rn, min(s / C + 1, last_tile), G, pv);
+
+  f32x4 acc[NACC];
+#pragma unroll
+  for (int i = 0; i < NACC; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  int parity = 0;
+  auto tile_end = [&](long u) {
     const long tile = u / C;
-    const int c0 = (int)(u % C);
-    const int c1 = (int)min(C, c0 + (e - u));
-    const int pass = (int)(tile / G), g = (int)(tile % G);
-    const int ex = pv.expert[pass], tb = pv.beg[pass], tc = pv.cnt[pass];
-    const int ntiles = (tc + 15) >> 4;
-    const uint16_t* w = w2 + ((size_t)ex * H + g * DOWN_ROWS + (lane & 15)) * I + kq;
-    size_t hrow[NT];
-    bool hok[NT];
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      const int n = nt * 16 + (lane & 15);
-      hok[nt] = n < tc && nt < ntiles;
-      hrow[nt] = (size_t)(tb + (n < tc ? n : 0)) * I + kq;
-    }
-    f32x4 acc[NACC];
-#pragma unroll
-    for (int i = 0; i < NACC; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-    bf16x8 a[DOWN_GROUPS][STEPS], bh[NT][STEPS], bl[NT][STEPS];
-    {
-      const size_t kb = (size_t)c0 * KUNIT;
-#pragma unroll
-      for (int rg = 0; rg < DOWN_GROUPS; ++rg)
-#pragma unroll
-        for (int st = 0; st < STEPS; ++st) a[rg][st] = ld8(w + (size_t)rg * 16 * I + kb + 32 * st);
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-        for (int st = 0; st < STEPS; ++st) {
-          bh[nt][st] = ld8_or_zero(h_hi + hrow[nt] + kb + 32 * st, hok[nt]);
-          bl[nt][st] = ld8_or_zero(h_lo + hrow[nt] + kb + 32 * st, hok[nt]);
-        }
-    }
-    for (int c = c0; c < c1; ++c) {
-      bf16x8 na[DOWN_GROUPS][STEPS], nh[NT][STEPS], nl[NT][STEPS];
-      if (c + 1 < c1) {
-        const size_t kb = (size_t)(c + 1) * KUNIT;
-#pragma unroll
-        for (int rg = 0; rg < DOWN_GROUPS; ++rg)
-#pragma unroll
-          for (int st = 0; st < STEPS; ++st)
-            na[rg][st] = ld8(w + (size_t)rg * 16 * I + kb + 32 * st);
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-          for (int st = 0; st < STEPS; ++st) {
-            nh[nt][st] = ld8_or_zero(h_hi + hrow[nt] + kb + 32 * st, hok[nt]);
-            nl[nt][st] = ld8_or_zero(h_lo + hrow[nt] + kb + 32 * st, hok[nt]);
-          }
-      }
-      switch (ntiles) {
-#define MOE_DNSK(n) \
-  case n:           \
-    if (n <= NT) down_mma<n>(a, bh, bl, acc); \
-    break;
-        MOE_DNSK(1) MOE_DNSK(2) MOE_DNSK(3) MOE_DNSK(4) MOE_DNSK(5) MOE_DNSK(6) MOE_DNSK(7)
-        MOE_DNSK(8)
-#undef MOE_DNSK
-      }
-#pragma unroll
-      for (int st = 0; st < STEPS; ++st) {
-#pragma unroll
-        for (int rg = 0; rg < DOWN_GROUPS; ++rg) a[rg][st] = na[rg][st];
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          bh[nt][st] = nh[nt][st];
-          bl[nt][st] = nl[nt][st];
-        }
-      }
-    }
-    block_reduce(acc, red, wave, lane);
+    block_reduce(acc, red, parity, wave, lane);
+    parity ^= 1;
     if (wave == 0) {
+      const bool split = tile * C < s || tile * C + C > e;
       bool done = true;
-#pragma unroll
-      for (int i = 0; i < NACC; ++i) acc[i] = red[i][lane];
-      if (!(c0 == 0 && c1 == C)) done = fixup(acc, slots, counters, tile, C, U, nb, b, lane);
+      if (split) done = fixup(acc, slots, counters, tile, C, U, nb, b, lane);
       if (done) {
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
           const int n = nt * 16 + (lane & 15);
-          if (n >= tc) continue;
-          float* o = out + (size_t)(tb + n) * H + g * DOWN_ROWS + (lane >> 4) * 4;
+          if (n >= ts.tc) continue;
+          float* o = out + (size_t)(ts.tb + n) * H + ts.g * DOWN_ROWS + (lane >> 4) * 4;
 #pragma unroll
           for (int rg = 0; rg < DOWN_GROUPS; ++rg)
             *reinterpret_cast<f32x4*>(o + rg * 16) = acc[nt * DOWN_GROUPS + rg];
         }
       }
     }
-    __syncthreads();
-    u += c1 - c0;
+#pragma unroll
+    for (int i = 0; i < NACC; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  };
+
+  auto step = [&](DownOps<NT, S>& cur, DownOps<NT, S>& nxt, long& u) -> bool {
+    const long un = u + 1 < e ? u + 1 : u;
+    const bool crosses = un != u && un % C == 0;
+    if (crosses) {
+      down_finish(tn, rn, H, I, lane, kq);
+      down_issue(rn, min(un / C + 1, last_tile), G, pv);  // the tile after
+    } else {
+      tn = ts;
+    }
+    const size_t kb = (size_t)(un % C) * KUNIT;
+    down_load(nxt, w2 + tn.wrow, I, h_hi, h_lo, tn.hrow, kb);
+    down_compute<NT, S>(cur, ts.ntiles, acc);
+    if (u % C == C - 1 || u == e - 1) tile_end(u);
+    if (u + 1 >= e) return false;
+    ts = tn;
+    u = un;
+    return true;
+  };
+
+  DownOps<NT, S> b0, b1;
+  down_load(b0, w2 + ts.wrow, I, h_hi, h_lo, ts.hrow, (size_t)(s % C) * KUNIT);
+  long u = s;
+  while (step(b0, b1, u) && step(b1, b0, u)) {
   }
 }
 
@@ -489,13 +612,13 @@ hipError_t launch_sk_nt(const uint16_t* x, const int* perm, const int* offsets, 
                      offsets, L, nmax, NT * 16, plan, lo.pmax, counters, lo.ncounters);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  const int nb_up = resident_blocks(ffn_up_sk_kernel<NT>);
-  hipLaunchKernelGGL(ffn_up_sk_kernel<NT>, dim3(nb_up), dim3(256), 0, stream, x, perm, k, H, I,
+  const int nb_up = resident_blocks(ffn_up_sk_kernel<NT, UP_STEPS>);
+  hipLaunchKernelGGL((ffn_up_sk_kernel<NT, UP_STEPS>), dim3(nb_up), dim3(256), 0, stream, x, perm, k, H, I,
                      nmax, w1, plan, lo.pmax, slots, counters, h_hi, h_lo, nb_up);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
-  const int nb_down = resident_blocks(ffn_down_sk_kernel<NT>);
-  hipLaunchKernelGGL(ffn_down_sk_kernel<NT>, dim3(nb_down), dim3(256), 0, stream, h_hi, h_lo, H,
+  const int nb_down = resident_blocks(ffn_down_sk_kernel<NT, DOWN_STEPS>);
+  hipLaunchKernelGGL((ffn_down_sk_kernel<NT, DOWN_STEPS>), dim3(nb_down), dim3(256), 0, stream, h_hi, h_lo, H,
                      I, w2, plan, lo.pmax, slots, counters + max_blocks(), out, nb_down);
   return hipGetLastError();
 }
@@ -504,7 +627,8 @@ hipError_t launch_sk_nt(const uint16_t* x, const int* perm, const int* offsets, 
 bool ffn_sk_applies(const void* x, const void* w1, const void* w2, int T, int k, int L, int H,
                     int I) {
   auto al = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
-  return al(x) && al(w1) && al(w2) && H % KUNIT == 0 && I % KUNIT == 0 && pick_nt(T, k, L) > 0;
+  return al(x) && al(w1) && al(w2) && H % UP_KUNIT == 0 && I % DOWN_KUNIT == 0 &&
+         I % UP_ROWS == 0 && H % DOWN_ROWS == 0 && pick_nt(T, k, L) > 0;
 }
 
 size_t ffn_sk_workspace_bytes(int T, int k, int L) {

@@ -10,71 +10,123 @@
 //  - few tokens (decode): one block per (token, 8 experts); the 256 threads
 //    split H, each keeps 8 fp64 partial sums, and the block adds them up in a
 //    fixed order (butterfly within a wave, then wave 0..3);
-//  - many tokens: VALU fp64 GEMM tiled through LDS, 64 tokens x 64 experts
-//    per 256-thread block, each thread a 4 x 4 register tile.
+//  - many tokens: fp64 MFMA GEMM, split over K into slices whose fp64 partial
+//    sums a second kernel adds in slice order.
 #include "device.h"
+
+#include <algorithm>
 
 namespace moe {
 
 namespace {
-constexpr int RT = 64;  // tokens per block
-constexpr int RE = 64;  // experts per block
-constexpr int RK = 32;  // K chunk
+// ---- many tokens: fp64 MFMA (v_mfma_f64_16x16x4f64) ----------------------
+// Block tile 64 tokens x 64 experts, 4 waves of 32 x 32 (2 x 2 MFMA tiles),
+// K staged through LDS in chunks of 32 as fp64 (k-major, so each 16-lane
+// group of a fragment read is one contiguous 128-byte row). The K range is
+// split over blockIdx.z; each slice writes fp64 partial sums, which a second
+// kernel adds in slice order (then the bias) and rounds to fp32 once.
+// fp64 MFMA layouts: A lane l = A[l % 16][l / 16], B lane l = B[l / 16][l % 16],
+// D lane l, register r = D[l / 16 + 4 r][l % 16].
+constexpr int MT = 64, MN = 64, MK = 32;
+typedef double f64x4 __attribute__((ext_vector_type(4)));
 
-template <bool HAS_BIAS>
-__global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __restrict__ x,
-                                                            const float* __restrict__ wg,
-                                                            const float* __restrict__ bias, int T,
-                                                            int H, int E,
-                                                            float* __restrict__ logits) {
-  __shared__ double xs[RK][RT + 2];
-  __shared__ double ws[RK][RE + 2];
-  const int t0 = blockIdx.x * RT, e0 = blockIdx.y * RE;
-  const int tx = threadIdx.x % 16, ty = threadIdx.x / 16;
-  double acc[4][4];
+template <bool VEC>
+__global__ __launch_bounds__(256) void router_mfma_kernel(const uint16_t* __restrict__ x,
+                                                          const float* __restrict__ wg, int T,
+                                                          int H, int E, int kslice,
+                                                          double* __restrict__ part) {
+  __shared__ double xs[MK][MT];
+  __shared__ double ws[MK][MN];
+  const int t0 = blockIdx.x * MT, e0 = blockIdx.y * MN;
+  const int kb0 = blockIdx.z * kslice, kb1 = min(H, kb0 + kslice);
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int wm = wave & 1, wn = wave >> 1;
+  // staging: thread -> (row, 8 consecutive k)
+  const int srow = tid >> 2, sk = (tid & 3) * 8;
+  f64x4 acc[2][2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = 0.0;
-
-  for (int h0 = 0; h0 < H; h0 += RK) {
-    // Stage x[t0:t0+64, h0:h0+32] and w_gate[e0:e0+64, h0:h0+32] as fp64.
-    for (int q = threadIdx.x; q < RT * RK; q += 256) {
-      const int r = q / RK, c = q % RK;
-      const int t = t0 + r, h = h0 + c;
-      xs[c][r] = (t < T && h < H) ? (double)bf16_bits_to_f32(x[(size_t)t * H + h]) : 0.0;
-      const int e = e0 + r;
-      ws[c][r] = (e < E && h < H) ? (double)wg[(size_t)e * H + h] : 0.0;
+    for (int j = 0; j < 2; ++j) acc[i][j] = f64x4{0.0, 0.0, 0.0, 0.0};
+  for (int k0 = kb0; k0 < kb1; k0 += MK) {
+    {
+      const int t = t0 + srow, e = e0 + srow, kk = k0 + sk;
+      double xv[8], wv[8];
+      if (VEC && kk + 8 <= kb1) {
+        u16x8 xr = {0, 0, 0, 0, 0, 0, 0, 0};
+        f32x4 w0 = {0.f, 0.f, 0.f, 0.f}, w1 = w0;
+        if (t < T) xr = *reinterpret_cast<const u16x8*>(x + (size_t)t * H + kk);
+        if (e < E) {
+          w0 = *reinterpret_cast<const f32x4*>(wg + (size_t)e * H + kk);
+          w1 = *reinterpret_cast<const f32x4*>(wg + (size_t)e * H + kk + 4);
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) xv[j] = bf16_bits_to_f32(xr[j]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          wv[j] = w0[j];
+          wv[4 + j] = w1[j];
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const bool ok = kk + j < kb1;
+          xv[j] = (ok && t < T) ? (double)bf16_bits_to_f32(x[(size_t)t * H + kk + j]) : 0.0;
+          wv[j] = (ok && e < E) ? (double)wg[(size_t)e * H + kk + j] : 0.0;
+        }
+      }
+      __syncthreads();  // the previous chunk's fragments have been read
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        xs[sk + j][srow] = xv[j];
+        ws[sk + j][srow] = wv[j];
+      }
+      __syncthreads();
     }
-    __syncthreads();
-#pragma unroll 8
-    for (int c = 0; c < RK; ++c) {
-      double a[4], b[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) a[i] = xs[c][ty * 4 + i];
+    for (int s4 = 0; s4 < MK / 4; ++s4) {
+      const int kr = s4 * 4 + (lane >> 4);
+      double a[2], b[2];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) b[j] = ws[c][tx * 4 + j];
+      for (int i = 0; i < 2; ++i) a[i] = xs[kr][wm * 32 + i * 16 + (lane & 15)];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int j = 0; j < 2; ++j) b[j] = ws[kr][wn * 32 + j * 16 + (lane & 15)];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = fma(a[i], b[j], acc[i][j]);
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[i], b[j], acc[i][j], 0, 0, 0);
     }
-    __syncthreads();
   }
+  double* out = part + (size_t)blockIdx.z * T * E;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int t = t0 + ty * 4 + i;
-    if (t >= T) continue;
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int e = e0 + tx * 4 + j;
-      if (e >= E) continue;
-      double v = acc[i][j];
-      if (HAS_BIAS) v += (double)bias[e];
-      logits[(size_t)t * E + e] = (float)v;
+    for (int j = 0; j < 2; ++j) {
+      const int e = e0 + wn * 32 + j * 16 + (lane & 15);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = t0 + wm * 32 + i * 16 + (lane >> 4) + 4 * r;
+        if (t < T && e < E) out[(size_t)t * E + e] = acc[i][j][r];
+      }
     }
+}
+
+// logits = fp32(sum over slices in order + bias)
+template <bool HAS_BIAS>
+__global__ __launch_bounds__(256) void router_reduce_kernel(const double* __restrict__ part,
+                                                            const float* __restrict__ bias,
+                                                            int T, int E, int nslices,
+                                                            float* __restrict__ logits) {
+  const size_t n = (size_t)T * E;
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) {
+    double v = part[i];
+    for (int z = 1; z < nslices; ++z) v += part[(size_t)z * n + i];
+    if (HAS_BIAS) v += (double)bias[i % E];
+    logits[i] = (float)v;
   }
 }
+
 constexpr int SE = 8;  // experts per block in the few-token kernel
 
 template <bool HAS_BIAS, bool VEC>
@@ -136,8 +188,31 @@ __global__ __launch_bounds__(256) void router_rows_kernel(const uint16_t* __rest
 // Up to this many tokens the few-token kernel runs.
 constexpr int kRowsMaxTokens = 64;
 
+namespace {
+// K slices for the many-token kernel: enough blocks to cover the GPU about four
+// times, each slice at least 256 wide and a multiple of the 32-wide chunk.
+int router_slices(int T, int H, int E, int* kslice) {
+  const long tiles = (long)((T + MT - 1) / MT) * ((E + MN - 1) / MN);
+  long want = (1024 + tiles - 1) / tiles;
+  const long most = (H + 255) / 256;
+  if (want > most) want = most;
+  if (want < 1) want = 1;
+  int ks = (int)((H + want - 1) / want);
+  ks = (ks + MK - 1) / MK * MK;
+  *kslice = ks;
+  return (H + ks - 1) / ks;
+}
+}  // namespace
+
+size_t router_workspace_bytes(int T, int H, int E) {
+  if (T <= kRowsMaxTokens) return 0;
+  int ks = 0;
+  const int z = router_slices(T, H, E, &ks);
+  return (size_t)z * T * E * sizeof(double);
+}
+
 hipError_t launch_router_logits(const uint16_t* x, const float* wg, const float* bias, int T, int H,
-                                int E, float* logits, hipStream_t stream) {
+                                int E, float* logits, void* ws, hipStream_t stream) {
   if (T <= kRowsMaxTokens) {
     const bool vec = H % 4 == 0 && (reinterpret_cast<uintptr_t>(x) & 7u) == 0 &&
                      (reinterpret_cast<uintptr_t>(wg) & 15u) == 0;
@@ -159,13 +234,28 @@ hipError_t launch_router_logits(const uint16_t* x, const float* wg, const float*
     }
     return hipGetLastError();
   }
-  dim3 grid((T + RT - 1) / RT, (E + RE - 1) / RE);
-  if (bias)
-    hipLaunchKernelGGL(router_logits_kernel<true>, grid, dim3(256), 0, stream, x, wg, bias, T, H, E,
-                       logits);
+  int ks = 0;
+  const int z = router_slices(T, H, E, &ks);
+  double* part = static_cast<double*>(ws);
+  const bool vec = H % 8 == 0 && (reinterpret_cast<uintptr_t>(x) & 15u) == 0 &&
+                   (reinterpret_cast<uintptr_t>(wg) & 15u) == 0;
+  dim3 grid((T + MT - 1) / MT, (E + MN - 1) / MN, z);
+  if (vec)
+    hipLaunchKernelGGL(router_mfma_kernel<true>, grid, dim3(256), 0, stream, x, wg, T, H, E, ks,
+                       part);
   else
-    hipLaunchKernelGGL(router_logits_kernel<false>, grid, dim3(256), 0, stream, x, wg, bias, T, H,
-                       E, logits);
+    hipLaunchKernelGGL(router_mfma_kernel<false>, grid, dim3(256), 0, stream, x, wg, T, H, E, ks,
+                       part);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  const size_t n = (size_t)T * E;
+  const int blocks = (int)std::min<size_t>((n + 255) / 256, 4096);
+  if (bias)
+    hipLaunchKernelGGL(router_reduce_kernel<true>, dim3(blocks), dim3(256), 0, stream, part, bias,
+                       T, E, z, logits);
+  else
+    hipLaunchKernelGGL(router_reduce_kernel<false>, dim3(blocks), dim3(256), 0, stream, part, bias,
+                       T, E, z, logits);
   return hipGetLastError();
 }
 

@@ -104,4 +104,5 @@ def test_calls_reject_bad_arguments_without_launching():
                          None, FAKE, 256, None) == 3
     assert L.moe_forward(FAKE, FAKE, None, FAKE, FAKE, 4, 64, 64, 8, 2, 0, 8, None, None, None,
                          None, FAKE, 1 << 30, None) == 1
-    assert L.moe_router_logits(FAKE, FAKE, None, 4, 0, 8, FAKE, None) == 1
+    assert L.moe_router_logits(FAKE, FAKE, None, 4, 0, 8, FAKE, None, 0, None) == 1
+    assert L.moe_router_logits(FAKE, FAKE, None, 100, 64, 8, FAKE, None, 0, None) == 3

@@ -20,8 +20,11 @@ pytestmark = pytest.mark.gpu
 
 def gpu_logits(x, wg, bias):
     t = torch()
-    lg = empty((x.shape[0], wg.shape[0]), t.float32)
-    moe.router_logits(dev(x), dev(wg), None if bias is None else dev(bias), lg)
+    T, H = x.shape
+    E = wg.shape[0]
+    lg = empty((T, E), t.float32)
+    ws = moe.alloc_workspace(T, H, 128, E, 1, 1)
+    moe.router_logits(dev(x), dev(wg), None if bias is None else dev(bias), lg, ws)
     sync()
     return host(lg)
 
@@ -69,3 +72,12 @@ def test_router_few_tokens(T, H, E):
     b = synth.normal_f32(6, 95, (E,), 1.0)
     check(x, wg, b, "few tokens")
     check(x, wg, None, "few tokens, no bias")
+
+
+@pytest.mark.parametrize("T,H,E", [(300, 1024, 100), (65, 7168, 256), (129, 200, 64)])
+def test_router_many_tokens(T, H, E):
+    """The fp64 MFMA kernel (T > 64): split K slices, partial tiles in T and E."""
+    x = synth.normal_bf16(8, 96, (T, H), 1.0)
+    wg = synth.normal_f32(8, 97, (E, H), 0.1)
+    b = synth.normal_f32(8, 98, (E,), 1.0)
+    check(x, wg, b, "many tokens")
