@@ -141,28 +141,31 @@ __device__ __forceinline__ void block_reduce(f32x4 (&acc)[N], f32x4 (*red)[4][N]
   }
 }
 
-// Cross-block fixup of a tile cut between blocks. Wave 0 stores the block's
-// partial (`part`, N f32x4 per lane) into its slot, then the last block to
+// Cross-block fixup of a tile cut between blocks, for one wave's share of it
+// (`sub` of `SUBS` independent parts). The wave stores its block's partial
+// (`part`, N f32x4 per lane) into its slot, then the wave of the last block to
 // arrive adds all slots in block order into `part` and returns true.
-template <int N>
+// A block holds at most two cut tiles (its first and its last): slot 2b for
+// the first, 2b + 1 for the last.
+template <int N, int SUBS = 1>
 __device__ bool fixup(f32x4 (&part)[N], f32x4* slots, int* counters, long tile, long C, long U,
-                      int NB, int b, int lane) {
+                      int NB, int b, int lane, int sub = 0) {
   const long t0 = tile * C;
   const int bf = block_of_unit(t0, U, NB), bl = block_of_unit(t0 + C - 1, U, NB);
-  const int my_slot = 2 * b + (first_unit(b, U, NB) < t0 ? 1 : 0);
+  const int my_slot = (2 * b + (first_unit(b, U, NB) < t0 ? 1 : 0)) * SUBS + sub;
   f32x4* mine = slots + (size_t)my_slot * N * kWave;
 #pragma unroll
   for (int i = 0; i < N; ++i) mine[i * kWave + lane] = part[i];
   __threadfence();
   int last = 0;
-  if (lane == 0) last = atomicAdd(&counters[bf], 1) == (bl - bf);
+  if (lane == 0) last = atomicAdd(&counters[bf * SUBS + sub], 1) == (bl - bf);
   last = __shfl(last, 0, kWave);
   if (!last) return false;
   __threadfence();
 #pragma unroll
   for (int i = 0; i < N; ++i) part[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   for (int pb = bf; pb <= bl; ++pb) {
-    const int slot = 2 * pb + (first_unit(pb, U, NB) < t0 ? 1 : 0);
+    const int slot = (2 * pb + (first_unit(pb, U, NB) < t0 ? 1 : 0)) * SUBS + sub;
     const f32x4* src = slots + (size_t)slot * N * kWave;
 #pragma unroll
     for (int i = 0; i < N; ++i) part[i] = part[i] + src[i * kWave + lane];
@@ -535,6 +538,266 @@ __global__ __launch_bounds__(256) void ffn_down_sk_kernel(
   }
 }
 
+// ================================================================ prefill
+// Many tokens per expert: the 4 waves of a block take different weight rows
+// (16 each) over the same 64-wide K chunk, and the chunk of the pass's token
+// rows (B operand, up to 128 tokens) is staged once per block in LDS, double
+// buffered: while chunk u is multiplied, the loads of chunk u + 1 are in
+// flight (token rows first, then weights, so waiting for the token rows never
+// waits for the weights). Same stream-K schedule and fixed-order fixup, per
+// wave (each wave owns its rows).
+constexpr int PF_K = 128;
+constexpr int PF_STEPS = PF_K / 32;
+constexpr int PF_ROWS = 64;   // rows per tile: 4 waves x 16
+constexpr int PF_PAD = 8;     // bf16 padding per LDS row
+
+typedef uint16_t pf_row_t[PF_K + PF_PAD];
+
+// Gather one 64-wide chunk of NR B rows: thread t holds pieces t, t + 256, ...
+// (piece = row n, 16-byte column q). `src[n]` is the row start (+ chunk base).
+template <int NR>
+struct PfStage {
+  static constexpr int PIECES = NR * (PF_K / 8);
+  static constexpr int PER = (PIECES + 255) / 256;
+  u16x8 v[PER];
+};
+
+template <int NR>
+__device__ __forceinline__ void pf_stage_load(PfStage<NR>& st, const uint16_t* base,
+                                              const size_t (&roff)[(NR * (PF_K / 8) + 255) / 256],
+                                              size_t kb) {
+#pragma unroll
+  for (int i = 0; i < PfStage<NR>::PER; ++i)
+    st.v[i] = *reinterpret_cast<const u16x8*>(base + roff[i] + kb);
+}
+
+template <int NR>
+__device__ __forceinline__ void pf_stage_store(const PfStage<NR>& st, pf_row_t* dst, int tid) {
+#pragma unroll
+  for (int i = 0; i < PfStage<NR>::PER; ++i) {
+    const int piece = tid + 256 * i;
+    if (PfStage<NR>::PIECES % 256 == 0 || piece < PfStage<NR>::PIECES)
+      *reinterpret_cast<u16x8*>(&dst[piece / (PF_K / 8)][(piece % (PF_K / 8)) * 8]) = st.v[i];
+  }
+}
+
+template <int NTILES, int NT>
+__device__ __forceinline__ void pf_up_mma(const bf16x8 (&ag)[PF_STEPS],
+                                          const bf16x8 (&au)[PF_STEPS], const pf_row_t* bs,
+                                          int lane, f32x4* acc) {
+#pragma unroll
+  for (int st = 0; st < PF_STEPS; ++st) {
+#pragma unroll
+    for (int nt = 0; nt < NTILES; ++nt) {
+      const bf16x8 b =
+          *reinterpret_cast<const bf16x8*>(&bs[nt * 16 + (lane & 15)][st * 32 + (lane >> 4) * 8]);
+      acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ag[st], b, acc[nt], 0, 0, 0);
+      acc[NT + nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(au[st], b, acc[NT + nt], 0, 0, 0);
+    }
+  }
+}
+
+template <int NTILES, int NT>
+__device__ __forceinline__ void pf_down_mma(const bf16x8 (&a)[PF_STEPS], const pf_row_t* bh,
+                                            const pf_row_t* bl, int lane, f32x4* acc) {
+#pragma unroll
+  for (int st = 0; st < PF_STEPS; ++st) {
+#pragma unroll
+    for (int nt = 0; nt < NTILES; ++nt) {
+      const int n = nt * 16 + (lane & 15), c = st * 32 + (lane >> 4) * 8;
+      const bf16x8 h = *reinterpret_cast<const bf16x8*>(&bh[n][c]);
+      const bf16x8 l = *reinterpret_cast<const bf16x8*>(&bl[n][c]);
+      acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[st], h, acc[nt], 0, 0, 0);
+      acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[st], l, acc[nt], 0, 0, 0);
+    }
+  }
+}
+
+// Tile state (plan entries and the B rows' offsets), loaded a tile ahead.
+template <int NT>
+struct PfRaw {
+  int g, ex, tb, tc;
+  int r[PfStage<NT * 16>::PER];
+};
+
+template <int NT, bool UP>
+__device__ __forceinline__ void pf_issue(PfRaw<NT>& raw, long tile, long G, const PlanRO& pv,
+                                         const int* perm, int tid) {
+  const int pass = (int)(tile / G);
+  raw.g = (int)(tile % G);
+  raw.ex = pv.expert[pass];
+  raw.tb = pv.beg[pass];
+  raw.tc = pv.cnt[pass];
+#pragma unroll
+  for (int i = 0; i < PfStage<NT * 16>::PER; ++i) {
+    const int n = (tid + 256 * i) / (PF_K / 8);
+    const int nn = n < raw.tc ? n : 0;  // rows past the entries read the first entry's row
+    raw.r[i] = UP ? perm[raw.tb + nn] : raw.tb + nn;
+  }
+}
+
+template <int NT>
+struct PfTile {
+  int g, tb, tc, ntiles;
+  size_t wrow;                           // this lane's weight row (+ K offset)
+  size_t roff[PfStage<NT * 16>::PER];    // staged B rows (+ this thread's column)
+};
+
+template <int NT, bool UP>
+__device__ __forceinline__ void pf_finish(PfTile<NT>& st, const PfRaw<NT>& raw, int k, int H,
+                                          int I, int nmax, int wave, int lane, int tid) {
+  st.g = raw.g;
+  st.tb = raw.tb;
+  st.tc = raw.tc;
+  st.ntiles = (raw.tc + 15) >> 4;
+  const int row = raw.g * PF_ROWS + wave * 16 + (lane & 15);
+  const int kq = (lane >> 4) * 8;
+  const int K = UP ? H : I;
+  st.wrow = (UP ? ((size_t)raw.ex * 2 * I + row) : ((size_t)raw.ex * H + row)) * K + kq;
+#pragma unroll
+  for (int i = 0; i < PfStage<NT * 16>::PER; ++i) {
+    const int q = (tid + 256 * i) % (PF_K / 8);
+    int r = raw.r[i];
+    if (UP) r = (r >= 0 && r < nmax) ? r / k : 0;
+    st.roff[i] = (size_t)r * K + q * 8;
+  }
+}
+
+template <int NT, bool UP>
+__global__ __launch_bounds__(256) void ffn_pf_kernel(
+    const uint16_t* __restrict__ b0src, const uint16_t* __restrict__ b1src,
+    const int* __restrict__ perm, int k, int H, int I, int nmax, const uint16_t* __restrict__ w,
+    const int* __restrict__ plan, int pmax, f32x4* slots, int* counters,
+    uint16_t* __restrict__ h_hi, uint16_t* __restrict__ h_lo, float* __restrict__ out, int NB) {
+  constexpr int NR = NT * 16;
+  constexpr int NACC = UP ? 2 * NT : NT;
+  constexpr int NB_ARR = UP ? 1 : 2;  // B arrays: x, or h_hi and h_lo
+  __shared__ __attribute__((aligned(16))) pf_row_t bs[2][NB_ARR][NR];
+  const PlanRO pv = plan_ro(plan, pmax);
+  const long P = pv.hdr[0];
+  const int K = UP ? H : I;
+  const long G = (UP ? I : H) / PF_ROWS, C = K / PF_K;
+  const long U = P * G * C;
+  const int nb = (int)min((long)NB, U);
+  const int b = xcd_block(blockIdx.x, NB);
+  if (b >= nb) return;
+  const long s = first_unit(b, U, nb), e = first_unit(b + 1, U, nb);
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+  const long last_tile = (e - 1) / C;
+  const size_t I_H = (size_t)I * H;
+
+  PfTile<NT> ts, tn;
+  PfRaw<NT> rn;
+  {
+    PfRaw<NT> r0;
+    pf_issue<NT, UP>(r0, s / C, G, pv, perm, tid);
+    pf_finish<NT, UP>(ts, r0, k, H, I, nmax, wave, lane, tid);
+  }
+  pf_issue<NT, UP>(rn, min(s / C + 1, last_tile), G, pv, perm, tid);
+
+  f32x4 acc[NACC];
+#pragma unroll
+  for (int i = 0; i < NACC; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto load_a = [&](bf16x8 (&a)[PF_STEPS], bf16x8 (&a2)[PF_STEPS], const PfTile<NT>& t,
+                    size_t kb) {
+#pragma unroll
+    for (int st = 0; st < PF_STEPS; ++st) {
+      a[st] = ld8(w + t.wrow + kb + 32 * st);
+      if (UP) a2[st] = ld8(w + t.wrow + I_H + kb + 32 * st);
+    }
+  };
+
+  auto tile_end = [&](long u) {
+    const long tile = u / C;
+    const bool split = tile * C < s || tile * C + C > e;
+    bool done = true;
+    if (split) done = fixup<NACC, 4>(acc, slots, counters, tile, C, U, nb, b, lane, wave);
+    if (done) {
+      const int rbase = ts.g * PF_ROWS + wave * 16 + (lane >> 4) * 4;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const int n = nt * 16 + (lane & 15);
+        if (n >= ts.tc) continue;
+        if (UP) {
+          typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
+          u16x4 hi, lo;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float gg = acc[nt][j], uu = acc[NT + nt][j];
+            const float a = gg / (1.0f + expf(-gg)) * uu;
+            hi[j] = f32_to_bf16_bits(a);
+            lo[j] = f32_to_bf16_bits(a - bf16_bits_to_f32(hi[j]));
+          }
+          const size_t o = (size_t)(ts.tb + n) * I + rbase;
+          *reinterpret_cast<u16x4*>(h_hi + o) = hi;
+          *reinterpret_cast<u16x4*>(h_lo + o) = lo;
+        } else {
+          *reinterpret_cast<f32x4*>(out + (size_t)(ts.tb + n) * H + rbase) = acc[nt];
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NACC; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  };
+
+  // prologue: chunk s staged in buffer 0, its weights in registers
+  bf16x8 a0[PF_STEPS], a0u[PF_STEPS], a1[PF_STEPS], a1u[PF_STEPS];
+  {
+    PfStage<NR> st0, st1;
+    const size_t kb = (size_t)(s % C) * PF_K;
+    pf_stage_load(st0, b0src, ts.roff, kb);
+    if (!UP) pf_stage_load(st1, b1src, ts.roff, kb);
+    load_a(a0, a0u, ts, kb);
+    pf_stage_store(st0, bs[0][0], tid);
+    if (!UP) pf_stage_store(st1, bs[0][NB_ARR - 1], tid);
+    __syncthreads();
+  }
+
+  // One unit: issue chunk u + 1 (token rows, then weights), multiply chunk u
+  // from LDS buffer `cb`, store the token rows into the other buffer, finish
+  // the tile if u ends it here, and synchronise the block.
+  auto step = [&](bf16x8 (&ca)[PF_STEPS], bf16x8 (&cau)[PF_STEPS], bf16x8 (&na)[PF_STEPS],
+                  bf16x8 (&nau)[PF_STEPS], int cb, long& u) -> bool {
+    const long un = u + 1 < e ? u + 1 : u;
+    const bool crosses = un != u && un % C == 0;
+    if (crosses) {
+      pf_finish<NT, UP>(tn, rn, k, H, I, nmax, wave, lane, tid);
+      pf_issue<NT, UP>(rn, min(un / C + 1, last_tile), G, pv, perm, tid);
+    } else {
+      tn = ts;
+    }
+    const size_t kb = (size_t)(un % C) * PF_K;
+    PfStage<NR> st0, st1;
+    pf_stage_load(st0, b0src, tn.roff, kb);
+    if (!UP) pf_stage_load(st1, b1src, tn.roff, kb);
+    load_a(na, nau, tn, kb);
+    switch (ts.ntiles) {
+#define MOE_PF(n)                                                                 \
+  case n:                                                                         \
+    if (n <= NT) {                                                                \
+      if (UP) pf_up_mma<n, NT>(ca, cau, bs[cb][0], lane, acc);                    \
+      else pf_down_mma<n, NT>(ca, bs[cb][0], bs[cb][NB_ARR - 1], lane, acc);      \
+    }                                                                             \
+    break;
+      MOE_PF(1) MOE_PF(2) MOE_PF(3) MOE_PF(4) MOE_PF(5) MOE_PF(6) MOE_PF(7) MOE_PF(8)
+#undef MOE_PF
+    }
+    pf_stage_store(st0, bs[cb ^ 1][0], tid);
+    if (!UP) pf_stage_store(st1, bs[cb ^ 1][NB_ARR - 1], tid);
+    if (u % C == C - 1 || u == e - 1) tile_end(u);
+    __syncthreads();
+    if (u + 1 >= e) return false;
+    ts = tn;
+    u = un;
+    return true;
+  };
+
+  long u = s;
+  while (step(a0, a0u, a1, a1u, 0, u) && step(a1, a1u, a0, a0u, 1, u)) {
+  }
+}
+
 int device_cus() {
   static int cached[64] = {0};
   int dev = 0;
@@ -565,37 +828,58 @@ int resident_blocks(K kernel) {
   return cached[dev];
 }
 
-// Token tiles per pass, from twice the mean entries per local expert (an
-// expert with more entries takes further passes); 0 = use the LDS-tiled
-// kernels instead (many tokens per expert: prefill shapes).
+// Token tiles (of 16) per pass, from twice the mean entries per local expert
+// (an expert with more entries takes further passes), capped by T (a token
+// picks an expert at most once). 1 or 2: the K-split kernels; 4 or 8: the
+// prefill kernels.
 int pick_nt(int T, int k, int L) {
-  const long bound = T;  // a token picks an expert at most once
+  const long bound = T;
   const long twice_mean = L > 0 ? (2L * T * k + L - 1) / L : bound;
   const long want = twice_mean < bound ? twice_mean : bound;
-  return want <= 16 ? 1 : want <= 32 ? 2 : 0;
+  return want <= 16 ? 1 : want <= 32 ? 2 : want <= 64 ? 4 : 8;
 }
 
 size_t a256(size_t n) { return (n + 255) & ~(size_t)255; }
 
-// Upper bound of resident 256-thread blocks: 8 per CU.
-int max_blocks() { return 8 * device_cus(); }
+template <int NT>
+int up_blocks() {
+  if constexpr (NT <= 2) return resident_blocks(ffn_up_sk_kernel<NT, UP_STEPS>);
+  else return resident_blocks(ffn_pf_kernel<NT, true>);
+}
+template <int NT>
+int down_blocks() {
+  if constexpr (NT <= 2) return resident_blocks(ffn_down_sk_kernel<NT, DOWN_STEPS>);
+  else return resident_blocks(ffn_pf_kernel<NT, false>);
+}
 
+int blocks_for(int NT, bool up) {
+  switch (NT) {
+    case 1: return up ? up_blocks<1>() : down_blocks<1>();
+    case 2: return up ? up_blocks<2>() : down_blocks<2>();
+    case 4: return up ? up_blocks<4>() : down_blocks<4>();
+    default: return up ? up_blocks<8>() : down_blocks<8>();
+  }
+}
+
+// Workspace after h_hi / h_lo: the plan, then per kernel (up, down) 4 counters
+// and 2 x 4 slots per block; a slot holds one wave's partial tile (at most
+// 4 NT f32x4 per lane).
 struct SkLayout {
   size_t plan, counters, slots, total;
-  int pmax, ncounters, slot_f32x4;
+  int pmax, nb_up, nb_down;
 };
 
 SkLayout sk_layout(int T, int k, int L, int NT) {
   SkLayout o{};
   const int nmax = T * k, nr = NT * 16;
   o.pmax = L + (nmax + nr - 1) / nr + 1;
-  o.ncounters = 2 * max_blocks();
-  // a slot holds the larger of an up piece (2 NT) and a down piece (4 NT) f32x4 per lane
-  o.slot_f32x4 = NT * DOWN_GROUPS * kWave;
+  o.nb_up = blocks_for(NT, true);
+  o.nb_down = blocks_for(NT, false);
+  const int nbm = o.nb_up > o.nb_down ? o.nb_up : o.nb_down;
   o.plan = 0;
   o.counters = a256((size_t)(4 + 3 * o.pmax) * 4);
-  o.slots = o.counters + a256((size_t)o.ncounters * 4);
-  o.total = o.slots + a256((size_t)2 * max_blocks() * o.slot_f32x4 * 16);
+  o.slots = o.counters + a256((size_t)2 * 4 * nbm * 4);
+  o.total = o.slots + a256((size_t)2 * 4 * nbm * (4 * NT) * kWave * 16);
   return o;
 }
 
@@ -608,18 +892,31 @@ hipError_t launch_sk_nt(const uint16_t* x, const int* perm, const int* offsets, 
   int* counters = reinterpret_cast<int*>(ws + lo.counters);
   f32x4* slots = reinterpret_cast<f32x4*>(ws + lo.slots);
   const int nmax = T * k;
+  const int nbm = lo.nb_up > lo.nb_down ? lo.nb_up : lo.nb_down;
   hipLaunchKernelGGL(ffn_plan_kernel, dim3(1), dim3(1024), (size_t)(L + 1 + 16) * 4, stream,
-                     offsets, L, nmax, NT * 16, plan, lo.pmax, counters, lo.ncounters);
+                     offsets, L, nmax, NT * 16, plan, lo.pmax, counters, 2 * 4 * nbm);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  const int nb_up = resident_blocks(ffn_up_sk_kernel<NT, UP_STEPS>);
-  hipLaunchKernelGGL((ffn_up_sk_kernel<NT, UP_STEPS>), dim3(nb_up), dim3(256), 0, stream, x, perm, k, H, I,
-                     nmax, w1, plan, lo.pmax, slots, counters, h_hi, h_lo, nb_up);
+  if constexpr (NT <= 2) {
+    hipLaunchKernelGGL((ffn_up_sk_kernel<NT, UP_STEPS>), dim3(lo.nb_up), dim3(256), 0, stream, x,
+                       perm, k, H, I, nmax, w1, plan, lo.pmax, slots, counters, h_hi, h_lo,
+                       lo.nb_up);
+  } else {
+    hipLaunchKernelGGL((ffn_pf_kernel<NT, true>), dim3(lo.nb_up), dim3(256), 0, stream, x, x,
+                       perm, k, H, I, nmax, w1, plan, lo.pmax, slots, counters, h_hi, h_lo,
+                       out, lo.nb_up);
+  }
   err = hipGetLastError();
   if (err != hipSuccess) return err;
-  const int nb_down = resident_blocks(ffn_down_sk_kernel<NT, DOWN_STEPS>);
-  hipLaunchKernelGGL((ffn_down_sk_kernel<NT, DOWN_STEPS>), dim3(nb_down), dim3(256), 0, stream, h_hi, h_lo, H,
-                     I, w2, plan, lo.pmax, slots, counters + max_blocks(), out, nb_down);
+  if constexpr (NT <= 2) {
+    hipLaunchKernelGGL((ffn_down_sk_kernel<NT, DOWN_STEPS>), dim3(lo.nb_down), dim3(256), 0,
+                       stream, h_hi, h_lo, H, I, w2, plan, lo.pmax, slots, counters + 4 * nbm,
+                       out, lo.nb_down);
+  } else {
+    hipLaunchKernelGGL((ffn_pf_kernel<NT, false>), dim3(lo.nb_down), dim3(256), 0, stream, h_hi,
+                       h_lo, perm, k, H, I, nmax, w2, plan, lo.pmax, slots, counters + 4 * nbm,
+                       h_hi, h_lo, out, lo.nb_down);
+  }
   return hipGetLastError();
 }
 }  // namespace
@@ -627,13 +924,14 @@ hipError_t launch_sk_nt(const uint16_t* x, const int* perm, const int* offsets, 
 bool ffn_sk_applies(const void* x, const void* w1, const void* w2, int T, int k, int L, int H,
                     int I) {
   auto al = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
-  return al(x) && al(w1) && al(w2) && H % UP_KUNIT == 0 && I % DOWN_KUNIT == 0 &&
-         I % UP_ROWS == 0 && H % DOWN_ROWS == 0 && pick_nt(T, k, L) > 0;
+  if (!(al(x) && al(w1) && al(w2))) return false;
+  if (pick_nt(T, k, L) <= 2)
+    return H % UP_KUNIT == 0 && I % DOWN_KUNIT == 0 && I % UP_ROWS == 0 && H % DOWN_ROWS == 0;
+  return H % PF_K == 0 && I % PF_K == 0 && H % PF_ROWS == 0 && I % PF_ROWS == 0;
 }
 
 size_t ffn_sk_workspace_bytes(int T, int k, int L) {
-  const int nt = pick_nt(T, k, L);
-  return sk_layout(T, k, L, nt > 0 ? nt : 1).total;
+  return sk_layout(T, k, L, pick_nt(T, k, L)).total;
 }
 
 hipError_t launch_grouped_ffn_sk(const uint16_t* x, const int* perm, const int* offsets, int L,
@@ -641,9 +939,12 @@ hipError_t launch_grouped_ffn_sk(const uint16_t* x, const int* perm, const int* 
                                  const uint16_t* w2, uint16_t* h_hi, uint16_t* h_lo, float* out,
                                  void* ws, hipStream_t stream) {
   char* w = static_cast<char*>(ws);
-  if (pick_nt(T, k, L) == 1)
-    return launch_sk_nt<1>(x, perm, offsets, L, T, k, H, I, w1, w2, h_hi, h_lo, out, w, stream);
-  return launch_sk_nt<2>(x, perm, offsets, L, T, k, H, I, w1, w2, h_hi, h_lo, out, w, stream);
+  switch (pick_nt(T, k, L)) {
+    case 1: return launch_sk_nt<1>(x, perm, offsets, L, T, k, H, I, w1, w2, h_hi, h_lo, out, w, stream);
+    case 2: return launch_sk_nt<2>(x, perm, offsets, L, T, k, H, I, w1, w2, h_hi, h_lo, out, w, stream);
+    case 4: return launch_sk_nt<4>(x, perm, offsets, L, T, k, H, I, w1, w2, h_hi, h_lo, out, w, stream);
+    default: return launch_sk_nt<8>(x, perm, offsets, L, T, k, H, I, w1, w2, h_hi, h_lo, out, w, stream);
+  }
 }
 
 }  // namespace moe

@@ -88,6 +88,25 @@ def test_ffn_stream_k_share():
     check_ffn(48, 512, 512, 12, 2, 4, 5)
 
 
+# Prefill path (many entries per expert: 4 or 8 token tiles per pass, the
+# token rows staged in LDS per block): one pass, several passes, a skewed
+# expert, a share.
+@pytest.mark.parametrize("T,H,I,E,k", [(96, 512, 256, 8, 2), (256, 512, 512, 8, 2),
+                                       (512, 256, 256, 4, 2), (200, 768, 320, 16, 8)])
+def test_ffn_prefill(T, H, I, E, k):
+    check_ffn(T, H, I, E, k, 0, E)
+
+
+def test_ffn_prefill_skewed():
+    T, E, k = 300, 6, 2
+    ids = np.stack([np.full(T, 2, np.int32), (3 + np.arange(T, dtype=np.int32) % 3)], 1)
+    check_ffn(T, 256, 256, E, k, 0, E, ids=ids)
+
+
+def test_ffn_prefill_share():
+    check_ffn(384, 512, 256, 20, 4, 5, 6)
+
+
 def test_ffn_share_and_empty_experts():
     check_ffn(40, 128, 256, 16, 2, 3, 9)   # several local experts get no rows
 
