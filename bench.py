@@ -190,15 +190,21 @@ def main():
         n_tok = min(T, 32)
         sample = np.arange(n_tok, dtype=np.int32)
         oracle.default()
+        # Repeat the sampled forward until about 10 s of host time have passed.
+        reps = 0
         c0 = time.perf_counter()
-        oracle.forward(d["x"], d["wg"], d["w1"], d["w2"], k, first, L, d["bias"], sample)
+        while True:
+            oracle.forward(d["x"], d["wg"], d["w1"], d["w2"], k, first, L, d["bias"], sample)
+            reps += 1
+            if time.perf_counter() - c0 >= 10.0:
+                break
         c1 = time.perf_counter()
         cores = int(os.environ.get("OMP_NUM_THREADS", len(os.sched_getaffinity(0))))
-        cpu = {"value": round(n_tok / (c1 - c0), 3), "unit": "tokens/s", "cores": cores,
+        cpu = {"value": round(reps * n_tok / (c1 - c0), 3), "unit": "tokens/s", "cores": cores,
                "kind": "oracle",
-               "sample": f"{n_tok} of {T} tokens of the {args.workload} workload: fp64 router "
-                         f"for all tokens, routing, and the expert FFN + combine of the "
-                         f"sampled tokens; {c1 - c0:.2f} s wall"}
+               "sample": f"{n_tok} of {T} tokens of the {args.workload} workload, {reps} times: "
+                         f"fp64 router for all tokens, routing, and the expert FFN + combine "
+                         f"of the sampled tokens; {c1 - c0:.2f} s wall"}
 
     out = {
         "metric": "MoE layer tokens/s + % of HBM/MFMA roofline; routing us at 1024 experts",
@@ -221,7 +227,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": committed_traffic(args.workload),
-                     "kernel": "grouped FFN call (ffn_up_kernel + ffn_down_kernel)",
+                     "kernel": "grouped-FFN call (plan, W1 + SwiGLU, W2 kernels)",
                      "kernel_ms": round(ffn_ms, 4), "algorithmic_bytes": ffn_bytes},
         "cpu_baseline": cpu,
         "forward_ms_per_step": round(forward_ms, 4),
