@@ -539,33 +539,44 @@ __global__ __launch_bounds__(256) void ffn_down_sk_kernel(
 }
 
 // ================================================================ prefill
-// Many tokens per expert: the 4 waves of a block take different weight rows
-// (16 each) over the same 64-wide K chunk, and the chunk of the pass's token
-// rows (B operand, up to 128 tokens) is staged once per block in LDS, double
-// buffered: while chunk u is multiplied, the loads of chunk u + 1 are in
-// flight (token rows first, then weights, so waiting for the token rows never
-// waits for the weights). Same stream-K schedule and fixed-order fixup, per
-// wave (each wave owns its rows).
-constexpr int PF_K = 128;
+// Many tokens per expert. A block of 8 waves owns a tile of 256 weight rows
+// (32 per wave: two 16-row MFMA groups) and walks its K range in 64-wide
+// chunks. The chunk of the pass's token rows (B operand, up to 128 tokens) is
+// staged once per block in LDS and read by all 8 waves, so each token byte
+// brought in serves 256 weight rows. Token rows are loaded two chunks ahead
+// (registers, then one of two LDS buffers) and weights one chunk ahead, so no
+// wait in a step is for a load issued in the same step. Up tiles hold 128 gate
+// rows and the matching 128 up rows (a wave: 16 of each), so SwiGLU is applied
+// in the epilogue.
+//
+// On this chip the vector-memory path of a CU moves about 10 bytes per clock
+// whatever the access pattern, and weights and token rows share it: the
+// token-row bytes per weight byte (tokens / tile rows, doubled for the hi + lo
+// intermediate of the down projection) set how close the weights stream comes
+// to the HBM rate, hence the tall tiles.
+constexpr int PF_WAVES = 8;
+constexpr int PF_THREADS = PF_WAVES * kWave;
+constexpr int PF_K = 64;
 constexpr int PF_STEPS = PF_K / 32;
-constexpr int PF_ROWS = 64;   // rows per tile: 4 waves x 16
-constexpr int PF_PAD = 8;     // bf16 padding per LDS row
+constexpr int PF_GROUPS = 2;                        // 16-row MFMA groups per wave
+constexpr int PF_ROWS = PF_WAVES * 16 * PF_GROUPS;  // weight rows per tile
+constexpr int PF_UP_COLS = PF_ROWS / 2;             // h columns per up tile
+constexpr int PF_PAD = 8;                           // bf16 padding per LDS row
 
 typedef uint16_t pf_row_t[PF_K + PF_PAD];
 
-// Gather one 64-wide chunk of NR B rows: thread t holds pieces t, t + 256, ...
-// (piece = row n, 16-byte column q). `src[n]` is the row start (+ chunk base).
+// One 64-wide chunk of NR B rows: thread t holds pieces t, t + 512, ...
+// (piece = row n, 16-byte column q).
 template <int NR>
 struct PfStage {
   static constexpr int PIECES = NR * (PF_K / 8);
-  static constexpr int PER = (PIECES + 255) / 256;
+  static constexpr int PER = (PIECES + PF_THREADS - 1) / PF_THREADS;
   u16x8 v[PER];
 };
 
 template <int NR>
 __device__ __forceinline__ void pf_stage_load(PfStage<NR>& st, const uint16_t* base,
-                                              const size_t (&roff)[(NR * (PF_K / 8) + 255) / 256],
-                                              size_t kb) {
+                                              const size_t (&roff)[PfStage<NR>::PER], size_t kb) {
 #pragma unroll
   for (int i = 0; i < PfStage<NR>::PER; ++i)
     st.v[i] = *reinterpret_cast<const u16x8*>(base + roff[i] + kb);
@@ -575,40 +586,32 @@ template <int NR>
 __device__ __forceinline__ void pf_stage_store(const PfStage<NR>& st, pf_row_t* dst, int tid) {
 #pragma unroll
   for (int i = 0; i < PfStage<NR>::PER; ++i) {
-    const int piece = tid + 256 * i;
-    if (PfStage<NR>::PIECES % 256 == 0 || piece < PfStage<NR>::PIECES)
+    const int piece = tid + PF_THREADS * i;
+    if (PfStage<NR>::PIECES % PF_THREADS == 0 || piece < PfStage<NR>::PIECES)
       *reinterpret_cast<u16x8*>(&dst[piece / (PF_K / 8)][(piece % (PF_K / 8)) * 8]) = st.v[i];
   }
 }
 
-template <int NTILES, int NT>
-__device__ __forceinline__ void pf_up_mma(const bf16x8 (&ag)[PF_STEPS],
-                                          const bf16x8 (&au)[PF_STEPS], const pf_row_t* bs,
-                                          int lane, f32x4* acc) {
+// acc[q * NT + nt] += A(group q) * B(token tile nt) over one chunk; the down
+// projection multiplies both halves (hi, lo) of the intermediate.
+template <int NT, bool UP>
+__device__ __forceinline__ void pf_mma(const bf16x8 (&a)[PF_GROUPS][PF_STEPS], const pf_row_t* b0,
+                                       const pf_row_t* b1, int lane, f32x4* acc) {
 #pragma unroll
   for (int st = 0; st < PF_STEPS; ++st) {
 #pragma unroll
-    for (int nt = 0; nt < NTILES; ++nt) {
-      const bf16x8 b =
-          *reinterpret_cast<const bf16x8*>(&bs[nt * 16 + (lane & 15)][st * 32 + (lane >> 4) * 8]);
-      acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ag[st], b, acc[nt], 0, 0, 0);
-      acc[NT + nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(au[st], b, acc[NT + nt], 0, 0, 0);
-    }
-  }
-}
-
-template <int NTILES, int NT>
-__device__ __forceinline__ void pf_down_mma(const bf16x8 (&a)[PF_STEPS], const pf_row_t* bh,
-                                            const pf_row_t* bl, int lane, f32x4* acc) {
-#pragma unroll
-  for (int st = 0; st < PF_STEPS; ++st) {
-#pragma unroll
-    for (int nt = 0; nt < NTILES; ++nt) {
+    for (int nt = 0; nt < NT; ++nt) {
       const int n = nt * 16 + (lane & 15), c = st * 32 + (lane >> 4) * 8;
-      const bf16x8 h = *reinterpret_cast<const bf16x8*>(&bh[n][c]);
-      const bf16x8 l = *reinterpret_cast<const bf16x8*>(&bl[n][c]);
-      acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[st], h, acc[nt], 0, 0, 0);
-      acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[st], l, acc[nt], 0, 0, 0);
+      const bf16x8 h = *reinterpret_cast<const bf16x8*>(&b0[n][c]);
+#pragma unroll
+      for (int q = 0; q < PF_GROUPS; ++q)
+        acc[q * NT + nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[q][st], h, acc[q * NT + nt], 0, 0, 0);
+      if (!UP) {
+        const bf16x8 l = *reinterpret_cast<const bf16x8*>(&b1[n][c]);
+#pragma unroll
+        for (int q = 0; q < PF_GROUPS; ++q)
+          acc[q * NT + nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[q][st], l, acc[q * NT + nt], 0, 0, 0);
+      }
     }
   }
 }
@@ -621,16 +624,16 @@ struct PfRaw {
 };
 
 template <int NT, bool UP>
-__device__ __forceinline__ void pf_issue(PfRaw<NT>& raw, long tile, long G, const PlanRO& pv,
+__device__ __forceinline__ void pf_issue(PfRaw<NT>& raw, int tile, int G, const PlanRO& pv,
                                          const int* perm, int tid) {
-  const int pass = (int)(tile / G);
-  raw.g = (int)(tile % G);
+  const int pass = tile / G;
+  raw.g = tile - pass * G;
   raw.ex = pv.expert[pass];
   raw.tb = pv.beg[pass];
   raw.tc = pv.cnt[pass];
 #pragma unroll
   for (int i = 0; i < PfStage<NT * 16>::PER; ++i) {
-    const int n = (tid + 256 * i) / (PF_K / 8);
+    const int n = (tid + PF_THREADS * i) / (PF_K / 8);
     const int nn = n < raw.tc ? n : 0;  // rows past the entries read the first entry's row
     raw.r[i] = UP ? perm[raw.tb + nn] : raw.tb + nn;
   }
@@ -639,9 +642,18 @@ __device__ __forceinline__ void pf_issue(PfRaw<NT>& raw, long tile, long G, cons
 template <int NT>
 struct PfTile {
   int g, tb, tc, ntiles;
-  size_t wrow;                           // this lane's weight row (+ K offset)
-  size_t roff[PfStage<NT * 16>::PER];    // staged B rows (+ this thread's column)
+  size_t wrow;                               // this lane's first weight row (+ K offset)
+  size_t roff[PfStage<NT * 16>::PER];        // staged B rows (+ this thread's column)
 };
+
+// Weight row of group q relative to the lane's first row: up groups 0, 1 are
+// gate rows c0 .. c0 + 31 and groups 2, 3 the up rows I + c0 .. ; down groups
+// are 16 consecutive output rows each.
+template <bool UP>
+__device__ __forceinline__ size_t pf_group_offset(int q, int H, int I) {
+  constexpr int HALF = PF_GROUPS / 2;
+  return UP ? (size_t)((q % HALF) * 16 + (q / HALF) * I) * H : (size_t)q * 16 * I;
+}
 
 template <int NT, bool UP>
 __device__ __forceinline__ void pf_finish(PfTile<NT>& st, const PfRaw<NT>& raw, int k, int H,
@@ -650,90 +662,147 @@ __device__ __forceinline__ void pf_finish(PfTile<NT>& st, const PfRaw<NT>& raw, 
   st.tb = raw.tb;
   st.tc = raw.tc;
   st.ntiles = (raw.tc + 15) >> 4;
-  const int row = raw.g * PF_ROWS + wave * 16 + (lane & 15);
   const int kq = (lane >> 4) * 8;
   const int K = UP ? H : I;
+  const int row = UP ? raw.g * PF_UP_COLS + wave * 8 * PF_GROUPS + (lane & 15)
+                     : raw.g * PF_ROWS + wave * 16 * PF_GROUPS + (lane & 15);
   st.wrow = (UP ? ((size_t)raw.ex * 2 * I + row) : ((size_t)raw.ex * H + row)) * K + kq;
 #pragma unroll
   for (int i = 0; i < PfStage<NT * 16>::PER; ++i) {
-    const int q = (tid + 256 * i) % (PF_K / 8);
+    const int q = (tid + PF_THREADS * i) % (PF_K / 8);
     int r = raw.r[i];
     if (UP) r = (r >= 0 && r < nmax) ? r / k : 0;
     st.roff[i] = (size_t)r * K + q * 8;
   }
 }
 
+// Position in the unit sequence: tile t, K chunk kc. Tiles are numbered
+// pass-major (t = pass * G + g) and fit in 32 bits; every step advances the
+// position by additions only.
+struct Pos {
+  int t, kc;
+};
+
 template <int NT, bool UP>
-__global__ __launch_bounds__(256) void ffn_pf_kernel(
+__global__ __launch_bounds__(PF_THREADS) void ffn_pf_kernel(
     const uint16_t* __restrict__ b0src, const uint16_t* __restrict__ b1src,
     const int* __restrict__ perm, int k, int H, int I, int nmax, const uint16_t* __restrict__ w,
     const int* __restrict__ plan, int pmax, f32x4* slots, int* counters,
     uint16_t* __restrict__ h_hi, uint16_t* __restrict__ h_lo, float* __restrict__ out, int NB) {
   constexpr int NR = NT * 16;
-  constexpr int NACC = UP ? 2 * NT : NT;
+  constexpr int NACC = PF_GROUPS * NT;
   constexpr int NB_ARR = UP ? 1 : 2;  // B arrays: x, or h_hi and h_lo
   __shared__ __attribute__((aligned(16))) pf_row_t bs[2][NB_ARR][NR];
   const PlanRO pv = plan_ro(plan, pmax);
-  const long P = pv.hdr[0];
+  const int P = pv.hdr[0];
   const int K = UP ? H : I;
-  const long G = (UP ? I : H) / PF_ROWS, C = K / PF_K;
-  const long U = P * G * C;
-  const int nb = (int)min((long)NB, U);
+  const int G = UP ? I / PF_UP_COLS : H / PF_ROWS, C = K / PF_K;
+  // Whole rounds of tiles first: in round r block b takes tile r * NB + b, so
+  // the blocks that run together on one XCD take neighbouring tiles of the
+  // same expert and walk K in step, reading each chunk of token rows from L2
+  // after the first of them fetched it. The remaining 1 to 2 rounds' tiles
+  // are cut into equal unit ranges (stream-K) as above.
+  const int TT = P * G;
+  const int R = TT >= 2 * NB ? TT / NB - 1 : 0;
+  const int TD = R * NB;                       // tiles of the whole rounds
+  const long US = (long)(TT - TD) * C;         // units of the stream-K part
+  const int nb = (int)min((long)NB, US);
   const int b = xcd_block(blockIdx.x, NB);
   if (b >= nb) return;
-  const long s = first_unit(b, U, nb), e = first_unit(b + 1, U, nb);
+  const long s_rel = first_unit(b, US, nb), e_rel = first_unit(b + 1, US, nb);
+  const Pos ps{TD + (int)(s_rel / C), (int)(s_rel % C)};              // first SK unit
+  const Pos pe{TD + (int)((e_rel - 1) / C), (int)((e_rel - 1) % C)};  // last unit
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
-  const long last_tile = (e - 1) / C;
-  const size_t I_H = (size_t)I * H;
+  // The block's tiles in order: b, b + NB, ... (whole rounds), then ps.t .. pe.t
+  auto next_tile = [&](int t) -> int {
+    if (t < TD) return t + NB < TD ? t + NB : ps.t;
+    return t < pe.t ? t + 1 : pe.t;
+  };
+  auto next_pos = [&](Pos p) -> Pos {
+    if (p.t == pe.t && p.kc == pe.kc) return p;  // the last unit: stay
+    if (p.kc + 1 < C) return Pos{p.t, p.kc + 1};
+    if (p.t >= TD) return Pos{p.t + 1, 0};
+    return p.t + NB < TD ? Pos{p.t + NB, 0} : ps;
+  };
+  const Pos p0 = R > 0 ? Pos{b, 0} : ps;
 
-  PfTile<NT> ts, tn;
+  // Tile states of the units in the pipeline: t0 for chunk p (multiplied this
+  // step), t1 for chunk p1 (its weights are loaded this step, its token rows
+  // were loaded the step before), t2 for chunk p2 (its token rows are loaded
+  // this step); rn holds the plan entries of the tile after t2's.
+  PfTile<NT> t0, t1, t2;
   PfRaw<NT> rn;
+  Pos p1 = next_pos(p0);
   {
     PfRaw<NT> r0;
-    pf_issue<NT, UP>(r0, s / C, G, pv, perm, tid);
-    pf_finish<NT, UP>(ts, r0, k, H, I, nmax, wave, lane, tid);
+    pf_issue<NT, UP>(r0, p0.t, G, pv, perm, tid);
+    pf_finish<NT, UP>(t0, r0, k, H, I, nmax, wave, lane, tid);
+    if (p1.t != p0.t) {
+      pf_issue<NT, UP>(r0, p1.t, G, pv, perm, tid);
+      pf_finish<NT, UP>(t1, r0, k, H, I, nmax, wave, lane, tid);
+    } else {
+      t1 = t0;
+    }
   }
-  pf_issue<NT, UP>(rn, min(s / C + 1, last_tile), G, pv, perm, tid);
+  pf_issue<NT, UP>(rn, next_tile(p1.t), G, pv, perm, tid);
 
   f32x4 acc[NACC];
 #pragma unroll
   for (int i = 0; i < NACC; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto load_a = [&](bf16x8 (&a)[PF_STEPS], bf16x8 (&a2)[PF_STEPS], const PfTile<NT>& t,
-                    size_t kb) {
+  auto load_a = [&](bf16x8 (&a)[PF_GROUPS][PF_STEPS], const PfTile<NT>& t, int kc) {
+    const size_t kb = (size_t)kc * PF_K;
 #pragma unroll
-    for (int st = 0; st < PF_STEPS; ++st) {
-      a[st] = ld8(w + t.wrow + kb + 32 * st);
-      if (UP) a2[st] = ld8(w + t.wrow + I_H + kb + 32 * st);
-    }
+    for (int q = 0; q < PF_GROUPS; ++q)
+#pragma unroll
+      for (int st = 0; st < PF_STEPS; ++st)
+        a[q][st] = ld8(w + t.wrow + pf_group_offset<UP>(q, H, I) + kb + 32 * st);
+  };
+  auto load_b = [&](PfStage<NR> (&st)[NB_ARR], const PfTile<NT>& t, int kc) {
+    const size_t kb = (size_t)kc * PF_K;
+    pf_stage_load(st[0], b0src, t.roff, kb);
+    if (!UP) pf_stage_load(st[NB_ARR - 1], b1src, t.roff, kb);
+  };
+  auto store_b = [&](const PfStage<NR> (&st)[NB_ARR], int buf) {
+    pf_stage_store(st[0], bs[buf][0], tid);
+    if (!UP) pf_stage_store(st[NB_ARR - 1], bs[buf][NB_ARR - 1], tid);
   };
 
-  auto tile_end = [&](long u) {
-    const long tile = u / C;
-    const bool split = tile * C < s || tile * C + C > e;
+  // End of tile p.t in this block: complete it (directly, or through the
+  // cross-block fixup when the stream-K cut falls inside it) and write it.
+  auto tile_end = [&](Pos p) {
+    const bool split = p.t >= TD && ((p.t == ps.t && ps.kc > 0) || (p.t == pe.t && pe.kc < C - 1));
     bool done = true;
-    if (split) done = fixup<NACC, 4>(acc, slots, counters, tile, C, U, nb, b, lane, wave);
+    if (split)
+      done = fixup<NACC, PF_WAVES>(acc, slots, counters, p.t - TD, C, US, nb, b, lane, wave);
     if (done) {
-      const int rbase = ts.g * PF_ROWS + wave * 16 + (lane >> 4) * 4;
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         const int n = nt * 16 + (lane & 15);
-        if (n >= ts.tc) continue;
+        if (n >= t0.tc) continue;
         if (UP) {
           typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
-          u16x4 hi, lo;
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const float gg = acc[nt][j], uu = acc[NT + nt][j];
-            const float a = gg / (1.0f + expf(-gg)) * uu;
-            hi[j] = f32_to_bf16_bits(a);
-            lo[j] = f32_to_bf16_bits(a - bf16_bits_to_f32(hi[j]));
+          for (int q = 0; q < PF_GROUPS / 2; ++q) {
+            u16x4 hi, lo;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const float gg = acc[q * NT + nt][j], uu = acc[(q + PF_GROUPS / 2) * NT + nt][j];
+              const float a = gg / (1.0f + expf(-gg)) * uu;
+              hi[j] = f32_to_bf16_bits(a);
+              lo[j] = f32_to_bf16_bits(a - bf16_bits_to_f32(hi[j]));
+            }
+            const int col = t0.g * PF_UP_COLS + wave * 8 * PF_GROUPS + q * 16 + (lane >> 4) * 4;
+            const size_t o = (size_t)(t0.tb + n) * I + col;
+            *reinterpret_cast<u16x4*>(h_hi + o) = hi;
+            *reinterpret_cast<u16x4*>(h_lo + o) = lo;
           }
-          const size_t o = (size_t)(ts.tb + n) * I + rbase;
-          *reinterpret_cast<u16x4*>(h_hi + o) = hi;
-          *reinterpret_cast<u16x4*>(h_lo + o) = lo;
         } else {
-          *reinterpret_cast<f32x4*>(out + (size_t)(ts.tb + n) * H + rbase) = acc[nt];
+#pragma unroll
+          for (int q = 0; q < PF_GROUPS; ++q) {
+            const int row = t0.g * PF_ROWS + wave * 16 * PF_GROUPS + q * 16 + (lane >> 4) * 4;
+            *reinterpret_cast<f32x4*>(out + (size_t)(t0.tb + n) * H + row) = acc[q * NT + nt];
+          }
         }
       }
     }
@@ -741,60 +810,47 @@ __global__ __launch_bounds__(256) void ffn_pf_kernel(
     for (int i = 0; i < NACC; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   };
 
-  // prologue: chunk s staged in buffer 0, its weights in registers
-  bf16x8 a0[PF_STEPS], a0u[PF_STEPS], a1[PF_STEPS], a1u[PF_STEPS];
-  {
-    PfStage<NR> st0, st1;
-    const size_t kb = (size_t)(s % C) * PF_K;
-    pf_stage_load(st0, b0src, ts.roff, kb);
-    if (!UP) pf_stage_load(st1, b1src, ts.roff, kb);
-    load_a(a0, a0u, ts, kb);
-    pf_stage_store(st0, bs[0][0], tid);
-    if (!UP) pf_stage_store(st1, bs[0][NB_ARR - 1], tid);
-    __syncthreads();
-  }
+  // prologue: chunk p0's token rows in LDS buffer 0 and its weights in
+  // registers; chunk p1's token rows in flight
+  bf16x8 a0[PF_GROUPS][PF_STEPS], a1[PF_GROUPS][PF_STEPS];
+  PfStage<NR> sb0[NB_ARR], sb1[NB_ARR];
+  load_b(sb1, t0, p0.kc);
+  load_a(a0, t0, p0.kc);
+  store_b(sb1, 0);
+  load_b(sb0, t1, p1.kc);
+  __syncthreads();
 
-  // One unit: issue chunk u + 1 (token rows, then weights), multiply chunk u
-  // from LDS buffer `cb`, store the token rows into the other buffer, finish
-  // the tile if u ends it here, and synchronise the block.
-  auto step = [&](bf16x8 (&ca)[PF_STEPS], bf16x8 (&cau)[PF_STEPS], bf16x8 (&na)[PF_STEPS],
-                  bf16x8 (&nau)[PF_STEPS], int cb, long& u) -> bool {
-    const long un = u + 1 < e ? u + 1 : u;
-    const bool crosses = un != u && un % C == 0;
-    if (crosses) {
-      pf_finish<NT, UP>(tn, rn, k, H, I, nmax, wave, lane, tid);
-      pf_issue<NT, UP>(rn, min(un / C + 1, last_tile), G, pv, perm, tid);
+  // One unit: issue chunk p2's token rows and chunk p1's weights, multiply
+  // chunk p (weights `ca`, token rows in LDS buffer `cb`), write chunk p1's
+  // token rows (`cs`, loaded a step earlier) into the other buffer, finish the
+  // tile if p ends it here, and synchronise the block. Returns false after
+  // the block's last unit.
+  auto step = [&](bf16x8 (&ca)[PF_GROUPS][PF_STEPS], bf16x8 (&na)[PF_GROUPS][PF_STEPS],
+                  PfStage<NR> (&cs)[NB_ARR], PfStage<NR> (&ns)[NB_ARR], int cb, Pos& p) -> bool {
+    const Pos p2 = next_pos(p1);
+    if (p2.t != p1.t) {
+      pf_finish<NT, UP>(t2, rn, k, H, I, nmax, wave, lane, tid);
+      pf_issue<NT, UP>(rn, next_tile(p2.t), G, pv, perm, tid);
     } else {
-      tn = ts;
+      t2 = t1;
     }
-    const size_t kb = (size_t)(un % C) * PF_K;
-    PfStage<NR> st0, st1;
-    pf_stage_load(st0, b0src, tn.roff, kb);
-    if (!UP) pf_stage_load(st1, b1src, tn.roff, kb);
-    load_a(na, nau, tn, kb);
-    switch (ts.ntiles) {
-#define MOE_PF(n)                                                                 \
-  case n:                                                                         \
-    if (n <= NT) {                                                                \
-      if (UP) pf_up_mma<n, NT>(ca, cau, bs[cb][0], lane, acc);                    \
-      else pf_down_mma<n, NT>(ca, bs[cb][0], bs[cb][NB_ARR - 1], lane, acc);      \
-    }                                                                             \
-    break;
-      MOE_PF(1) MOE_PF(2) MOE_PF(3) MOE_PF(4) MOE_PF(5) MOE_PF(6) MOE_PF(7) MOE_PF(8)
-#undef MOE_PF
-    }
-    pf_stage_store(st0, bs[cb ^ 1][0], tid);
-    if (!UP) pf_stage_store(st1, bs[cb ^ 1][NB_ARR - 1], tid);
-    if (u % C == C - 1 || u == e - 1) tile_end(u);
+    load_b(ns, t2, p2.kc);
+    load_a(na, t1, p1.kc);
+    pf_mma<NT, UP>(ca, bs[cb][0], bs[cb][NB_ARR - 1], lane, acc);
+    store_b(cs, cb ^ 1);
+    const bool last = p.t == pe.t && p.kc == pe.kc;
+    if (p.kc == C - 1 || last) tile_end(p);
     __syncthreads();
-    if (u + 1 >= e) return false;
-    ts = tn;
-    u = un;
+    if (last) return false;
+    t0 = t1;
+    t1 = t2;
+    p = p1;
+    p1 = p2;
     return true;
   };
 
-  long u = s;
-  while (step(a0, a0u, a1, a1u, 0, u) && step(a1, a1u, a0, a0u, 1, u)) {
+  Pos p = p0;
+  while (step(a0, a1, sb0, sb1, 0, p) && step(a1, a0, sb1, sb0, 1, p)) {
   }
 }
 
@@ -811,15 +867,15 @@ int device_cus() {
   return cached[dev];
 }
 
-// Resident 256-thread blocks of `kernel` on the current device (cached).
+// Resident blocks of `threads` threads of `kernel` on the current device (cached).
 template <typename K>
-int resident_blocks(K kernel) {
+int resident_blocks(K kernel, int threads = 256) {
   static int cached[64] = {0};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
   if (cached[dev] == 0) {
     int per_cu = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, 0) != hipSuccess ||
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess ||
         per_cu <= 0)
       per_cu = 1;
     if (per_cu > 8) per_cu = 8;  // the workspace holds slots for 8 blocks per CU
@@ -844,12 +900,12 @@ size_t a256(size_t n) { return (n + 255) & ~(size_t)255; }
 template <int NT>
 int up_blocks() {
   if constexpr (NT <= 2) return resident_blocks(ffn_up_sk_kernel<NT, UP_STEPS>);
-  else return resident_blocks(ffn_pf_kernel<NT, true>);
+  else return resident_blocks(ffn_pf_kernel<NT, true>, PF_THREADS);
 }
 template <int NT>
 int down_blocks() {
   if constexpr (NT <= 2) return resident_blocks(ffn_down_sk_kernel<NT, DOWN_STEPS>);
-  else return resident_blocks(ffn_pf_kernel<NT, false>);
+  else return resident_blocks(ffn_pf_kernel<NT, false>, PF_THREADS);
 }
 
 int blocks_for(int NT, bool up) {
@@ -861,12 +917,14 @@ int blocks_for(int NT, bool up) {
   }
 }
 
-// Workspace after h_hi / h_lo: the plan, then per kernel (up, down) 4 counters
-// and 2 x 4 slots per block; a slot holds one wave's partial tile (at most
-// 4 NT f32x4 per lane).
+// Workspace after h_hi / h_lo: the plan, then per kernel (up, down) `subs`
+// counters per block, and 2 x `subs` slots per block shared by both kernels
+// (a block's first and last tile; `subs` = 1 for the K-split kernels, one per
+// wave for the prefill kernels). A slot holds one wave's partial tile, at most
+// 4 NT f32x4 per lane.
 struct SkLayout {
   size_t plan, counters, slots, total;
-  int pmax, nb_up, nb_down;
+  int pmax, nb_up, nb_down, subs;
 };
 
 SkLayout sk_layout(int T, int k, int L, int NT) {
@@ -877,9 +935,10 @@ SkLayout sk_layout(int T, int k, int L, int NT) {
   o.nb_down = blocks_for(NT, false);
   const int nbm = o.nb_up > o.nb_down ? o.nb_up : o.nb_down;
   o.plan = 0;
+  o.subs = NT <= 2 ? 1 : PF_WAVES;
   o.counters = a256((size_t)(4 + 3 * o.pmax) * 4);
-  o.slots = o.counters + a256((size_t)2 * 4 * nbm * 4);
-  o.total = o.slots + a256((size_t)2 * 4 * nbm * (4 * NT) * kWave * 16);
+  o.slots = o.counters + a256((size_t)2 * o.subs * nbm * 4);
+  o.total = o.slots + a256((size_t)2 * o.subs * nbm * (4 * NT) * kWave * 16);
   return o;
 }
 
@@ -894,7 +953,7 @@ hipError_t launch_sk_nt(const uint16_t* x, const int* perm, const int* offsets, 
   const int nmax = T * k;
   const int nbm = lo.nb_up > lo.nb_down ? lo.nb_up : lo.nb_down;
   hipLaunchKernelGGL(ffn_plan_kernel, dim3(1), dim3(1024), (size_t)(L + 1 + 16) * 4, stream,
-                     offsets, L, nmax, NT * 16, plan, lo.pmax, counters, 2 * 4 * nbm);
+                     offsets, L, nmax, NT * 16, plan, lo.pmax, counters, 2 * lo.subs * nbm);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   if constexpr (NT <= 2) {
@@ -902,7 +961,7 @@ hipError_t launch_sk_nt(const uint16_t* x, const int* perm, const int* offsets, 
                        perm, k, H, I, nmax, w1, plan, lo.pmax, slots, counters, h_hi, h_lo,
                        lo.nb_up);
   } else {
-    hipLaunchKernelGGL((ffn_pf_kernel<NT, true>), dim3(lo.nb_up), dim3(256), 0, stream, x, x,
+    hipLaunchKernelGGL((ffn_pf_kernel<NT, true>), dim3(lo.nb_up), dim3(PF_THREADS), 0, stream, x, x,
                        perm, k, H, I, nmax, w1, plan, lo.pmax, slots, counters, h_hi, h_lo,
                        out, lo.nb_up);
   }
@@ -910,11 +969,11 @@ hipError_t launch_sk_nt(const uint16_t* x, const int* perm, const int* offsets, 
   if (err != hipSuccess) return err;
   if constexpr (NT <= 2) {
     hipLaunchKernelGGL((ffn_down_sk_kernel<NT, DOWN_STEPS>), dim3(lo.nb_down), dim3(256), 0,
-                       stream, h_hi, h_lo, H, I, w2, plan, lo.pmax, slots, counters + 4 * nbm,
+                       stream, h_hi, h_lo, H, I, w2, plan, lo.pmax, slots, counters + lo.subs * nbm,
                        out, lo.nb_down);
   } else {
-    hipLaunchKernelGGL((ffn_pf_kernel<NT, false>), dim3(lo.nb_down), dim3(256), 0, stream, h_hi,
-                       h_lo, perm, k, H, I, nmax, w2, plan, lo.pmax, slots, counters + 4 * nbm,
+    hipLaunchKernelGGL((ffn_pf_kernel<NT, false>), dim3(lo.nb_down), dim3(PF_THREADS), 0, stream, h_hi,
+                       h_lo, perm, k, H, I, nmax, w2, plan, lo.pmax, slots, counters + lo.subs * nbm,
                        h_hi, h_lo, out, lo.nb_down);
   }
   return hipGetLastError();
@@ -927,7 +986,7 @@ bool ffn_sk_applies(const void* x, const void* w1, const void* w2, int T, int k,
   if (!(al(x) && al(w1) && al(w2))) return false;
   if (pick_nt(T, k, L) <= 2)
     return H % UP_KUNIT == 0 && I % DOWN_KUNIT == 0 && I % UP_ROWS == 0 && H % DOWN_ROWS == 0;
-  return H % PF_K == 0 && I % PF_K == 0 && H % PF_ROWS == 0 && I % PF_ROWS == 0;
+  return H % PF_K == 0 && I % PF_K == 0 && H % PF_ROWS == 0 && I % PF_UP_COLS == 0;
 }
 
 size_t ffn_sk_workspace_bytes(int T, int k, int L) {

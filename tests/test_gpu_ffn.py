@@ -89,12 +89,19 @@ def test_ffn_stream_k_share():
 
 
 # Prefill path (many entries per expert: 4 or 8 token tiles per pass, the
-# token rows staged in LDS per block): one pass, several passes, a skewed
-# expert, a share.
+# token rows staged in LDS per block; H a multiple of 256, I of 128): one
+# pass, several passes, a skewed expert, a share.
 @pytest.mark.parametrize("T,H,I,E,k", [(96, 512, 256, 8, 2), (256, 512, 512, 8, 2),
-                                       (512, 256, 256, 4, 2), (200, 768, 320, 16, 8)])
+                                       (512, 256, 256, 4, 2), (200, 768, 384, 16, 8)])
 def test_ffn_prefill(T, H, I, E, k):
     check_ffn(T, H, I, E, k, 0, E)
+
+
+def test_ffn_prefill_whole_rounds():
+    """512 experts of ~64 entries: 512 up tiles and 512 down tiles, at least
+    twice the resident blocks of a 256-CU part, so whole rounds of tiles (one
+    tile per block, no cut) run before the stream-K remainder."""
+    check_ffn(4096, 256, 128, 512, 8, 0, 512)
 
 
 def test_ffn_prefill_skewed():
