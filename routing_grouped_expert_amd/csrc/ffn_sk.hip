@@ -44,6 +44,9 @@ constexpr int UP_STEPS = 2;
 constexpr int DOWN_STEPS = 4;
 constexpr int UP_KUNIT = 4 * 32 * UP_STEPS;
 constexpr int DOWN_KUNIT = 4 * 32 * DOWN_STEPS;
+// Blocks per CU of the K-split up kernel: measured on MI355X at the decode
+// shape, 3, 4 and 5 resident blocks take 1.21x, 1x and 1.42x the time of 4.
+constexpr int UP_CAP = 4;
 constexpr int UP_ROWS = 16;       // gate rows (and as many up rows) per up tile
 constexpr int DOWN_GROUPS = 4;    // 16-row groups per down tile
 constexpr int DOWN_ROWS = 16 * DOWN_GROUPS;
@@ -112,6 +115,37 @@ __device__ __forceinline__ int block_of_unit(long u, long U, int NB) {
   return (int)(((u + 1) * NB + U - 1) / U) - 1;
 }
 __device__ __forceinline__ long first_unit(int b, long U, int NB) { return (long)b * U / NB; }
+
+// Position in a block's unit sequence: tile t, K chunk kc (unit t * C + kc).
+// Tiles are numbered pass-major (t = pass * G + g) and fit in 32 bits; the
+// main loops advance positions by additions only (a 64-bit division per step
+// costs more than a step's arithmetic).
+struct Pos {
+  int t, kc;
+};
+
+// Block b's range [first_unit(b), first_unit(b + 1)) of U units of C chunks.
+struct SkRange {
+  Pos ps, pe;  // its first and last unit
+  int C;
+  __device__ SkRange(int b, long U, int NB, int C_) : C(C_) {
+    const long s = first_unit(b, U, NB), e = first_unit(b + 1, U, NB) - 1;
+    ps = Pos{(int)(s / C), (int)(s % C)};
+    pe = Pos{(int)(e / C), (int)(e % C)};
+  }
+  __device__ bool last(Pos p) const { return p.t == pe.t && p.kc == pe.kc; }
+  // the unit after p (p itself after the last)
+  __device__ Pos next(Pos p) const {
+    if (last(p)) return p;
+    return p.kc + 1 < C ? Pos{p.t, p.kc + 1} : Pos{p.t + 1, 0};
+  }
+  __device__ int next_tile(int t) const { return t < pe.t ? t + 1 : pe.t; }
+  __device__ bool ends_tile(Pos p) const { return p.kc == C - 1 || last(p); }
+  // tile t is shared with another block
+  __device__ bool split(int t) const {
+    return (t == ps.t && ps.kc > 0) || (t == pe.t && pe.kc < C - 1);
+  }
+};
 
 // Workgroups are dispatched to the 8 XCDs round-robin (block b to XCD b % 8),
 // and each XCD has its own L2. Renumber blocks so that consecutive unit
@@ -236,10 +270,10 @@ struct UpTile {
 };
 
 template <int NT>
-__device__ __forceinline__ void up_issue(UpRaw<NT>& raw, long tile, long G, const PlanRO& pv,
+__device__ __forceinline__ void up_issue(UpRaw<NT>& raw, int tile, int G, const PlanRO& pv,
                                          const int* perm, int lane) {
-  const int pass = (int)(tile / G);
-  raw.g = (int)(tile % G);
+  const int pass = tile / G;
+  raw.g = tile - pass * G;
   raw.ex = pv.expert[pass];
   raw.tb = pv.beg[pass];
   raw.tc = pv.cnt[pass];
@@ -276,26 +310,25 @@ __global__ __launch_bounds__(256) void ffn_up_sk_kernel(
   constexpr int KUNIT = 4 * 32 * S;
   __shared__ f32x4 red[2][4][2 * NT][kWave];
   const PlanRO pv = plan_ro(plan, pmax);
-  const long P = pv.hdr[0];
-  const long G = I / UP_ROWS, C = H / KUNIT;
-  const long U = P * G * C;
+  const int P = pv.hdr[0];
+  const int G = I / UP_ROWS, C = H / KUNIT;
+  const long U = (long)P * G * C;
   const int nb = (int)min((long)NB, U);
   const int b = xcd_block(blockIdx.x, NB);
   if (b >= nb) return;
-  const long s = first_unit(b, U, nb), e = first_unit(b + 1, U, nb);
+  const SkRange rg(b, U, nb, C);
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int kq = (lane >> 4) * 8 + wave * 32 * S;
   const size_t I_H = (size_t)I * H;
-  const long last_tile = (e - 1) / C;
 
   UpTile<NT> ts, tn;
   UpRaw<NT> rn;
   {
     UpRaw<NT> r0;
-    up_issue(r0, s / C, G, pv, perm, lane);
+    up_issue(r0, rg.ps.t, G, pv, perm, lane);
     up_finish(ts, r0, k, H, I, nmax, lane, kq);
   }
-  up_issue(rn, min(s / C + 1, last_tile), G, pv, perm, lane);
+  up_issue(rn, rg.next_tile(rg.ps.t), G, pv, perm, lane);
 
   f32x4 acc[2 * NT];
 #pragma unroll
@@ -304,14 +337,12 @@ __global__ __launch_bounds__(256) void ffn_up_sk_kernel(
   // End of the tile of unit u: add the waves' partials, complete the tile
   // (directly, or through the cross-block fixup) and write a = silu(g) * u.
   int parity = 0;
-  auto tile_end = [&](long u) {
-    const long tile = u / C;
+  auto tile_end = [&](int tile) {
     block_reduce(acc, red, parity, wave, lane);
     parity ^= 1;
     if (wave == 0) {
-      const bool split = tile * C < s || tile * C + C > e;
       bool done = true;
-      if (split) done = fixup(acc, slots, counters, tile, C, U, nb, b, lane);
+      if (rg.split(tile)) done = fixup(acc, slots, counters, tile, C, U, nb, b, lane);
       if (done) {
         // lane l: rows g*16 + 4*(l/16) + j of token slot l % 16 of each N-tile
         const int ir = ts.g * UP_ROWS + (lane >> 4) * 4;
@@ -341,29 +372,28 @@ __global__ __launch_bounds__(256) void ffn_up_sk_kernel(
   // One unit: start the loads of unit u + 1 (in the next tile when u ends
   // one), multiply unit u, and finish its tile when u is the tile's last unit
   // in this block. Returns false after the block's last unit.
-  auto step = [&](UpOps<NT, S>& cur, UpOps<NT, S>& nxt, long& u) -> bool {
-    const long un = u + 1 < e ? u + 1 : u;  // past the end: reload u (unused)
-    const bool crosses = un != u && un % C == 0;
-    if (crosses) {
+  auto step = [&](UpOps<NT, S>& cur, UpOps<NT, S>& nxt, Pos& p) -> bool {
+    const Pos pn = rg.next(p);  // past the end: reload p (unused)
+    if (pn.t != p.t) {
       up_finish(tn, rn, k, H, I, nmax, lane, kq);
-      up_issue(rn, min(un / C + 1, last_tile), G, pv, perm, lane);  // the tile after
+      up_issue(rn, rg.next_tile(pn.t), G, pv, perm, lane);  // the tile after
     } else {
       tn = ts;
     }
-    const size_t kb = (size_t)(un % C) * KUNIT;
+    const size_t kb = (size_t)pn.kc * KUNIT;
     up_load(nxt, w1 + tn.wrow, w1 + tn.wrow + I_H, x, tn.xoff, kb);
     up_compute<NT, S>(cur, ts.ntiles, acc);
-    if (u % C == C - 1 || u == e - 1) tile_end(u);
-    if (u + 1 >= e) return false;
+    if (rg.ends_tile(p)) tile_end(p.t);
+    if (rg.last(p)) return false;
     ts = tn;
-    u = un;
+    p = pn;
     return true;
   };
 
   UpOps<NT, S> b0, b1;
-  up_load(b0, w1 + ts.wrow, w1 + ts.wrow + I_H, x, ts.xoff, (size_t)(s % C) * KUNIT);
-  long u = s;
-  while (step(b0, b1, u) && step(b1, b0, u)) {
+  up_load(b0, w1 + ts.wrow, w1 + ts.wrow + I_H, x, ts.xoff, (size_t)rg.ps.kc * KUNIT);
+  Pos p = rg.ps;
+  while (step(b0, b1, p) && step(b1, b0, p)) {
   }
 }
 
@@ -431,9 +461,9 @@ struct DownTile {
   size_t hrow[NT];   // lane's row of h (+ its K offset), per N-tile
 };
 
-__device__ __forceinline__ void down_issue(DownRaw& raw, long tile, long G, const PlanRO& pv) {
-  const int pass = (int)(tile / G);
-  raw.g = (int)(tile % G);
+__device__ __forceinline__ void down_issue(DownRaw& raw, int tile, int G, const PlanRO& pv) {
+  const int pass = tile / G;
+  raw.g = tile - pass * G;
   raw.ex = pv.expert[pass];
   raw.tb = pv.beg[pass];
   raw.tc = pv.cnt[pass];
@@ -463,39 +493,36 @@ __global__ __launch_bounds__(256) void ffn_down_sk_kernel(
   constexpr int NACC = NT * DOWN_GROUPS;
   __shared__ f32x4 red[2][4][NACC][kWave];
   const PlanRO pv = plan_ro(plan, pmax);
-  const long P = pv.hdr[0];
-  const long G = H / DOWN_ROWS, C = I / KUNIT;
-  const long U = P * G * C;
+  const int P = pv.hdr[0];
+  const int G = H / DOWN_ROWS, C = I / KUNIT;
+  const long U = (long)P * G * C;
   const int nb = (int)min((long)NB, U);
   const int b = xcd_block(blockIdx.x, NB);
   if (b >= nb) return;
-  const long s = first_unit(b, U, nb), e = first_unit(b + 1, U, nb);
+  const SkRange rg(b, U, nb, C);
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int kq = (lane >> 4) * 8 + wave * 32 * S;
-  const long last_tile = (e - 1) / C;
 
   DownTile<NT> ts, tn;
   DownRaw rn;
   {
     DownRaw r0;
-    down_issue(r0, s / C, G, pv);
+    down_issue(r0, rg.ps.t, G, pv);
     down_finish(ts, r0, H, I, lane, kq);
   }
-  down_issue(rn, min(s / C + 1, last_tile), G, pv);
+  down_issue(rn, rg.next_tile(rg.ps.t), G, pv);
 
   f32x4 acc[NACC];
 #pragma unroll
   for (int i = 0; i < NACC; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   int parity = 0;
-  auto tile_end = [&](long u) {
-    const long tile = u / C;
+  auto tile_end = [&](int tile) {
     block_reduce(acc, red, parity, wave, lane);
     parity ^= 1;
     if (wave == 0) {
-      const bool split = tile * C < s || tile * C + C > e;
       bool done = true;
-      if (split) done = fixup(acc, slots, counters, tile, C, U, nb, b, lane);
+      if (rg.split(tile)) done = fixup(acc, slots, counters, tile, C, U, nb, b, lane);
       if (done) {
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
@@ -512,29 +539,28 @@ __global__ __launch_bounds__(256) void ffn_down_sk_kernel(
     for (int i = 0; i < NACC; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   };
 
-  auto step = [&](DownOps<NT, S>& cur, DownOps<NT, S>& nxt, long& u) -> bool {
-    const long un = u + 1 < e ? u + 1 : u;
-    const bool crosses = un != u && un % C == 0;
-    if (crosses) {
+  auto step = [&](DownOps<NT, S>& cur, DownOps<NT, S>& nxt, Pos& p) -> bool {
+    const Pos pn = rg.next(p);
+    if (pn.t != p.t) {
       down_finish(tn, rn, H, I, lane, kq);
-      down_issue(rn, min(un / C + 1, last_tile), G, pv);  // the tile after
+      down_issue(rn, rg.next_tile(pn.t), G, pv);  // the tile after
     } else {
       tn = ts;
     }
-    const size_t kb = (size_t)(un % C) * KUNIT;
+    const size_t kb = (size_t)pn.kc * KUNIT;
     down_load(nxt, w2 + tn.wrow, I, h_hi, h_lo, tn.hrow, kb);
     down_compute<NT, S>(cur, ts.ntiles, acc);
-    if (u % C == C - 1 || u == e - 1) tile_end(u);
-    if (u + 1 >= e) return false;
+    if (rg.ends_tile(p)) tile_end(p.t);
+    if (rg.last(p)) return false;
     ts = tn;
-    u = un;
+    p = pn;
     return true;
   };
 
   DownOps<NT, S> b0, b1;
-  down_load(b0, w2 + ts.wrow, I, h_hi, h_lo, ts.hrow, (size_t)(s % C) * KUNIT);
-  long u = s;
-  while (step(b0, b1, u) && step(b1, b0, u)) {
+  down_load(b0, w2 + ts.wrow, I, h_hi, h_lo, ts.hrow, (size_t)rg.ps.kc * KUNIT);
+  Pos p = rg.ps;
+  while (step(b0, b1, p) && step(b1, b0, p)) {
   }
 }
 
@@ -675,13 +701,6 @@ __device__ __forceinline__ void pf_finish(PfTile<NT>& st, const PfRaw<NT>& raw, 
     st.roff[i] = (size_t)r * K + q * 8;
   }
 }
-
-// Position in the unit sequence: tile t, K chunk kc. Tiles are numbered
-// pass-major (t = pass * G + g) and fit in 32 bits; every step advances the
-// position by additions only.
-struct Pos {
-  int t, kc;
-};
 
 template <int NT, bool UP>
 __global__ __launch_bounds__(PF_THREADS) void ffn_pf_kernel(
@@ -869,7 +888,7 @@ int device_cus() {
 
 // Resident blocks of `threads` threads of `kernel` on the current device (cached).
 template <typename K>
-int resident_blocks(K kernel, int threads = 256) {
+int resident_blocks(K kernel, int threads = 256, int cap = 8) {
   static int cached[64] = {0};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
@@ -878,7 +897,7 @@ int resident_blocks(K kernel, int threads = 256) {
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess ||
         per_cu <= 0)
       per_cu = 1;
-    if (per_cu > 8) per_cu = 8;  // the workspace holds slots for 8 blocks per CU
+    if (per_cu > cap) per_cu = cap;  // at most 8: the workspace holds slots for 8 blocks per CU
     cached[dev] = per_cu * device_cus();
   }
   return cached[dev];
@@ -899,7 +918,7 @@ size_t a256(size_t n) { return (n + 255) & ~(size_t)255; }
 
 template <int NT>
 int up_blocks() {
-  if constexpr (NT <= 2) return resident_blocks(ffn_up_sk_kernel<NT, UP_STEPS>);
+  if constexpr (NT <= 2) return resident_blocks(ffn_up_sk_kernel<NT, UP_STEPS>, 256, UP_CAP);
   else return resident_blocks(ffn_pf_kernel<NT, true>, PF_THREADS);
 }
 template <int NT>
