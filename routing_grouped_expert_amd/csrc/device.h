@@ -24,20 +24,42 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
   return static_cast<uint16_t>(u >> 16);
 }
 
-__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int mask) {
-  uint32_t lo = static_cast<uint32_t>(v), hi = static_cast<uint32_t>(v >> 32);
-  lo = __shfl_xor(lo, mask, kWave);
-  hi = __shfl_xor(hi, mask, kWave);
+// DPP move within rows of 16 lanes (CTRL: a gfx9 dpp_ctrl code, e.g. 0x121 +
+// n - 1 for row_ror:n); every lane of a full wave has a source.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), CTRL, 0xF, 0xF, false));
+}
+
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+  const uint32_t lo = dpp_u32<CTRL>(static_cast<uint32_t>(v));
+  const uint32_t hi = dpp_u32<CTRL>(static_cast<uint32_t>(v >> 32));
   return (static_cast<uint64_t>(hi) << 32) | lo;
 }
 
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int lane) {
+  const uint32_t lo = __builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(v)), lane);
+  const uint32_t hi = __builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(v >> 32)), lane);
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+// Maximum over a full wave, wave-uniform: rotations by 1, 2, 4, 8 within each
+// row of 16 lanes leave every lane with its row's maximum, then the four rows
+// are combined from one lane each.
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+  uint64_t o;
+  o = dpp_u64<0x121>(v); v = o > v ? o : v;
+  o = dpp_u64<0x122>(v); v = o > v ? o : v;
+  o = dpp_u64<0x124>(v); v = o > v ? o : v;
+  o = dpp_u64<0x128>(v); v = o > v ? o : v;
+  uint64_t r = readlane_u64(v, 0);
 #pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) {
-    uint64_t o = shfl_xor_u64(v, m);
-    v = o > v ? o : v;
+  for (int row = 1; row < 4; ++row) {
+    const uint64_t x = readlane_u64(v, 16 * row);
+    r = x > r ? x : r;
   }
-  return v;
+  return r;
 }
 
 // Butterfly sum: every lane ends with the same value, summed in the same

@@ -11,8 +11,10 @@
 // entries keep ascending t, hence ascending r. Masks are built with LDS
 // atomic OR (order-free, so the result is deterministic).
 //
-// T <= 64: one block does all of it in LDS. Larger T: three kernels (tile
-// masks, scan, scatter) through the workspace.
+// T <= 64: one block does all of it in LDS. Larger T: three kernels through
+// the workspace: tile masks; a scan over the tiles of each expert (a thread per
+// expert), whose last block to finish scans the local experts' counts into
+// offsets; scatter.
 #include "device.h"
 
 namespace moe {
@@ -61,10 +63,12 @@ __global__ __launch_bounds__(1024) void permute_small_kernel(const int* __restri
 // Grid: one block per 64-token tile. masks[tile * E + e].
 __global__ __launch_bounds__(256) void tile_masks_kernel(const int* __restrict__ ids, int T, int k,
                                                          int E,
-                                                         unsigned long long* __restrict__ masks) {
+                                                         unsigned long long* __restrict__ masks,
+                                                         int* __restrict__ done) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   unsigned long long* mask = reinterpret_cast<unsigned long long*>(smem);
   const int b = blockIdx.x, tid = threadIdx.x;
+  if (b == 0 && tid == 0) *done = 0;  // the scan kernel's arrival counter
   for (int e = tid; e < E; e += blockDim.x) mask[e] = 0ull;
   __syncthreads();
   const int t0 = b * TILE;
@@ -78,39 +82,58 @@ __global__ __launch_bounds__(256) void tile_masks_kernel(const int* __restrict__
   for (int e = tid; e < E; e += blockDim.x) masks[(size_t)b * E + e] = mask[e];
 }
 
-// One block of 1024 threads. counts over all E; offsets over the share;
-// base[tile * L + i] = offsets[i] + entries of local expert i in earlier tiles.
-// Dynamic LDS: (L + 1) ints + 16 ints.
-__global__ __launch_bounds__(1024) void scan_kernel(const unsigned long long* __restrict__ masks,
-                                                    int nb, int E, int first, int L,
-                                                    int* __restrict__ counts,
-                                                    int* __restrict__ offsets,
-                                                    int* __restrict__ base) {
+// Grid: ceil(E / 64) blocks of 4 waves; lane j of every wave owns expert
+// 64 * block + j and wave w the w-th quarter of the tiles: counts[e], and
+// base[tile * L + i] = entries of local expert i in earlier tiles. The last
+// block to finish writes offsets, the exclusive scan of the local experts'
+// counts. Dynamic LDS: (L + 1) + 16 ints.
+__global__ __launch_bounds__(256) void expert_scan_kernel(const unsigned long long* __restrict__ masks,
+                                                          int nb, int E, int first, int L,
+                                                          int* counts, int* __restrict__ offsets,
+                                                          int* __restrict__ base, int* done) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  __shared__ int part[4][kWave];
+  __shared__ int is_last;
   int* off = reinterpret_cast<int*>(smem);
-  int* tmp = off + (L + 1);
-  const int tid = threadIdx.x, nt = blockDim.x;
-  for (int e = tid; e < E; e += nt) {
-    int c = 0;
-    for (int b = 0; b < nb; ++b) c += __popcll(masks[(size_t)b * E + e]);
-    counts[e] = c;
-    if (e >= first && e < first + L) off[e - first] = c;
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+  const int e = blockIdx.x * kWave + lane;
+  const int per = (nb + 3) / 4;
+  const int b0 = min(nb, wave * per), b1 = min(nb, b0 + per);
+  int c = 0;
+  if (e < E) {
+#pragma unroll 8
+    for (int b = b0; b < b1; ++b) c += __popcll(masks[(size_t)b * E + e]);
   }
+  part[wave][lane] = c;
   __syncthreads();
-  block_exclusive_scan(off, L, tmp);
-  for (int i = tid; i <= L; i += nt) offsets[i] = off[i];
-  for (int i = tid; i < L; i += nt) {
-    int run = off[i];
-    for (int b = 0; b < nb; ++b) {
+  int run = 0;  // entries of expert e in tiles before b0
+  for (int w = 0; w < wave; ++w) run += part[w][lane];
+  const int i = e - first;
+  if (e < E && i >= 0 && i < L) {
+#pragma unroll 8
+    for (int b = b0; b < b1; ++b) {
       base[(size_t)b * L + i] = run;
-      run += __popcll(masks[(size_t)b * E + first + i]);
+      run += __popcll(masks[(size_t)b * E + e]);
     }
   }
+  if (wave == 0 && e < E) counts[e] = part[0][lane] + part[1][lane] + part[2][lane] + part[3][lane];
+  __threadfence();  // counts visible before this block is counted
+  __syncthreads();
+  if (tid == 0) is_last = atomicAdd(done, 1) == (int)gridDim.x - 1;
+  __syncthreads();
+  if (!is_last) return;
+  __threadfence();
+  for (int j = tid; j < L; j += blockDim.x)
+    off[j] = __hip_atomic_load(&counts[first + j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  block_exclusive_scan(off, L, off + L + 1);
+  for (int j = tid; j <= L; j += blockDim.x) offsets[j] = off[j];
 }
 
 __global__ __launch_bounds__(256) void scatter_kernel(const int* __restrict__ ids, int T, int k,
                                                       int E, int first, int L,
                                                       const unsigned long long* __restrict__ masks,
+                                                      const int* __restrict__ offsets,
                                                       const int* __restrict__ base,
                                                       int* __restrict__ perm,
                                                       int* __restrict__ e2p) {
@@ -125,7 +148,8 @@ __global__ __launch_bounds__(256) void scatter_kernel(const int* __restrict__ id
     if (e >= first && e < first + L) {
       const int tl = q / k;
       const unsigned long long m = masks[(size_t)b * E + e];
-      p = base[(size_t)b * L + (e - first)] + __popcll(m & ((1ull << tl) - 1ull));
+      p = offsets[e - first] + base[(size_t)b * L + (e - first)] +
+          __popcll(m & ((1ull << tl) - 1ull));
       perm[p] = r;
     }
     e2p[r] = p;
@@ -133,13 +157,15 @@ __global__ __launch_bounds__(256) void scatter_kernel(const int* __restrict__ id
 }
 }  // namespace
 
+// Workspace for T > 64: tile masks [nb, E] u64, bases [nb, L] int, and the
+// scan kernel's arrival counter.
 size_t permute_workspace_bytes(int T, int E, int L) {
   if (T <= TILE) return 0;
   const size_t nb = (T + TILE - 1) / TILE;
   size_t masks = nb * (size_t)E * 8;
   masks = (masks + 255) & ~(size_t)255;
   size_t base = nb * (size_t)(L > 0 ? L : 1) * 4;
-  return masks + ((base + 255) & ~(size_t)255);
+  return masks + ((base + 255) & ~(size_t)255) + 256;
 }
 
 hipError_t launch_permute(const int* ids, int T, int k, int E, int first, int L, int* counts,
@@ -155,18 +181,21 @@ hipError_t launch_permute(const int* ids, int T, int k, int E, int first, int L,
   }
   const int nb = (T + TILE - 1) / TILE;
   unsigned long long* masks = static_cast<unsigned long long*>(ws);
-  size_t mbytes = ((size_t)nb * E * 8 + 255) & ~(size_t)255;
+  const size_t mbytes = ((size_t)nb * E * 8 + 255) & ~(size_t)255;
+  const size_t bbytes = ((size_t)nb * (L > 0 ? L : 1) * 4 + 255) & ~(size_t)255;
   int* base = reinterpret_cast<int*>(static_cast<char*>(ws) + mbytes);
+  int* done = reinterpret_cast<int*>(static_cast<char*>(ws) + mbytes + bbytes);
   hipLaunchKernelGGL(tile_masks_kernel, dim3(nb), dim3(256), (size_t)E * 8, stream, ids, T, k, E,
-                     masks);
+                     masks, done);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), (size_t)(L + 1) * 4 + 16 * 4, stream, masks,
-                     nb, E, first, L, counts, offsets, base);
+  hipLaunchKernelGGL(expert_scan_kernel, dim3((E + kWave - 1) / kWave), dim3(256),
+                     (size_t)(L + 1 + 16) * 4, stream, masks, nb, E, first, L, counts, offsets,
+                     base, done);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(scatter_kernel, dim3(nb), dim3(256), 0, stream, ids, T, k, E, first, L, masks,
-                     base, perm, e2p);
+                     offsets, base, perm, e2p);
   return hipGetLastError();
 }
 

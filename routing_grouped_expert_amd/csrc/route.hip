@@ -39,13 +39,33 @@ __device__ __forceinline__ int key_id(uint64_t key) {
   return static_cast<int>(0xFFFFFFFFu - static_cast<uint32_t>(key));
 }
 
+// Lane-local top two of the keys below `limit` (0 = none).
+template <int VPL>
+__device__ __forceinline__ void top2_below(const uint64_t (&key)[VPL], uint64_t limit, uint64_t& h1,
+                                           uint64_t& h2) {
+  h1 = 0;
+  h2 = 0;
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) {
+    const uint64_t k = key[i] < limit ? key[i] : 0ull;
+    const bool c1 = k > h1, c2 = k > h2;
+    h2 = c1 ? h1 : (c2 ? k : h2);
+    h1 = c1 ? k : h1;
+  }
+}
+
+// Selection: every lane keeps the two largest of its keys not yet taken
+// (h1 > h2). A round takes the wave-wide maximum of the h1s; the lane that
+// held it moves h2 up, and when it wins a second time (its h2 already moved
+// up) it rescans its keys below the last one it gave. Lane j keeps the key
+// taken in round j.
 template <int VPL>
 __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ logits, int T, int E,
                                                    int k, int* __restrict__ ids,
                                                    float* __restrict__ weights) {
   const int lane = threadIdx.x % kWave;
   const int t = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
-  if (t >= T) return;
+  if (t >= T) return;  // whole waves leave: every selection round runs on a full wave
   const float* l = logits + (size_t)t * E;
   uint64_t key[VPL];
 #pragma unroll
@@ -53,22 +73,31 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
     const int e = lane + kWave * i;
     key[i] = e < E ? make_key(l[e], e) : 0ull;  // a valid key is never 0
   }
-  uint64_t mine = 0;  // lane j keeps the key of selection j
+  uint64_t h1, h2;
+  top2_below(key, ~0ull, h1, h2);
+  bool h2_fresh = true;  // h2 is this lane's second largest key below h1
+  uint64_t mine = 0, top = 0;
   for (int j = 0; j < k; ++j) {
-    uint64_t best = key[0];
-#pragma unroll
-    for (int i = 1; i < VPL; ++i) best = key[i] > best ? key[i] : best;
-    best = wave_max_u64(best);
-#pragma unroll
-    for (int i = 0; i < VPL; ++i)
-      if (key[i] == best) key[i] = 0ull;
+    const uint64_t best = wave_max_u64(h1);
+    if (j == 0) top = best;
     if (lane == j) mine = best;
+    const bool win = h1 == best;  // keys are unique: one lane
+    const bool rescan = win && !h2_fresh;
+    if (win) {
+      h1 = h2;
+      h2_fresh = false;
+    }
+    if (__builtin_amdgcn_ballot_w64(rescan)) {
+      if (rescan) {
+        top2_below(key, best, h1, h2);
+        h2_fresh = true;
+      }
+    }
   }
-  // Lane 0 holds the first (largest) selection.
-  const uint32_t top_bits = __shfl(static_cast<uint32_t>(mine >> 32), 0, kWave);
-  const float top = key_value(static_cast<uint64_t>(top_bits) << 32);
-  const float ex = lane < k ? expf(key_value(mine) - top) : 0.0f;
-  const float s = wave_sum_f32(ex);
+  const float topv = key_value(top);
+  const float ex = lane < k ? expf(key_value(mine) - topv) : 0.0f;
+  float s = 0.0f;  // sum in slot order
+  for (int j = 0; j < k; ++j) s += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ex), j));
   if (lane < k) {
     ids[(size_t)t * k + lane] = key_id(mine);
     weights[(size_t)t * k + lane] = ex / s;
