@@ -904,33 +904,35 @@ int resident_blocks(K kernel, int threads = 256, int cap = 8) {
 }
 
 // Token tiles (of 16) per pass, from twice the mean entries per local expert
-// (an expert with more entries takes further passes), capped by T (a token
-// picks an expert at most once). 1 or 2: the K-split kernels; 4 or 8: the
-// prefill kernels.
+// (an expert with more entries takes further passes, each reading its weights
+// again), capped by T (a token picks an expert at most once). 1: the K-split
+// kernels; 4 or 8: the kernels with token rows staged in LDS. Between 16 and
+// 32 the staged kernels with 4 tiles win over 2-tile passes: on the
+// fine-grained shape (T512 H7168 I2048 E256 top-8) 4.05 ms against 5.46 ms,
+// mostly by not repeating passes for the experts above 32 entries.
 int pick_nt(int T, int k, int L) {
   const long bound = T;
   const long twice_mean = L > 0 ? (2L * T * k + L - 1) / L : bound;
   const long want = twice_mean < bound ? twice_mean : bound;
-  return want <= 16 ? 1 : want <= 32 ? 2 : want <= 64 ? 4 : 8;
+  return want <= 16 ? 1 : want <= 64 ? 4 : 8;
 }
 
 size_t a256(size_t n) { return (n + 255) & ~(size_t)255; }
 
 template <int NT>
 int up_blocks() {
-  if constexpr (NT <= 2) return resident_blocks(ffn_up_sk_kernel<NT, UP_STEPS>, 256, UP_CAP);
+  if constexpr (NT == 1) return resident_blocks(ffn_up_sk_kernel<NT, UP_STEPS>, 256, UP_CAP);
   else return resident_blocks(ffn_pf_kernel<NT, true>, PF_THREADS);
 }
 template <int NT>
 int down_blocks() {
-  if constexpr (NT <= 2) return resident_blocks(ffn_down_sk_kernel<NT, DOWN_STEPS>);
+  if constexpr (NT == 1) return resident_blocks(ffn_down_sk_kernel<NT, DOWN_STEPS>);
   else return resident_blocks(ffn_pf_kernel<NT, false>, PF_THREADS);
 }
 
 int blocks_for(int NT, bool up) {
   switch (NT) {
     case 1: return up ? up_blocks<1>() : down_blocks<1>();
-    case 2: return up ? up_blocks<2>() : down_blocks<2>();
     case 4: return up ? up_blocks<4>() : down_blocks<4>();
     default: return up ? up_blocks<8>() : down_blocks<8>();
   }
@@ -954,7 +956,7 @@ SkLayout sk_layout(int T, int k, int L, int NT) {
   o.nb_down = blocks_for(NT, false);
   const int nbm = o.nb_up > o.nb_down ? o.nb_up : o.nb_down;
   o.plan = 0;
-  o.subs = NT <= 2 ? 1 : PF_WAVES;
+  o.subs = NT == 1 ? 1 : PF_WAVES;
   o.counters = a256((size_t)(4 + 3 * o.pmax) * 4);
   o.slots = o.counters + a256((size_t)2 * o.subs * nbm * 4);
   o.total = o.slots + a256((size_t)2 * o.subs * nbm * (4 * NT) * kWave * 16);
@@ -975,7 +977,7 @@ hipError_t launch_sk_nt(const uint16_t* x, const int* perm, const int* offsets, 
                      offsets, L, nmax, NT * 16, plan, lo.pmax, counters, 2 * lo.subs * nbm);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  if constexpr (NT <= 2) {
+  if constexpr (NT == 1) {
     hipLaunchKernelGGL((ffn_up_sk_kernel<NT, UP_STEPS>), dim3(lo.nb_up), dim3(256), 0, stream, x,
                        perm, k, H, I, nmax, w1, plan, lo.pmax, slots, counters, h_hi, h_lo,
                        lo.nb_up);
@@ -986,7 +988,7 @@ hipError_t launch_sk_nt(const uint16_t* x, const int* perm, const int* offsets, 
   }
   err = hipGetLastError();
   if (err != hipSuccess) return err;
-  if constexpr (NT <= 2) {
+  if constexpr (NT == 1) {
     hipLaunchKernelGGL((ffn_down_sk_kernel<NT, DOWN_STEPS>), dim3(lo.nb_down), dim3(256), 0,
                        stream, h_hi, h_lo, H, I, w2, plan, lo.pmax, slots, counters + lo.subs * nbm,
                        out, lo.nb_down);
@@ -1003,7 +1005,7 @@ bool ffn_sk_applies(const void* x, const void* w1, const void* w2, int T, int k,
                     int I) {
   auto al = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
   if (!(al(x) && al(w1) && al(w2))) return false;
-  if (pick_nt(T, k, L) <= 2)
+  if (pick_nt(T, k, L) == 1)
     return H % UP_KUNIT == 0 && I % DOWN_KUNIT == 0 && I % UP_ROWS == 0 && H % DOWN_ROWS == 0;
   return H % PF_K == 0 && I % PF_K == 0 && H % PF_ROWS == 0 && I % PF_UP_COLS == 0;
 }
@@ -1019,7 +1021,6 @@ hipError_t launch_grouped_ffn_sk(const uint16_t* x, const int* perm, const int* 
   char* w = static_cast<char*>(ws);
   switch (pick_nt(T, k, L)) {
     case 1: return launch_sk_nt<1>(x, perm, offsets, L, T, k, H, I, w1, w2, h_hi, h_lo, out, w, stream);
-    case 2: return launch_sk_nt<2>(x, perm, offsets, L, T, k, H, I, w1, w2, h_hi, h_lo, out, w, stream);
     case 4: return launch_sk_nt<4>(x, perm, offsets, L, T, k, H, I, w1, w2, h_hi, h_lo, out, w, stream);
     default: return launch_sk_nt<8>(x, perm, offsets, L, T, k, H, I, w1, w2, h_hi, h_lo, out, w, stream);
   }

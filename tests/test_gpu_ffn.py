@@ -67,9 +67,10 @@ def test_ffn_fast_path_tiles(T, E, k):
     check_ffn(T, 256, 384, E, k, 0, E)
 
 
-# Persistent stream-K path (H, I multiples of 256; at most 32 mean-doubled
-# entries per expert): every tile cut between blocks when there are fewer
-# units than blocks, long K ranges, NT = 1 and 2, several passes per expert.
+# Persistent stream-K path (H, I multiples of 256; at most 16 mean-doubled
+# entries per expert, one 16-token tile per pass): every tile cut between
+# blocks when there are fewer units than blocks, long K ranges, several passes
+# per expert; (60, 512, 768) doubles to 30 and takes the staged path.
 @pytest.mark.parametrize("T,H,I,E,k", [(24, 512, 512, 8, 2), (60, 512, 768, 8, 2),
                                        (32, 4096, 512, 8, 2), (16, 256, 4096, 4, 1),
                                        (200, 1024, 512, 64, 2)])
@@ -79,8 +80,8 @@ def test_ffn_stream_k(T, H, I, E, k):
 
 def test_ffn_stream_k_skewed_passes():
     """One expert takes every token (three 16-token passes), others few."""
-    T, E, k = 40, 8, 2
-    ids = np.stack([np.zeros(T, np.int32), 1 + np.arange(T, dtype=np.int32) % 7], 1)
+    T, E, k = 40, 16, 2
+    ids = np.stack([np.zeros(T, np.int32), 1 + np.arange(T, dtype=np.int32) % 15], 1)
     check_ffn(T, 512, 512, E, k, 0, E, ids=ids)
 
 
@@ -89,10 +90,10 @@ def test_ffn_stream_k_share():
 
 
 # Prefill path (many entries per expert: 4 or 8 token tiles per pass, the
-# token rows staged in LDS per block; H a multiple of 256, I of 128): one
+# token rows staged in LDS per block; H a multiple of 512, I of 256): one
 # pass, several passes, a skewed expert, a share.
 @pytest.mark.parametrize("T,H,I,E,k", [(96, 512, 256, 8, 2), (256, 512, 512, 8, 2),
-                                       (512, 256, 256, 4, 2), (200, 768, 384, 16, 8)])
+                                       (512, 512, 256, 4, 2), (200, 1024, 512, 16, 8)])
 def test_ffn_prefill(T, H, I, E, k):
     check_ffn(T, H, I, E, k, 0, E)
 
@@ -101,13 +102,13 @@ def test_ffn_prefill_whole_rounds():
     """512 experts of ~64 entries: 512 up tiles and 512 down tiles, at least
     twice the resident blocks of a 256-CU part, so whole rounds of tiles (one
     tile per block, no cut) run before the stream-K remainder."""
-    check_ffn(4096, 256, 128, 512, 8, 0, 512)
+    check_ffn(4096, 512, 256, 512, 8, 0, 512)
 
 
 def test_ffn_prefill_skewed():
     T, E, k = 300, 6, 2
     ids = np.stack([np.full(T, 2, np.int32), (3 + np.arange(T, dtype=np.int32) % 3)], 1)
-    check_ffn(T, 256, 256, E, k, 0, E, ids=ids)
+    check_ffn(T, 512, 256, E, k, 0, E, ids=ids)
 
 
 def test_ffn_prefill_share():
