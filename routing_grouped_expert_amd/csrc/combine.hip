@@ -28,22 +28,42 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   __syncthreads();
   uint16_t* yt = y + (size_t)t * H;
   if (VEC) {
-    for (int c = threadIdx.x * 4; c < H; c += blockDim.x * 4) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    // Up to 8 column chunks of 1024 per round; for each selection j the
+    // chunks' loads are issued together (rows of skipped selections read row
+    // 0 and are multiplied by nothing), so a round waits for memory k times.
+    constexpr int CH = 8;
+    typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
+    for (int c0 = threadIdx.x * 4; c0 < H; c0 += CH * blockDim.x * 4) {
+      f32x4 acc[CH];
+#pragma unroll
+      for (int i = 0; i < CH; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
       for (int j = 0; j < k; ++j) {
         const int p = s_p[j];
+        const float wj = p < 0 ? 0.f : s_w[j];
+        const float* row = eo + (size_t)(p < 0 ? 0 : p) * H;
+        f32x4 v[CH];
+#pragma unroll
+        for (int i = 0; i < CH; ++i) {
+          const int c = c0 + i * blockDim.x * 4;
+          v[i] = c < H ? *reinterpret_cast<const f32x4*>(row + c) : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
         if (p < 0) continue;
-        const f32x4 v = *reinterpret_cast<const f32x4*>(eo + (size_t)p * H + c);
-        const float wj = s_w[j];
-        acc[0] = fmaf(wj, v[0], acc[0]);
-        acc[1] = fmaf(wj, v[1], acc[1]);
-        acc[2] = fmaf(wj, v[2], acc[2]);
-        acc[3] = fmaf(wj, v[3], acc[3]);
+#pragma unroll
+        for (int i = 0; i < CH; ++i) {
+          acc[i][0] = fmaf(wj, v[i][0], acc[i][0]);
+          acc[i][1] = fmaf(wj, v[i][1], acc[i][1]);
+          acc[i][2] = fmaf(wj, v[i][2], acc[i][2]);
+          acc[i][3] = fmaf(wj, v[i][3], acc[i][3]);
+        }
       }
-      typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
-      *reinterpret_cast<u16x4*>(yt + c) =
-          u16x4{f32_to_bf16_bits(acc[0]), f32_to_bf16_bits(acc[1]), f32_to_bf16_bits(acc[2]),
-                f32_to_bf16_bits(acc[3])};
+#pragma unroll
+      for (int i = 0; i < CH; ++i) {
+        const int c = c0 + i * blockDim.x * 4;
+        if (c < H)
+          *reinterpret_cast<u16x4*>(yt + c) =
+              u16x4{f32_to_bf16_bits(acc[i][0]), f32_to_bf16_bits(acc[i][1]),
+                    f32_to_bf16_bits(acc[i][2]), f32_to_bf16_bits(acc[i][3])};
+      }
     }
   } else {
     for (int c = threadIdx.x; c < H; c += blockDim.x) {

@@ -15,6 +15,7 @@
 #include "device.h"
 
 #include <algorithm>
+#include <type_traits>
 
 namespace moe {
 
@@ -129,6 +130,30 @@ __global__ __launch_bounds__(256) void router_reduce_kernel(const double* __rest
 
 constexpr int SE = 8;  // experts per block in the few-token kernel
 
+// Sum over a full wave of fp64 values in a fixed order: rotations by 1, 2, 4,
+// 8 within each row of 16 lanes (DPP), then the four row sums in row order.
+__device__ __forceinline__ double wave_sum_f64(double v) {
+  auto rot = [](double x, auto ctrl) {
+    const uint64_t u = __builtin_bit_cast(uint64_t, x);
+    return __builtin_bit_cast(double, dpp_u64<decltype(ctrl)::value>(u));
+  };
+  v += rot(v, std::integral_constant<int, 0x121>{});
+  v += rot(v, std::integral_constant<int, 0x122>{});
+  v += rot(v, std::integral_constant<int, 0x124>{});
+  v += rot(v, std::integral_constant<int, 0x128>{});
+  const uint64_t u = __builtin_bit_cast(uint64_t, v);
+  double r = __builtin_bit_cast(double, readlane_u64(u, 0));
+  r += __builtin_bit_cast(double, readlane_u64(u, 16));
+  r += __builtin_bit_cast(double, readlane_u64(u, 32));
+  r += __builtin_bit_cast(double, readlane_u64(u, 48));
+  return r;
+}
+
+// One block per (token, 8 experts): the 256 threads split H in 4-wide pieces,
+// each keeps 8 fp64 partial sums; waves sum in a fixed order, then the block
+// adds the four wave sums in wave order. All of a thread's loads are issued
+// before its products (unrolled by 4 pieces), so a block waits for memory
+// about once.
 template <bool HAS_BIAS, bool VEC>
 __global__ __launch_bounds__(256) void router_rows_kernel(const uint16_t* __restrict__ x,
                                                           const float* __restrict__ wg,
@@ -145,19 +170,19 @@ __global__ __launch_bounds__(256) void router_rows_kernel(const uint16_t* __rest
   for (int j = 0; j < SE; ++j) acc[j] = 0.0;
   if (VEC) {
     typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
+#pragma unroll 4
     for (int h = tid * 4; h < H; h += 256 * 4) {
       const u16x4 xv = *reinterpret_cast<const u16x4*>(xr + h);
-      const double x0 = bf16_bits_to_f32(xv[0]), x1 = bf16_bits_to_f32(xv[1]);
-      const double x2 = bf16_bits_to_f32(xv[2]), x3 = bf16_bits_to_f32(xv[3]);
+      f32x4 w[SE];
 #pragma unroll
-      for (int j = 0; j < SE; ++j) {
-        if (j < ne) {
-          const f32x4 w = *reinterpret_cast<const f32x4*>(wr + (size_t)j * H + h);
-          acc[j] = fma(x0, (double)w[0], acc[j]);
-          acc[j] = fma(x1, (double)w[1], acc[j]);
-          acc[j] = fma(x2, (double)w[2], acc[j]);
-          acc[j] = fma(x3, (double)w[3], acc[j]);
-        }
+      for (int j = 0; j < SE; ++j)
+        w[j] = j < ne ? *reinterpret_cast<const f32x4*>(wr + (size_t)j * H + h)
+                      : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const double xc = bf16_bits_to_f32(xv[c]);
+#pragma unroll
+        for (int j = 0; j < SE; ++j) acc[j] = fma(xc, (double)w[j][c], acc[j]);
       }
     }
   } else {
@@ -170,9 +195,7 @@ __global__ __launch_bounds__(256) void router_rows_kernel(const uint16_t* __rest
   }
 #pragma unroll
   for (int j = 0; j < SE; ++j) {
-    double v = acc[j];
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
+    const double v = wave_sum_f64(acc[j]);
     if (lane == 0) part[wave][j] = v;
   }
   __syncthreads();
