@@ -8,7 +8,8 @@
 // resident number of blocks NB is launched and the work is cut into equal
 // contiguous ranges of units:
 //   tile = (pass, row group)   pass = up to NT*16 tokens of one expert
-//   unit = (tile, 256-wide K chunk); the 4 waves of a block take 64 each.
+//   unit = (tile, K chunk of 512 (up) or 1024 (down)), taken in two halves;
+//          the 4 waves of a block take a quarter of each half.
 // (With fewer units than resident blocks only the first U blocks take part,
 // so every participating block owns at least one unit.)
 // A block runs its units in order, adding its waves' partial sums in LDS in a
@@ -23,10 +24,9 @@
 // (page "FlashInfer MoE optimisation: overlapping grouped activation staging
 // on Ampere and Hopper", flashinfer PR #7368, section 1: route index divided
 // by the route divisor, 128-bit loads, absent members read as zero) are the B
-// operand, loaded per lane from L2 with 16-byte loads. Weight loads of the
-// next chunk are issued before the current chunk's MFMAs (section 2 of the
-// same page: the weight stream starts first and overlaps the activation
-// gather).
+// operand, loaded per lane from L2 with 16-byte loads. The loads of the next
+// half unit are issued before the current half's MFMAs (section 2 of the same
+// page: the weight stream starts first and overlaps the activation gather).
 //
 // up:   tile rows = 16 gate rows + the 16 matching up rows; the finished tile
 //       applies SwiGLU and writes a = silu(g) * u as hi = bf16(a),
@@ -39,16 +39,26 @@
 namespace moe {
 
 namespace {
-// MFMA K-steps (of 32) per wave per unit; a unit spans 4 waves.
+// Tile shapes, measured on MI355X at the decode shape (T32 H4096 I14336 E8
+// top-2; up kernel / down kernel, microseconds):
+//   up   1 gate group, 4 blocks per CU 354; 2 groups, 1 block per CU 320;
+//        2 groups, 2 blocks 392; 4 groups, 1 block 354
+//   down 8 groups, 1 block per CU 174; 4 groups 180-184; 16 groups 179;
+//        the 4-group tiles of units of 4 steps, 2 blocks per CU 176
+// A CU holding fewer, taller tiles keeps fewer weight rows open at once, and
+// the token bytes per weight byte shrink with the tile height.
+// MFMA K-steps (of 32) per wave per half unit; a unit is two halves, each
+// spanning the 4 waves.
 constexpr int UP_STEPS = 2;
-constexpr int DOWN_STEPS = 4;
-constexpr int UP_KUNIT = 4 * 32 * UP_STEPS;
-constexpr int DOWN_KUNIT = 4 * 32 * DOWN_STEPS;
-// Blocks per CU of the K-split up kernel: measured on MI355X at the decode
-// shape, 3, 4 and 5 resident blocks take 1.21x, 1x and 1.42x the time of 4.
-constexpr int UP_CAP = 4;
-constexpr int UP_ROWS = 16;       // gate rows (and as many up rows) per up tile
-constexpr int DOWN_GROUPS = 4;    // 16-row groups per down tile
+constexpr int DOWN_STEPS = 2;
+constexpr int UP_KUNIT = 2 * 4 * 32 * UP_STEPS;
+constexpr int DOWN_KUNIT = 2 * 4 * 32 * DOWN_STEPS;
+// Blocks per CU of the K-split kernels.
+constexpr int UP_CAP = 1;
+constexpr int DOWN_CAP = 1;
+constexpr int UP_RG = 2;          // 16-row gate groups (and as many up groups) per up tile
+constexpr int UP_ROWS = 16 * UP_RG;
+constexpr int DOWN_GROUPS = 8;    // 16-row groups per down tile
 constexpr int DOWN_ROWS = 16 * DOWN_GROUPS;
 
 // Plan layout (ints): [0] passes P, then pass_expert[Pmax], pass_beg[Pmax],
@@ -124,26 +134,44 @@ struct Pos {
   int t, kc;
 };
 
-// Block b's range [first_unit(b), first_unit(b + 1)) of U units of C chunks.
-struct SkRange {
-  Pos ps, pe;  // its first and last unit
-  int C;
-  __device__ SkRange(int b, long U, int NB, int C_) : C(C_) {
-    const long s = first_unit(b, U, NB), e = first_unit(b + 1, U, NB) - 1;
-    ps = Pos{(int)(s / C), (int)(s % C)};
-    pe = Pos{(int)(e / C), (int)(e % C)};
+// The units of a block: whole rounds of tiles first, then a stream-K share.
+// Of TT tiles of C units, R = TT / NB - 1 whole rounds are taken when
+// TT >= 2 NB (in round r block b takes tile r NB + b, so the blocks running
+// together on one XCD hold neighbouring tiles of the same pass and read its
+// token rows from the same L2); the remaining NB to 2 NB - 1 tiles, or all
+// tiles when TT < 2 NB, are cut into nb equal unit ranges. Only a tile cut by
+// a range boundary needs the cross-block fixup.
+struct Sched {
+  int C, NB, TD, nb;
+  long US;        // units of the stream-K part
+  Pos ps, pe, p0; // the block's first and last stream-K unit, its first unit
+  __device__ Sched(int b, int TT, int C_, int NB_) : C(C_), NB(NB_) {
+    const int R = TT >= 2 * NB ? TT / NB - 1 : 0;
+    TD = R * NB;
+    US = (long)(TT - TD) * C;
+    nb = (int)min((long)NB, US);
+    const long s = first_unit(b, US, nb), e = first_unit(b + 1, US, nb) - 1;
+    ps = Pos{TD + (int)(s / C), (int)(s % C)};
+    pe = Pos{TD + (int)(e / C), (int)(e % C)};
+    p0 = R > 0 ? Pos{b, 0} : ps;
   }
   __device__ bool last(Pos p) const { return p.t == pe.t && p.kc == pe.kc; }
   // the unit after p (p itself after the last)
   __device__ Pos next(Pos p) const {
     if (last(p)) return p;
-    return p.kc + 1 < C ? Pos{p.t, p.kc + 1} : Pos{p.t + 1, 0};
+    if (p.kc + 1 < C) return Pos{p.t, p.kc + 1};
+    if (p.t >= TD) return Pos{p.t + 1, 0};
+    return p.t + NB < TD ? Pos{p.t + NB, 0} : ps;
   }
-  __device__ int next_tile(int t) const { return t < pe.t ? t + 1 : pe.t; }
+  // the block's tile after t (t itself after the last)
+  __device__ int next_tile(int t) const {
+    if (t < TD) return t + NB < TD ? t + NB : ps.t;
+    return t < pe.t ? t + 1 : pe.t;
+  }
   __device__ bool ends_tile(Pos p) const { return p.kc == C - 1 || last(p); }
   // tile t is shared with another block
   __device__ bool split(int t) const {
-    return (t == ps.t && ps.kc > 0) || (t == pe.t && pe.kc < C - 1);
+    return t >= TD && ((t == ps.t && ps.kc > 0) || (t == pe.t && pe.kc < C - 1));
   }
 };
 
@@ -156,22 +184,30 @@ __device__ __forceinline__ int xcd_block(int b, int NB) {
   return NB % kXcds == 0 ? (b % kXcds) * (NB / kXcds) + b / kXcds : b;
 }
 
-// Sum the four waves' accumulators of one tile through LDS with one barrier:
-// every wave writes its own region, then wave 0 adds them in wave order
-// 0, 1, 2, 3 into `acc`. Regions alternate between two sets (`parity`), so a
-// region is rewritten only after the next tile's barrier, by which time wave 0
-// has read it. Every thread must call this.
+// Sum the four waves' accumulators of one tile through LDS, RCH f32x4 per
+// lane at a time: every wave writes its region, then wave 0 adds them in wave
+// order 0, 1, 2, 3 into `acc`. Rounds alternate between two buffers
+// (`parity`, carried from tile to tile), so a buffer is rewritten only after
+// the next round's barrier, by which time wave 0 has read it. Every thread
+// must call this.
+constexpr int RCH = 4;
 template <int N>
-__device__ __forceinline__ void block_reduce(f32x4 (&acc)[N], f32x4 (*red)[4][N][kWave],
-                                             int parity, int wave, int lane) {
+__device__ __forceinline__ void block_reduce(f32x4 (&acc)[N], f32x4 (*red)[4][RCH][kWave],
+                                             int& parity, int wave, int lane) {
+  static_assert(N % RCH == 0 || N < RCH, "rounds");
+  constexpr int W = N < RCH ? N : RCH;
 #pragma unroll
-  for (int i = 0; i < N; ++i) red[parity][wave][i][lane] = acc[i];
-  __syncthreads();
-  if (wave == 0) {
+  for (int r = 0; r < N; r += W) {
 #pragma unroll
-    for (int i = 0; i < N; ++i)
-      acc[i] = ((red[parity][0][i][lane] + red[parity][1][i][lane]) + red[parity][2][i][lane]) +
-               red[parity][3][i][lane];
+    for (int i = 0; i < W; ++i) red[parity][wave][i][lane] = acc[r + i];
+    __syncthreads();
+    if (wave == 0) {
+#pragma unroll
+      for (int i = 0; i < W; ++i)
+        acc[r + i] = ((red[parity][0][i][lane] + red[parity][1][i][lane]) + red[parity][2][i][lane]) +
+                     red[parity][3][i][lane];
+    }
+    parity ^= 1;
   }
 }
 
@@ -208,257 +244,226 @@ __device__ bool fixup(f32x4 (&part)[N], f32x4* slots, int* counters, long tile, 
 }
 
 // ----------------------------------------------------------------- up
-template <int NTILES, int S>
-__device__ __forceinline__ void up_mma(const bf16x8 (&ag)[S], const bf16x8 (&au)[S],
-                                       const bf16x8 (*bx)[S], f32x4* accg, f32x4* accu) {
-#pragma unroll
-  for (int s = 0; s < S; ++s) {
-#pragma unroll
-    for (int nt = 0; nt < NTILES; ++nt) {
-      accg[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ag[s], bx[nt][s], accg[nt], 0, 0, 0);
-      accu[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(au[s], bx[nt][s], accu[nt], 0, 0, 0);
-    }
-  }
-}
+// A tile is RG groups of 16 gate rows and the RG matching groups of up rows,
+// all multiplied by the same token fragment: the token bytes a wave loads per
+// weight byte are 1 / (2 RG), and on this chip the token loads share each
+// CU's vector-memory path with the weight stream.
+//
+// Every token slot of the 16 is multiplied whatever the pass's entry count:
+// columns past the entries are never stored. A branch on the count inside the
+// main loop costs far more than the idle MFMAs: where the paths merge the
+// compiler cannot tell whether the skipped operands' loads have landed, and
+// waits for the next loads before issuing the ones after.
 
-// Operands of one K chunk for one wave (up projection).
-template <int NT, int S>
+// Operands of one half unit for one wave (up projection).
+template <int RG, int S>
 struct UpOps {
-  bf16x8 g[S], u[S], x[NT][S];
+  bf16x8 g[RG][S], u[RG][S], x[S];
 };
 
-template <int NT, int S>
-__device__ __forceinline__ void up_load(UpOps<NT, S>& r, const uint16_t* wg, const uint16_t* wu,
-                                        const uint16_t* x, const size_t (&xoff)[NT], size_t kb) {
+// Loads go out row group by row group, so a lane's requests to one weight
+// row follow each other (on the down projection at the decode shape this
+// order took 176 us against 199 us for the groups interleaved step by step).
+template <int RG, int S>
+__device__ __forceinline__ void up_load(UpOps<RG, S>& r, const uint16_t* wg, const uint16_t* wu,
+                                        const uint16_t* x, int H, size_t kb) {
 #pragma unroll
-  for (int st = 0; st < S; ++st) {
-    r.g[st] = ld8(wg + kb + 32 * st);
-    r.u[st] = ld8(wu + kb + 32 * st);
-  }
+  for (int q = 0; q < RG; ++q)
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt)
+    for (int st = 0; st < S; ++st) r.g[q][st] = ld8(wg + (size_t)q * 16 * H + kb + 32 * st);
 #pragma unroll
-    for (int st = 0; st < S; ++st) r.x[nt][st] = ld8(x + xoff[nt] + kb + 32 * st);
+  for (int q = 0; q < RG; ++q)
+#pragma unroll
+    for (int st = 0; st < S; ++st) r.u[q][st] = ld8(wu + (size_t)q * 16 * H + kb + 32 * st);
+#pragma unroll
+  for (int st = 0; st < S; ++st) r.x[st] = ld8(x + kb + 32 * st);
 }
 
-template <int NT, int S>
-__device__ __forceinline__ void up_compute(const UpOps<NT, S>& r, int ntiles, f32x4* acc) {
-  switch (ntiles) {
-#define MOE_UPSK(n) \
-  case n:           \
-    if (n <= NT) up_mma<n, S>(r.g, r.u, r.x, acc, acc + NT); \
-    break;
-    MOE_UPSK(1) MOE_UPSK(2) MOE_UPSK(3) MOE_UPSK(4) MOE_UPSK(5) MOE_UPSK(6) MOE_UPSK(7) MOE_UPSK(8)
-#undef MOE_UPSK
-  }
+// acc[q]: gate group q, acc[RG + q]: up group q.
+template <int RG, int S>
+__device__ __forceinline__ void up_mma(const UpOps<RG, S>& r, f32x4 (&acc)[2 * RG]) {
+#pragma unroll
+  for (int st = 0; st < S; ++st)
+#pragma unroll
+    for (int q = 0; q < RG; ++q) {
+      acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(r.g[q][st], r.x[st], acc[q], 0, 0, 0);
+      acc[RG + q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(r.u[q][st], r.x[st], acc[RG + q], 0, 0, 0);
+    }
 }
 
 // Per-tile state of the up projection, in two stages: `issue` loads the plan
-// entries and the permutation rows of a tile early (one tile ahead); `finish`
+// entries and the permutation row of a tile early (one tile ahead); `finish`
 // turns them into addresses when the tile is reached, so those loads never
 // stall the weight stream.
-template <int NT>
 struct UpRaw {
-  int g, ex, tb, tc;
-  int r[NT];
+  int g, ex, tb, tc, r;
 };
-template <int NT>
 struct UpTile {
-  int g, tb, tc, ntiles;
-  size_t wrow;       // lane's gate row (+ its K offset) in W1
-  size_t xoff[NT];   // lane's token row (+ its K offset) in x, per N-tile
+  int g, tb, tc;
+  size_t wrow;  // lane's gate row (+ its K offset) in W1
+  size_t xoff;  // lane's token row (+ its K offset) in x
 };
 
-template <int NT>
-__device__ __forceinline__ void up_issue(UpRaw<NT>& raw, int tile, int G, const PlanRO& pv,
+__device__ __forceinline__ void up_issue(UpRaw& raw, int tile, int G, const PlanRO& pv,
                                          const int* perm, int lane) {
   const int pass = tile / G;
   raw.g = tile - pass * G;
   raw.ex = pv.expert[pass];
   raw.tb = pv.beg[pass];
   raw.tc = pv.cnt[pass];
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const int n = nt * 16 + (lane & 15);
-    raw.r[nt] = perm[raw.tb + (n < raw.tc ? n : 0)];
-  }
+  const int n = lane & 15;
+  raw.r = perm[raw.tb + (n < raw.tc ? n : 0)];
 }
 
 // Token slots past the pass's entries read a valid row (the first entry's):
 // MFMA output column n depends only on B column n and those columns are never
 // stored, so every load of the main loop is unconditional.
-template <int NT>
-__device__ __forceinline__ void up_finish(UpTile<NT>& st, const UpRaw<NT>& raw, int k, int H,
-                                          int I, int nmax, int lane, int kq) {
+template <int RG>
+__device__ __forceinline__ void up_finish(UpTile& st, const UpRaw& raw, int k, int H, int I,
+                                          int nmax, int lane, int kq) {
   st.g = raw.g;
   st.tb = raw.tb;
   st.tc = raw.tc;
-  st.ntiles = (raw.tc + 15) >> 4;
-  st.wrow = ((size_t)raw.ex * 2 * I + raw.g * UP_ROWS + (lane & 15)) * H + kq;
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const int r = (raw.r[nt] >= 0 && raw.r[nt] < nmax) ? raw.r[nt] : 0;
-    st.xoff[nt] = (size_t)(r / k) * H + kq;
-  }
+  st.wrow = ((size_t)raw.ex * 2 * I + raw.g * (16 * RG) + (lane & 15)) * H + kq;
+  const int r = (raw.r >= 0 && raw.r < nmax) ? raw.r : 0;
+  st.xoff = (size_t)(r / k) * H + kq;
 }
 
-template <int NT, int S>
+template <int RG, int S>
 __global__ __launch_bounds__(256) void ffn_up_sk_kernel(
     const uint16_t* __restrict__ x, const int* __restrict__ perm, int k, int H, int I, int nmax,
     const uint16_t* __restrict__ w1, const int* __restrict__ plan, int pmax, f32x4* slots,
     int* counters, uint16_t* __restrict__ h_hi, uint16_t* __restrict__ h_lo, int NB) {
-  constexpr int KUNIT = 4 * 32 * S;
-  __shared__ f32x4 red[2][4][2 * NT][kWave];
+  constexpr int KHALF = 4 * 32 * S, KUNIT = 2 * KHALF, N = 2 * RG;
+  __shared__ f32x4 red[2][4][RCH][kWave];
   const PlanRO pv = plan_ro(plan, pmax);
   const int P = pv.hdr[0];
-  const int G = I / UP_ROWS, C = H / KUNIT;
-  const long U = (long)P * G * C;
-  const int nb = (int)min((long)NB, U);
+  const int G = I / (16 * RG), C = H / KUNIT;
   const int b = xcd_block(blockIdx.x, NB);
-  if (b >= nb) return;
-  const SkRange rg(b, U, nb, C);
+  const Sched rg(b, P * G, C, NB);
+  if (b >= rg.nb) return;
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int kq = (lane >> 4) * 8 + wave * 32 * S;
   const size_t I_H = (size_t)I * H;
 
-  UpTile<NT> ts, tn;
-  UpRaw<NT> rn;
+  UpTile ts, tn;
+  UpRaw rn;
   {
-    UpRaw<NT> r0;
-    up_issue(r0, rg.ps.t, G, pv, perm, lane);
-    up_finish(ts, r0, k, H, I, nmax, lane, kq);
+    UpRaw r0;
+    up_issue(r0, rg.p0.t, G, pv, perm, lane);
+    up_finish<RG>(ts, r0, k, H, I, nmax, lane, kq);
   }
-  up_issue(rn, rg.next_tile(rg.ps.t), G, pv, perm, lane);
+  up_issue(rn, rg.next_tile(rg.p0.t), G, pv, perm, lane);
+  __builtin_amdgcn_sched_barrier(0);  // ahead of the weight loads
 
-  f32x4 acc[2 * NT];
+  f32x4 acc[N];
 #pragma unroll
-  for (int i = 0; i < 2 * NT; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < N; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // End of the tile of unit u: add the waves' partials, complete the tile
   // (directly, or through the cross-block fixup) and write a = silu(g) * u.
   int parity = 0;
   auto tile_end = [&](int tile) {
     block_reduce(acc, red, parity, wave, lane);
-    parity ^= 1;
     if (wave == 0) {
       bool done = true;
-      if (rg.split(tile)) done = fixup(acc, slots, counters, tile, C, U, nb, b, lane);
-      if (done) {
-        // lane l: rows g*16 + 4*(l/16) + j of token slot l % 16 of each N-tile
-        const int ir = ts.g * UP_ROWS + (lane >> 4) * 4;
+      if (rg.split(tile)) done = fixup(acc, slots, counters, tile - rg.TD, C, rg.US, rg.nb, b, lane);
+      const int n = lane & 15;
+      if (done && n < ts.tc) {
+        // lane l: rows 16 q + 4 (l / 16) + j of the tile, token slot l % 16
+        typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          const int n = nt * 16 + (lane & 15);
-          if (n >= ts.tc) continue;
-          typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
+        for (int q = 0; q < RG; ++q) {
           u16x4 hi, lo;
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            const float gg = acc[nt][j], uu = acc[NT + nt][j];
+            const float gg = acc[q][j], uu = acc[RG + q][j];
             const float a = gg / (1.0f + expf(-gg)) * uu;
             hi[j] = f32_to_bf16_bits(a);
             lo[j] = f32_to_bf16_bits(a - bf16_bits_to_f32(hi[j]));
           }
-          const size_t o = (size_t)(ts.tb + n) * I + ir;
+          const size_t o = (size_t)(ts.tb + n) * I + ts.g * (16 * RG) + q * 16 + (lane >> 4) * 4;
           *reinterpret_cast<u16x4*>(h_hi + o) = hi;
           *reinterpret_cast<u16x4*>(h_lo + o) = lo;
         }
       }
     }
 #pragma unroll
-    for (int i = 0; i < 2 * NT; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < N; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   };
 
-  // One unit: start the loads of unit u + 1 (in the next tile when u ends
-  // one), multiply unit u, and finish its tile when u is the tile's last unit
-  // in this block. Returns false after the block's last unit.
-  auto step = [&](UpOps<NT, S>& cur, UpOps<NT, S>& nxt, Pos& p) -> bool {
-    const Pos pn = rg.next(p);  // past the end: reload p (unused)
+  // One unit in two halves with their own registers: load the second half,
+  // multiply the first; load the first half of the next unit (in the next
+  // tile when this unit ends one), multiply the second; finish the tile when
+  // this is its last unit in the block. Every unit starts with its first
+  // half in flight in `h0`, so no register changes role between units.
+  UpOps<RG, S> h0, h1;
+  up_load(h0, w1 + ts.wrow, w1 + ts.wrow + I_H, x + ts.xoff, H, (size_t)rg.p0.kc * KUNIT);
+  __builtin_amdgcn_sched_barrier(0);
+  for (Pos p = rg.p0;;) {
+    up_load(h1, w1 + ts.wrow, w1 + ts.wrow + I_H, x + ts.xoff, H, (size_t)p.kc * KUNIT + KHALF);
+    __builtin_amdgcn_sched_barrier(0);
+    up_mma(h0, acc);
+    const Pos pn = rg.next(p);  // past the end: p again (loaded, unused)
     if (pn.t != p.t) {
-      up_finish(tn, rn, k, H, I, nmax, lane, kq);
+      up_finish<RG>(tn, rn, k, H, I, nmax, lane, kq);
       up_issue(rn, rg.next_tile(pn.t), G, pv, perm, lane);  // the tile after
     } else {
       tn = ts;
     }
-    const size_t kb = (size_t)pn.kc * KUNIT;
-    up_load(nxt, w1 + tn.wrow, w1 + tn.wrow + I_H, x, tn.xoff, kb);
-    up_compute<NT, S>(cur, ts.ntiles, acc);
+    up_load(h0, w1 + tn.wrow, w1 + tn.wrow + I_H, x + tn.xoff, H, (size_t)pn.kc * KUNIT);
+    __builtin_amdgcn_sched_barrier(0);
+    up_mma(h1, acc);
     if (rg.ends_tile(p)) tile_end(p.t);
-    if (rg.last(p)) return false;
+    if (rg.last(p)) break;
     ts = tn;
     p = pn;
-    return true;
-  };
-
-  UpOps<NT, S> b0, b1;
-  up_load(b0, w1 + ts.wrow, w1 + ts.wrow + I_H, x, ts.xoff, (size_t)rg.ps.kc * KUNIT);
-  Pos p = rg.ps;
-  while (step(b0, b1, p) && step(b1, b0, p)) {
   }
 }
 
 // --------------------------------------------------------------- down
-template <int NTILES, int S>
-__device__ __forceinline__ void down_mma(const bf16x8 (&a)[DOWN_GROUPS][S], const bf16x8 (*bh)[S],
-                                         const bf16x8 (*bl)[S], f32x4* acc) {
-#pragma unroll
-  for (int st = 0; st < S; ++st) {
-#pragma unroll
-    for (int nt = 0; nt < NTILES; ++nt) {
-#pragma unroll
-      for (int rg = 0; rg < DOWN_GROUPS; ++rg) {
-        f32x4& c = acc[nt * DOWN_GROUPS + rg];
-        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[rg][st], bh[nt][st], c, 0, 0, 0);
-        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[rg][st], bl[nt][st], c, 0, 0, 0);
-      }
-    }
-  }
-}
+// A tile is DG groups of 16 rows of W2 sharing each B fragment (hi and lo of
+// the intermediate: two MFMAs into one fp32 accumulator).
 
-// Operands of one K chunk for one wave (down projection).
-template <int NT, int S>
+// Operands of one half unit for one wave (down projection).
+template <int DG, int S>
 struct DownOps {
-  bf16x8 a[DOWN_GROUPS][S], h[NT][S], l[NT][S];
+  bf16x8 a[DG][S], h[S], l[S];
 };
 
-template <int NT, int S>
-__device__ __forceinline__ void down_load(DownOps<NT, S>& r, const uint16_t* w, int I,
-                                          const uint16_t* h_hi, const uint16_t* h_lo,
-                                          const size_t (&hrow)[NT], size_t kb) {
+template <int DG, int S>
+__device__ __forceinline__ void down_load(DownOps<DG, S>& r, const uint16_t* w, int I,
+                                          const uint16_t* hh, const uint16_t* hl, size_t kb) {
 #pragma unroll
-  for (int rg = 0; rg < DOWN_GROUPS; ++rg)
+  for (int q = 0; q < DG; ++q)
 #pragma unroll
-    for (int st = 0; st < S; ++st) r.a[rg][st] = ld8(w + (size_t)rg * 16 * I + kb + 32 * st);
+    for (int st = 0; st < S; ++st) r.a[q][st] = ld8(w + (size_t)q * 16 * I + kb + 32 * st);
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-    for (int st = 0; st < S; ++st) {
-      r.h[nt][st] = ld8(h_hi + hrow[nt] + kb + 32 * st);
-      r.l[nt][st] = ld8(h_lo + hrow[nt] + kb + 32 * st);
-    }
+  for (int st = 0; st < S; ++st) {
+    r.h[st] = ld8(hh + kb + 32 * st);
+    r.l[st] = ld8(hl + kb + 32 * st);
+  }
 }
 
-template <int NT, int S>
-__device__ __forceinline__ void down_compute(const DownOps<NT, S>& r, int ntiles, f32x4* acc) {
-  switch (ntiles) {
-#define MOE_DNSK(n) \
-  case n:           \
-    if (n <= NT) down_mma<n, S>(r.a, r.h, r.l, acc); \
-    break;
-    MOE_DNSK(1) MOE_DNSK(2) MOE_DNSK(3) MOE_DNSK(4) MOE_DNSK(5) MOE_DNSK(6) MOE_DNSK(7) MOE_DNSK(8)
-#undef MOE_DNSK
-  }
+template <int DG, int S>
+__device__ __forceinline__ void down_mma(const DownOps<DG, S>& r, f32x4 (&acc)[DG]) {
+#pragma unroll
+  for (int st = 0; st < S; ++st)
+#pragma unroll
+    for (int q = 0; q < DG; ++q) {
+      acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(r.a[q][st], r.h[st], acc[q], 0, 0, 0);
+      acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(r.a[q][st], r.l[st], acc[q], 0, 0, 0);
+    }
 }
 
 // Per-tile state of the down projection (plan entries loaded a tile ahead).
 struct DownRaw {
   int g, ex, tb, tc;
 };
-template <int NT>
 struct DownTile {
-  int g, tb, tc, ntiles;
-  size_t wrow;       // lane's first W2 row (+ its K offset)
-  size_t hrow[NT];   // lane's row of h (+ its K offset), per N-tile
+  int g, tb, tc;
+  size_t wrow;  // lane's first W2 row (+ its K offset)
+  size_t hrow;  // lane's row of h (+ its K offset)
 };
 
 __device__ __forceinline__ void down_issue(DownRaw& raw, int tile, int G, const PlanRO& pv) {
@@ -469,98 +474,85 @@ __device__ __forceinline__ void down_issue(DownRaw& raw, int tile, int G, const 
   raw.tc = pv.cnt[pass];
 }
 
-template <int NT>
-__device__ __forceinline__ void down_finish(DownTile<NT>& st, const DownRaw& raw, int H, int I,
+template <int DG>
+__device__ __forceinline__ void down_finish(DownTile& st, const DownRaw& raw, int H, int I,
                                             int lane, int kq) {
   st.g = raw.g;
   st.tb = raw.tb;
   st.tc = raw.tc;
-  st.ntiles = (raw.tc + 15) >> 4;
-  st.wrow = ((size_t)raw.ex * H + raw.g * DOWN_ROWS + (lane & 15)) * I + kq;
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const int n = nt * 16 + (lane & 15);  // slots past the entries read the first entry's row
-    st.hrow[nt] = (size_t)(raw.tb + (n < raw.tc ? n : 0)) * I + kq;
-  }
+  st.wrow = ((size_t)raw.ex * H + raw.g * (16 * DG) + (lane & 15)) * I + kq;
+  const int n = lane & 15;  // slots past the entries read the first entry's row
+  st.hrow = (size_t)(raw.tb + (n < raw.tc ? n : 0)) * I + kq;
 }
 
-template <int NT, int S>
+template <int DG, int S>
 __global__ __launch_bounds__(256) void ffn_down_sk_kernel(
     const uint16_t* __restrict__ h_hi, const uint16_t* __restrict__ h_lo, int H, int I,
     const uint16_t* __restrict__ w2, const int* __restrict__ plan, int pmax, f32x4* slots,
     int* counters, float* __restrict__ out, int NB) {
-  constexpr int KUNIT = 4 * 32 * S;
-  constexpr int NACC = NT * DOWN_GROUPS;
-  __shared__ f32x4 red[2][4][NACC][kWave];
+  constexpr int KHALF = 4 * 32 * S, KUNIT = 2 * KHALF;
+  __shared__ f32x4 red[2][4][RCH][kWave];
   const PlanRO pv = plan_ro(plan, pmax);
   const int P = pv.hdr[0];
-  const int G = H / DOWN_ROWS, C = I / KUNIT;
-  const long U = (long)P * G * C;
-  const int nb = (int)min((long)NB, U);
+  const int G = H / (16 * DG), C = I / KUNIT;
   const int b = xcd_block(blockIdx.x, NB);
-  if (b >= nb) return;
-  const SkRange rg(b, U, nb, C);
+  const Sched rg(b, P * G, C, NB);
+  if (b >= rg.nb) return;
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int kq = (lane >> 4) * 8 + wave * 32 * S;
 
-  DownTile<NT> ts, tn;
+  DownTile ts, tn;
   DownRaw rn;
   {
     DownRaw r0;
-    down_issue(r0, rg.ps.t, G, pv);
-    down_finish(ts, r0, H, I, lane, kq);
+    down_issue(r0, rg.p0.t, G, pv);
+    down_finish<DG>(ts, r0, H, I, lane, kq);
   }
-  down_issue(rn, rg.next_tile(rg.ps.t), G, pv);
+  down_issue(rn, rg.next_tile(rg.p0.t), G, pv);
 
-  f32x4 acc[NACC];
+  f32x4 acc[DG];
 #pragma unroll
-  for (int i = 0; i < NACC; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < DG; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   int parity = 0;
   auto tile_end = [&](int tile) {
     block_reduce(acc, red, parity, wave, lane);
-    parity ^= 1;
     if (wave == 0) {
       bool done = true;
-      if (rg.split(tile)) done = fixup(acc, slots, counters, tile, C, U, nb, b, lane);
-      if (done) {
+      if (rg.split(tile)) done = fixup(acc, slots, counters, tile - rg.TD, C, rg.US, rg.nb, b, lane);
+      const int n = lane & 15;
+      if (done && n < ts.tc) {
+        float* o = out + (size_t)(ts.tb + n) * H + ts.g * (16 * DG) + (lane >> 4) * 4;
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          const int n = nt * 16 + (lane & 15);
-          if (n >= ts.tc) continue;
-          float* o = out + (size_t)(ts.tb + n) * H + ts.g * DOWN_ROWS + (lane >> 4) * 4;
-#pragma unroll
-          for (int rg = 0; rg < DOWN_GROUPS; ++rg)
-            *reinterpret_cast<f32x4*>(o + rg * 16) = acc[nt * DOWN_GROUPS + rg];
-        }
+        for (int q = 0; q < DG; ++q) *reinterpret_cast<f32x4*>(o + q * 16) = acc[q];
       }
     }
 #pragma unroll
-    for (int i = 0; i < NACC; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < DG; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   };
 
-  auto step = [&](DownOps<NT, S>& cur, DownOps<NT, S>& nxt, Pos& p) -> bool {
+  // Units in two halves, as in the up projection.
+  DownOps<DG, S> h0, h1;
+  down_load(h0, w2 + ts.wrow, I, h_hi + ts.hrow, h_lo + ts.hrow, (size_t)rg.p0.kc * KUNIT);
+  __builtin_amdgcn_sched_barrier(0);
+  for (Pos p = rg.p0;;) {
+    down_load(h1, w2 + ts.wrow, I, h_hi + ts.hrow, h_lo + ts.hrow, (size_t)p.kc * KUNIT + KHALF);
+    __builtin_amdgcn_sched_barrier(0);
+    down_mma(h0, acc);
     const Pos pn = rg.next(p);
     if (pn.t != p.t) {
-      down_finish(tn, rn, H, I, lane, kq);
+      down_finish<DG>(tn, rn, H, I, lane, kq);
       down_issue(rn, rg.next_tile(pn.t), G, pv);  // the tile after
     } else {
       tn = ts;
     }
-    const size_t kb = (size_t)pn.kc * KUNIT;
-    down_load(nxt, w2 + tn.wrow, I, h_hi, h_lo, tn.hrow, kb);
-    down_compute<NT, S>(cur, ts.ntiles, acc);
+    down_load(h0, w2 + tn.wrow, I, h_hi + tn.hrow, h_lo + tn.hrow, (size_t)pn.kc * KUNIT);
+    __builtin_amdgcn_sched_barrier(0);
+    down_mma(h1, acc);
     if (rg.ends_tile(p)) tile_end(p.t);
-    if (rg.last(p)) return false;
+    if (rg.last(p)) break;
     ts = tn;
     p = pn;
-    return true;
-  };
-
-  DownOps<NT, S> b0, b1;
-  down_load(b0, w2 + ts.wrow, I, h_hi, h_lo, ts.hrow, (size_t)rg.ps.kc * KUNIT);
-  Pos p = rg.ps;
-  while (step(b0, b1, p) && step(b1, b0, p)) {
   }
 }
 
@@ -716,34 +708,11 @@ __global__ __launch_bounds__(PF_THREADS) void ffn_pf_kernel(
   const int P = pv.hdr[0];
   const int K = UP ? H : I;
   const int G = UP ? I / PF_UP_COLS : H / PF_ROWS, C = K / PF_K;
-  // Whole rounds of tiles first: in round r block b takes tile r * NB + b, so
-  // the blocks that run together on one XCD take neighbouring tiles of the
-  // same expert and walk K in step, reading each chunk of token rows from L2
-  // after the first of them fetched it. The remaining 1 to 2 rounds' tiles
-  // are cut into equal unit ranges (stream-K) as above.
-  const int TT = P * G;
-  const int R = TT >= 2 * NB ? TT / NB - 1 : 0;
-  const int TD = R * NB;                       // tiles of the whole rounds
-  const long US = (long)(TT - TD) * C;         // units of the stream-K part
-  const int nb = (int)min((long)NB, US);
   const int b = xcd_block(blockIdx.x, NB);
-  if (b >= nb) return;
-  const long s_rel = first_unit(b, US, nb), e_rel = first_unit(b + 1, US, nb);
-  const Pos ps{TD + (int)(s_rel / C), (int)(s_rel % C)};              // first SK unit
-  const Pos pe{TD + (int)((e_rel - 1) / C), (int)((e_rel - 1) % C)};  // last unit
+  const Sched sc(b, P * G, C, NB);
+  if (b >= sc.nb) return;
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
-  // The block's tiles in order: b, b + NB, ... (whole rounds), then ps.t .. pe.t
-  auto next_tile = [&](int t) -> int {
-    if (t < TD) return t + NB < TD ? t + NB : ps.t;
-    return t < pe.t ? t + 1 : pe.t;
-  };
-  auto next_pos = [&](Pos p) -> Pos {
-    if (p.t == pe.t && p.kc == pe.kc) return p;  // the last unit: stay
-    if (p.kc + 1 < C) return Pos{p.t, p.kc + 1};
-    if (p.t >= TD) return Pos{p.t + 1, 0};
-    return p.t + NB < TD ? Pos{p.t + NB, 0} : ps;
-  };
-  const Pos p0 = R > 0 ? Pos{b, 0} : ps;
+  const Pos p0 = sc.p0;
 
   // Tile states of the units in the pipeline: t0 for chunk p (multiplied this
   // step), t1 for chunk p1 (its weights are loaded this step, its token rows
@@ -751,7 +720,7 @@ __global__ __launch_bounds__(PF_THREADS) void ffn_pf_kernel(
   // this step); rn holds the plan entries of the tile after t2's.
   PfTile<NT> t0, t1, t2;
   PfRaw<NT> rn;
-  Pos p1 = next_pos(p0);
+  Pos p1 = sc.next(p0);
   {
     PfRaw<NT> r0;
     pf_issue<NT, UP>(r0, p0.t, G, pv, perm, tid);
@@ -763,7 +732,7 @@ __global__ __launch_bounds__(PF_THREADS) void ffn_pf_kernel(
       t1 = t0;
     }
   }
-  pf_issue<NT, UP>(rn, next_tile(p1.t), G, pv, perm, tid);
+  pf_issue<NT, UP>(rn, sc.next_tile(p1.t), G, pv, perm, tid);
 
   f32x4 acc[NACC];
 #pragma unroll
@@ -790,10 +759,9 @@ __global__ __launch_bounds__(PF_THREADS) void ffn_pf_kernel(
   // End of tile p.t in this block: complete it (directly, or through the
   // cross-block fixup when the stream-K cut falls inside it) and write it.
   auto tile_end = [&](Pos p) {
-    const bool split = p.t >= TD && ((p.t == ps.t && ps.kc > 0) || (p.t == pe.t && pe.kc < C - 1));
     bool done = true;
-    if (split)
-      done = fixup<NACC, PF_WAVES>(acc, slots, counters, p.t - TD, C, US, nb, b, lane, wave);
+    if (sc.split(p.t))
+      done = fixup<NACC, PF_WAVES>(acc, slots, counters, p.t - sc.TD, C, sc.US, sc.nb, b, lane, wave);
     if (done) {
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
@@ -846,10 +814,10 @@ __global__ __launch_bounds__(PF_THREADS) void ffn_pf_kernel(
   // the block's last unit.
   auto step = [&](bf16x8 (&ca)[PF_GROUPS][PF_STEPS], bf16x8 (&na)[PF_GROUPS][PF_STEPS],
                   PfStage<NR> (&cs)[NB_ARR], PfStage<NR> (&ns)[NB_ARR], int cb, Pos& p) -> bool {
-    const Pos p2 = next_pos(p1);
+    const Pos p2 = sc.next(p1);
     if (p2.t != p1.t) {
       pf_finish<NT, UP>(t2, rn, k, H, I, nmax, wave, lane, tid);
-      pf_issue<NT, UP>(rn, next_tile(p2.t), G, pv, perm, tid);
+      pf_issue<NT, UP>(rn, sc.next_tile(p2.t), G, pv, perm, tid);
     } else {
       t2 = t1;
     }
@@ -857,8 +825,8 @@ __global__ __launch_bounds__(PF_THREADS) void ffn_pf_kernel(
     load_a(na, t1, p1.kc);
     pf_mma<NT, UP>(ca, bs[cb][0], bs[cb][NB_ARR - 1], lane, acc);
     store_b(cs, cb ^ 1);
-    const bool last = p.t == pe.t && p.kc == pe.kc;
-    if (p.kc == C - 1 || last) tile_end(p);
+    const bool last = sc.last(p);
+    if (sc.ends_tile(p)) tile_end(p);
     __syncthreads();
     if (last) return false;
     t0 = t1;
@@ -921,12 +889,12 @@ size_t a256(size_t n) { return (n + 255) & ~(size_t)255; }
 
 template <int NT>
 int up_blocks() {
-  if constexpr (NT == 1) return resident_blocks(ffn_up_sk_kernel<NT, UP_STEPS>, 256, UP_CAP);
+  if constexpr (NT == 1) return resident_blocks(ffn_up_sk_kernel<UP_RG, UP_STEPS>, 256, UP_CAP);
   else return resident_blocks(ffn_pf_kernel<NT, true>, PF_THREADS);
 }
 template <int NT>
 int down_blocks() {
-  if constexpr (NT == 1) return resident_blocks(ffn_down_sk_kernel<NT, DOWN_STEPS>);
+  if constexpr (NT == 1) return resident_blocks(ffn_down_sk_kernel<DOWN_GROUPS, DOWN_STEPS>, 256, DOWN_CAP);
   else return resident_blocks(ffn_pf_kernel<NT, false>, PF_THREADS);
 }
 
@@ -941,8 +909,9 @@ int blocks_for(int NT, bool up) {
 // Workspace after h_hi / h_lo: the plan, then per kernel (up, down) `subs`
 // counters per block, and 2 x `subs` slots per block shared by both kernels
 // (a block's first and last tile; `subs` = 1 for the K-split kernels, one per
-// wave for the prefill kernels). A slot holds one wave's partial tile, at most
-// 4 NT f32x4 per lane.
+// wave for the prefill kernels). A slot holds one wave's partial tile: for the
+// K-split kernels the larger of the two tiles' accumulators (2 UP_RG or
+// DOWN_GROUPS f32x4 per lane), for the prefill kernels at most 4 NT.
 struct SkLayout {
   size_t plan, counters, slots, total;
   int pmax, nb_up, nb_down, subs;
@@ -959,7 +928,8 @@ SkLayout sk_layout(int T, int k, int L, int NT) {
   o.subs = NT == 1 ? 1 : PF_WAVES;
   o.counters = a256((size_t)(4 + 3 * o.pmax) * 4);
   o.slots = o.counters + a256((size_t)2 * o.subs * nbm * 4);
-  o.total = o.slots + a256((size_t)2 * o.subs * nbm * (4 * NT) * kWave * 16);
+  const int slot_n = NT == 1 ? (2 * UP_RG > DOWN_GROUPS ? 2 * UP_RG : DOWN_GROUPS) : 4 * NT;
+  o.total = o.slots + a256((size_t)2 * o.subs * nbm * slot_n * kWave * 16);
   return o;
 }
 
@@ -978,7 +948,7 @@ hipError_t launch_sk_nt(const uint16_t* x, const int* perm, const int* offsets, 
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   if constexpr (NT == 1) {
-    hipLaunchKernelGGL((ffn_up_sk_kernel<NT, UP_STEPS>), dim3(lo.nb_up), dim3(256), 0, stream, x,
+    hipLaunchKernelGGL((ffn_up_sk_kernel<UP_RG, UP_STEPS>), dim3(lo.nb_up), dim3(256), 0, stream, x,
                        perm, k, H, I, nmax, w1, plan, lo.pmax, slots, counters, h_hi, h_lo,
                        lo.nb_up);
   } else {
@@ -989,7 +959,7 @@ hipError_t launch_sk_nt(const uint16_t* x, const int* perm, const int* offsets, 
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   if constexpr (NT == 1) {
-    hipLaunchKernelGGL((ffn_down_sk_kernel<NT, DOWN_STEPS>), dim3(lo.nb_down), dim3(256), 0,
+    hipLaunchKernelGGL((ffn_down_sk_kernel<DOWN_GROUPS, DOWN_STEPS>), dim3(lo.nb_down), dim3(256), 0,
                        stream, h_hi, h_lo, H, I, w2, plan, lo.pmax, slots, counters + lo.subs * nbm,
                        out, lo.nb_down);
   } else {

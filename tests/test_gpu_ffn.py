@@ -67,13 +67,13 @@ def test_ffn_fast_path_tiles(T, E, k):
     check_ffn(T, 256, 384, E, k, 0, E)
 
 
-# Persistent stream-K path (H, I multiples of 256; at most 16 mean-doubled
-# entries per expert, one 16-token tile per pass): every tile cut between
-# blocks when there are fewer units than blocks, long K ranges, several passes
-# per expert; (60, 512, 768) doubles to 30 and takes the staged path.
-@pytest.mark.parametrize("T,H,I,E,k", [(24, 512, 512, 8, 2), (60, 512, 768, 8, 2),
-                                       (32, 4096, 512, 8, 2), (16, 256, 4096, 4, 1),
-                                       (200, 1024, 512, 64, 2)])
+# Persistent stream-K path (H a multiple of 512, I of 1024; at most 16
+# mean-doubled entries per expert, one 16-token tile per pass): every tile cut
+# between blocks when there are fewer units than blocks, long K ranges, several
+# passes per expert; (60, 512, 768) doubles to 30 and takes the staged path.
+@pytest.mark.parametrize("T,H,I,E,k", [(24, 512, 1024, 8, 2), (60, 512, 768, 8, 2),
+                                       (32, 4096, 1024, 8, 2), (16, 512, 4096, 4, 1),
+                                       (200, 1024, 1024, 64, 2)])
 def test_ffn_stream_k(T, H, I, E, k):
     check_ffn(T, H, I, E, k, 0, E)
 
@@ -82,11 +82,11 @@ def test_ffn_stream_k_skewed_passes():
     """One expert takes every token (three 16-token passes), others few."""
     T, E, k = 40, 16, 2
     ids = np.stack([np.zeros(T, np.int32), 1 + np.arange(T, dtype=np.int32) % 15], 1)
-    check_ffn(T, 512, 512, E, k, 0, E, ids=ids)
+    check_ffn(T, 512, 1024, E, k, 0, E, ids=ids)
 
 
 def test_ffn_stream_k_share():
-    check_ffn(48, 512, 512, 12, 2, 4, 5)
+    check_ffn(48, 512, 1024, 12, 2, 4, 5)
 
 
 # Prefill path (many entries per expert: 4 or 8 token tiles per pass, the
