@@ -67,13 +67,17 @@ def test_ffn_fast_path_tiles(T, E, k):
     check_ffn(T, 256, 384, E, k, 0, E)
 
 
-# Persistent stream-K path (H a multiple of 512, I of 1024; at most 16
-# mean-doubled entries per expert, one 16-token tile per pass): every tile cut
-# between blocks when there are fewer units than blocks, long K ranges, several
-# passes per expert; (60, 512, 768) doubles to 30 and takes the staged path.
+# K-split path (H a multiple of 512, I of 1024; at most 16 mean-doubled
+# entries per expert, one 16-token tile per pass). On a 256-CU part (256
+# blocks): whole tiles only when the rounds come out nearly even (24, 32, 200);
+# stream-K over all tiles, every tile cut, for the up kernel (16, 4096, 1024)
+# and the down kernel (16, 512, 4096); one whole round and then stream-K with
+# cut tiles for the up kernel (40, 1024, 1024) and the down kernel
+# (40, 4096, 2048); (60, 512, 768) doubles to 30 and takes the staged path.
 @pytest.mark.parametrize("T,H,I,E,k", [(24, 512, 1024, 8, 2), (60, 512, 768, 8, 2),
                                        (32, 4096, 1024, 8, 2), (16, 512, 4096, 4, 1),
-                                       (200, 1024, 1024, 64, 2)])
+                                       (200, 1024, 1024, 64, 2), (16, 4096, 1024, 4, 1),
+                                       (40, 1024, 1024, 20, 2), (40, 4096, 2048, 20, 2)])
 def test_ffn_stream_k(T, H, I, E, k):
     check_ffn(T, H, I, E, k, 0, E)
 
@@ -99,10 +103,16 @@ def test_ffn_prefill(T, H, I, E, k):
 
 
 def test_ffn_prefill_whole_rounds():
-    """512 experts of ~64 entries: 512 up tiles and 512 down tiles, at least
-    twice the resident blocks of a 256-CU part, so whole rounds of tiles (one
-    tile per block, no cut) run before the stream-K remainder."""
+    """512 experts of ~64 entries: 1024 up tiles and 1024 down tiles, four
+    even rounds of a 256-CU part, so every tile is dealt whole."""
     check_ffn(4096, 512, 256, 512, 8, 0, 512)
+
+
+def test_ffn_prefill_rounds_then_cuts():
+    """300 experts of ~85 entries: 600 up and 600 down tiles, 2.3 rounds of a
+    256-CU part: one whole round, then the remaining tiles cut into equal unit
+    ranges, most of them finished through the cross-block fixup."""
+    check_ffn(3200, 512, 256, 300, 8, 0, 300)
 
 
 def test_ffn_prefill_skewed():
