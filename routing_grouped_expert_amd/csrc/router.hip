@@ -21,7 +21,8 @@ namespace moe {
 
 namespace {
 // ---- many tokens: fp64 MFMA (v_mfma_f64_16x16x4f64) ----------------------
-// Block tile 64 tokens x 64 experts, 4 waves of 32 x 32 (2 x 2 MFMA tiles),
+// Any H and alignment (the full-chunk kernel below serves H a multiple of 32
+// with 16-byte aligned rows): block tile 64 tokens x 64 experts, 4 waves of 32 x 32 (2 x 2 MFMA tiles),
 // K staged through LDS in chunks of 32 as fp64 (k-major, so each 16-lane
 // group of a fragment read is one contiguous 128-byte row). The K range is
 // split over blockIdx.z; each slice writes fp64 partial sums, which a second
@@ -108,6 +109,99 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(const uint16_t* __rest
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int t = t0 + wm * 32 + i * 16 + (lane >> 4) + 4 * r;
+        if (t < T && e < E) out[(size_t)t * E + e] = acc[i][j][r];
+      }
+    }
+}
+
+// The same GEMM for full chunks (H a multiple of 32, 16-byte aligned rows),
+// on 128-token tiles (4 waves of 64 tokens x 32 experts: 4 x 2 MFMA tiles, so
+// each fragment read from LDS feeds 2 or 4 MFMAs). x and w_gate are staged in
+// LDS as they are (bf16 bits, fp32) and widened to fp64 as the fragments are
+// read; two LDS buffers, and the next chunk's global loads are issued before
+// the current chunk's MFMAs, so one barrier per chunk and no wait on HBM
+// inside it. Rows past T or E load the last valid row (their results are
+// never stored), so every load is unconditional.
+constexpr int FT = 128;              // tokens per block tile
+constexpr int XPAD = 16, WPAD = 16;  // row paddings: conflict-free fragment reads
+// At most 168 registers (3 blocks per CU): share-0 router 412 us against
+// 423 us at 176 registers (2 blocks).
+__global__ __launch_bounds__(256, 3) void router_mfma_full_kernel(const uint16_t* __restrict__ x,
+                                                               const float* __restrict__ wg,
+                                                               int T, int H, int E, int kslice,
+                                                               double* __restrict__ part) {
+  constexpr int TI = FT / 32;  // MFMA token tiles per wave
+  __shared__ uint16_t xs[2][MK][FT + XPAD];
+  __shared__ float ws[2][MK][MN + WPAD];
+  const int t0 = blockIdx.x * FT, e0 = blockIdx.y * MN;
+  const int kb0 = blockIdx.z * kslice, kb1 = min(H, kb0 + kslice);
+  const int nch = (kb1 - kb0) / MK;
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int wm = wave & 1, wn = wave >> 1;
+  // staging: thread -> (row, 8 consecutive k); x rows srow and srow + 64
+  const int srow = tid >> 2, sk = (tid & 3) * 8;
+  const uint16_t* xrow0 = x + (size_t)min(t0 + srow, T - 1) * H + kb0 + sk;
+  const uint16_t* xrow1 = x + (size_t)min(t0 + 64 + srow, T - 1) * H + kb0 + sk;
+  const float* wrow = wg + (size_t)min(e0 + srow, E - 1) * H + kb0 + sk;
+  u16x8 xr0, xr1;
+  f32x4 w0, w1;
+  auto load = [&](int c) {
+    xr0 = *reinterpret_cast<const u16x8*>(xrow0 + c * MK);
+    xr1 = *reinterpret_cast<const u16x8*>(xrow1 + c * MK);
+    w0 = *reinterpret_cast<const f32x4*>(wrow + c * MK);
+    w1 = *reinterpret_cast<const f32x4*>(wrow + c * MK + 4);
+  };
+  auto store = [&](int buf) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      xs[buf][sk + j][srow] = xr0[j];
+      xs[buf][sk + j][64 + srow] = xr1[j];
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      ws[buf][sk + j][srow] = w0[j];
+      ws[buf][sk + 4 + j][srow] = w1[j];
+    }
+  };
+  f64x4 acc[TI][2];
+#pragma unroll
+  for (int i = 0; i < TI; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f64x4{0.0, 0.0, 0.0, 0.0};
+  load(0);
+  store(0);
+  __syncthreads();
+  for (int c = 0; c < nch; ++c) {
+    const int buf = c & 1;
+    load(c + 1 < nch ? c + 1 : c);  // past the last chunk: reloaded, unused
+    __builtin_amdgcn_sched_barrier(0);  // the loads go out before the MFMAs
+#pragma unroll
+    for (int s4 = 0; s4 < MK / 4; ++s4) {
+      const int kr = s4 * 4 + (lane >> 4);
+      double a[TI], b[2];
+#pragma unroll
+      for (int i = 0; i < TI; ++i)
+        a[i] = bf16_bits_to_f32(xs[buf][kr][wm * (FT / 2) + i * 16 + (lane & 15)]);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) b[j] = ws[buf][kr][wn * 32 + j * 16 + (lane & 15)];
+#pragma unroll
+      for (int i = 0; i < TI; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[i], b[j], acc[i][j], 0, 0, 0);
+    }
+    store(buf ^ 1);  // that buffer was last read before the previous barrier
+    __syncthreads();
+  }
+  double* out = part + (size_t)blockIdx.z * T * E;
+#pragma unroll
+  for (int i = 0; i < TI; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int e = e0 + wn * 32 + j * 16 + (lane & 15);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = t0 + wm * (FT / 2) + i * 16 + (lane >> 4) + 4 * r;
         if (t < T && e < E) out[(size_t)t * E + e] = acc[i][j][r];
       }
     }
@@ -212,10 +306,10 @@ __global__ __launch_bounds__(256) void router_rows_kernel(const uint16_t* __rest
 constexpr int kRowsMaxTokens = 64;
 
 namespace {
-// K slices for the many-token kernel: enough blocks to cover the GPU about four
-// times, each slice at least 256 wide and a multiple of the 32-wide chunk.
-int router_slices(int T, int H, int E, int* kslice) {
-  const long tiles = (long)((T + MT - 1) / MT) * ((E + MN - 1) / MN);
+// K slices for the many-token kernels (block tiles of mt tokens): about 1024
+// blocks, each slice at least 256 wide and a multiple of the 32-wide chunk.
+int router_slices(int T, int H, int E, int mt, int* kslice) {
+  const long tiles = (long)((T + mt - 1) / mt) * ((E + MN - 1) / MN);
   long want = (1024 + tiles - 1) / tiles;
   const long most = (H + 255) / 256;
   if (want > most) want = most;
@@ -230,7 +324,7 @@ int router_slices(int T, int H, int E, int* kslice) {
 size_t router_workspace_bytes(int T, int H, int E) {
   if (T <= kRowsMaxTokens) return 0;
   int ks = 0;
-  const int z = router_slices(T, H, E, &ks);
+  const int z = std::max(router_slices(T, H, E, MT, &ks), router_slices(T, H, E, FT, &ks));
   return (size_t)z * T * E * sizeof(double);
 }
 
@@ -257,13 +351,17 @@ hipError_t launch_router_logits(const uint16_t* x, const float* wg, const float*
     }
     return hipGetLastError();
   }
-  int ks = 0;
-  const int z = router_slices(T, H, E, &ks);
   double* part = static_cast<double*>(ws);
-  const bool vec = H % 8 == 0 && (reinterpret_cast<uintptr_t>(x) & 15u) == 0 &&
-                   (reinterpret_cast<uintptr_t>(wg) & 15u) == 0;
-  dim3 grid((T + MT - 1) / MT, (E + MN - 1) / MN, z);
-  if (vec)
+  const bool aligned = (reinterpret_cast<uintptr_t>(x) & 15u) == 0 &&
+                       (reinterpret_cast<uintptr_t>(wg) & 15u) == 0;
+  const bool full = aligned && H % MK == 0;
+  int ks = 0;
+  const int z = router_slices(T, H, E, full ? FT : MT, &ks);
+  dim3 grid((T + (full ? FT : MT) - 1) / (full ? FT : MT), (E + MN - 1) / MN, z);
+  if (full)
+    hipLaunchKernelGGL(router_mfma_full_kernel, grid, dim3(256), 0, stream, x, wg, T, H, E, ks,
+                       part);
+  else if (aligned && H % 8 == 0)
     hipLaunchKernelGGL(router_mfma_kernel<true>, grid, dim3(256), 0, stream, x, wg, T, H, E, ks,
                        part);
   else
