@@ -652,12 +652,23 @@ struct PfStage {
   u16x8 v[PER];
 };
 
+// Token rows are read through a buffer resource over the whole source array:
+// the pieces of rows past the pass's entries carry an offset beyond the
+// resource's size, which the hardware answers with zeros without a memory
+// request, so padding costs no traffic and needs no branch.
+constexpr uint32_t kPadOffset = 0x80000000u;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t pf_rsrc(const uint16_t* base, size_t elems) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), 0, (int)(elems * 2),
+                                           0x00020000);
+}
+
 template <int NR>
-__device__ __forceinline__ void pf_stage_load(PfStage<NR>& st, const uint16_t* base,
-                                              const size_t (&roff)[PfStage<NR>::PER], size_t kb) {
+__device__ __forceinline__ void pf_stage_load(PfStage<NR>& st, __amdgpu_buffer_rsrc_t rs,
+                                              const uint32_t (&voff)[PfStage<NR>::PER],
+                                              uint32_t kb_bytes) {
 #pragma unroll
   for (int i = 0; i < PfStage<NR>::PER; ++i)
-    st.v[i] = *reinterpret_cast<const u16x8*>(base + roff[i] + kb);
+    st.v[i] = __builtin_bit_cast(u16x8, __builtin_amdgcn_raw_buffer_load_b128(rs, voff[i], kb_bytes, 0));
 }
 
 template <int NR>
@@ -721,7 +732,7 @@ template <int NT>
 struct PfTile {
   int g, tb, tc, ntiles;
   size_t wrow;                               // this lane's first weight row (+ K offset)
-  size_t roff[PfStage<NT * 16>::PER];        // staged B rows (+ this thread's column)
+  uint32_t voff[PfStage<NT * 16>::PER];      // staged B rows (+ this thread's column), bytes
 };
 
 // Weight row of group q relative to the lane's first row: up groups 0, 1 are
@@ -747,10 +758,10 @@ __device__ __forceinline__ void pf_finish(PfTile<NT>& st, const PfRaw<NT>& raw, 
   st.wrow = (UP ? ((size_t)raw.ex * 2 * I + row) : ((size_t)raw.ex * H + row)) * K + kq;
 #pragma unroll
   for (int i = 0; i < PfStage<NT * 16>::PER; ++i) {
-    const int q = (tid + PF_THREADS * i) % (PF_K / 8);
+    const int n = (tid + PF_THREADS * i) / (PF_K / 8), q = (tid + PF_THREADS * i) % (PF_K / 8);
     int r = raw.r[i];
     if (UP) r = (r >= 0 && r < nmax) ? r / k : 0;
-    st.roff[i] = (size_t)r * K + q * 8;
+    st.voff[i] = n < raw.tc ? (uint32_t)((r * K + q * 8) * 2) : kPadOffset;
   }
 }
 
@@ -774,6 +785,9 @@ __global__ __launch_bounds__(PF_THREADS) void ffn_pf_kernel(
   if (b >= sc.nb) return;
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
   const Pos p0 = sc.p0;
+  // token rows: x (T = nmax / k rows of H) or h_hi and h_lo (nmax rows of I)
+  const __amdgpu_buffer_rsrc_t rs0 = pf_rsrc(b0src, UP ? (size_t)(nmax / k) * H : (size_t)nmax * I);
+  const __amdgpu_buffer_rsrc_t rs1 = pf_rsrc(b1src, (size_t)nmax * I);
 
   // Tile states of the units in the pipeline: t0 for chunk p (multiplied this
   // step), t1 for chunk p1 (its weights are loaded this step, its token rows
@@ -809,8 +823,8 @@ __global__ __launch_bounds__(PF_THREADS) void ffn_pf_kernel(
   };
   auto load_b = [&](PfStage<NR> (&st)[NB_ARR], const PfTile<NT>& t, int kc) {
     const size_t kb = (size_t)kc * PF_K;
-    pf_stage_load(st[0], b0src, t.roff, kb);
-    if (!UP) pf_stage_load(st[NB_ARR - 1], b1src, t.roff, kb);
+    pf_stage_load(st[0], rs0, t.voff, (uint32_t)(kb * 2));
+    if (!UP) pf_stage_load(st[NB_ARR - 1], rs1, t.voff, (uint32_t)(kb * 2));
   };
   auto store_b = [&](const PfStage<NR> (&st)[NB_ARR], int buf) {
     pf_stage_store(st[0], bs[buf][0], tid);
@@ -1039,7 +1053,10 @@ bool ffn_sk_applies(const void* x, const void* w1, const void* w2, int T, int k,
   if (!(al(x) && al(w1) && al(w2))) return false;
   if (pick_nt(T, k, L) == 1)
     return H % UP_KUNIT == 0 && I % DOWN_KUNIT == 0 && I % UP_ROWS == 0 && H % DOWN_ROWS == 0;
-  return H % PF_K == 0 && I % PF_K == 0 && H % PF_ROWS == 0 && I % PF_UP_COLS == 0;
+  // the staged kernels address token rows with 32-bit byte offsets below 2^31
+  const size_t lim = (size_t)1 << 31;
+  return H % PF_K == 0 && I % PF_K == 0 && H % PF_ROWS == 0 && I % PF_UP_COLS == 0 &&
+         (size_t)T * H * 2 < lim && (size_t)T * k * I * 2 < lim;
 }
 
 size_t ffn_sk_workspace_bytes(int T, int k, int L) {
