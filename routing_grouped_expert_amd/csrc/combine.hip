@@ -19,35 +19,48 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
                                                       int nmax, uint16_t* __restrict__ y) {
   __shared__ int s_p[MAXK];
   __shared__ float s_w[MAXK];
+  __shared__ int s_n;
   const int t = blockIdx.x;
-  if (threadIdx.x < k) {
-    int p = e2p[(size_t)t * k + threadIdx.x];
-    s_p[threadIdx.x] = (p >= 0 && p < nmax) ? p : -1;
-    s_w[threadIdx.x] = w[(size_t)t * k + threadIdx.x];
+  // The selections inside the share, compacted in ascending j (wave 0).
+  if (threadIdx.x < kWave) {
+    const int j = threadIdx.x;
+    int p = -1;
+    float wj = 0.f;
+    if (j < k) {
+      p = e2p[(size_t)t * k + j];
+      wj = w[(size_t)t * k + j];
+    }
+    const bool on = j < k && p >= 0 && p < nmax;
+    const uint64_t m = __ballot(on);
+    if (on) {
+      const int pos = __popcll(m & ((1ull << j) - 1));
+      s_p[pos] = p;
+      s_w[pos] = wj;
+    }
+    if (j == 0) s_n = __popcll(m);
   }
   __syncthreads();
+  const int nv = s_n;
   uint16_t* yt = y + (size_t)t * H;
   if (VEC) {
-    // Up to 8 column chunks of 1024 per round; for each selection j the
-    // chunks' loads are issued together (rows of skipped selections read row
-    // 0 and are multiplied by nothing), so a round waits for memory k times.
+    // Up to 8 column chunks of 1024 per round; for each selection the
+    // chunks' loads are issued together, so a round waits for memory once per
+    // selection inside the share.
     constexpr int CH = 8;
     typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
     for (int c0 = threadIdx.x * 4; c0 < H; c0 += CH * blockDim.x * 4) {
       f32x4 acc[CH];
 #pragma unroll
       for (int i = 0; i < CH; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-      for (int j = 0; j < k; ++j) {
-        const int p = s_p[j];
-        const float wj = p < 0 ? 0.f : s_w[j];
-        const float* row = eo + (size_t)(p < 0 ? 0 : p) * H;
+      for (int j = 0; j < nv; ++j) {
+        const float wj = s_w[j];
+        const float* row = eo + (size_t)s_p[j] * H;
         f32x4 v[CH];
 #pragma unroll
         for (int i = 0; i < CH; ++i) {
           const int c = c0 + i * blockDim.x * 4;
           v[i] = c < H ? *reinterpret_cast<const f32x4*>(row + c) : f32x4{0.f, 0.f, 0.f, 0.f};
         }
-        if (p < 0) continue;
 #pragma unroll
         for (int i = 0; i < CH; ++i) {
           acc[i][0] = fmaf(wj, v[i][0], acc[i][0]);
@@ -68,11 +81,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   } else {
     for (int c = threadIdx.x; c < H; c += blockDim.x) {
       float acc = 0.f;
-      for (int j = 0; j < k; ++j) {
-        const int p = s_p[j];
-        if (p < 0) continue;
-        acc = fmaf(s_w[j], eo[(size_t)p * H + c], acc);
-      }
+      for (int j = 0; j < nv; ++j) acc = fmaf(s_w[j], eo[(size_t)s_p[j] * H + c], acc);
       yt[c] = f32_to_bf16_bits(acc);
     }
   }
