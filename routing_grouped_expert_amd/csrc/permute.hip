@@ -82,26 +82,27 @@ __global__ __launch_bounds__(256) void tile_masks_kernel(const int* __restrict__
   for (int e = tid; e < E; e += blockDim.x) masks[(size_t)b * E + e] = mask[e];
 }
 
-// Grid: ceil(E / 64) blocks of 4 waves; lane j of every wave owns expert
-// 64 * block + j and wave w the w-th quarter of the tiles: counts[e], and
-// base[tile * L + i] = entries of local expert i in earlier tiles. The last
-// block to finish writes offsets, the exclusive scan of the local experts'
-// counts. Dynamic LDS: (L + 1) + 16 ints.
-__global__ __launch_bounds__(256) void expert_scan_kernel(const unsigned long long* __restrict__ masks,
-                                                          int nb, int E, int first, int L,
-                                                          int* counts, int* __restrict__ offsets,
-                                                          int* __restrict__ base, int* done) {
+// Grid: ceil(E / 64) blocks of SW waves; lane j of every wave owns expert
+// 64 * block + j and wave w the w-th of SW equal parts of the tiles:
+// counts[e], and base[tile * L + i] = entries of local expert i in earlier
+// tiles. The last block to finish writes offsets, the exclusive scan of the
+// local experts' counts. Dynamic LDS: (L + 1) + 16 ints.
+constexpr int SW = 16;
+__global__ __launch_bounds__(SW * 64) void expert_scan_kernel(const unsigned long long* __restrict__ masks,
+                                                              int nb, int E, int first, int L,
+                                                              int* counts, int* __restrict__ offsets,
+                                                              int* __restrict__ base, int* done) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  __shared__ int part[4][kWave];
+  __shared__ int part[SW][kWave];
   __shared__ int is_last;
   int* off = reinterpret_cast<int*>(smem);
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
   const int e = blockIdx.x * kWave + lane;
-  const int per = (nb + 3) / 4;
+  const int per = (nb + SW - 1) / SW;
   const int b0 = min(nb, wave * per), b1 = min(nb, b0 + per);
   int c = 0;
   if (e < E) {
-#pragma unroll 8
+#pragma unroll 4
     for (int b = b0; b < b1; ++b) c += __popcll(masks[(size_t)b * E + e]);
   }
   part[wave][lane] = c;
@@ -110,19 +111,30 @@ __global__ __launch_bounds__(256) void expert_scan_kernel(const unsigned long lo
   for (int w = 0; w < wave; ++w) run += part[w][lane];
   const int i = e - first;
   if (e < E && i >= 0 && i < L) {
-#pragma unroll 8
+#pragma unroll 4
     for (int b = b0; b < b1; ++b) {
       base[(size_t)b * L + i] = run;
       run += __popcll(masks[(size_t)b * E + e]);
     }
   }
-  if (wave == 0 && e < E) counts[e] = part[0][lane] + part[1][lane] + part[2][lane] + part[3][lane];
-  __threadfence();  // counts visible before this block is counted
+  if (wave == 0 && e < E) {
+    int tot = 0;
+    for (int w = 0; w < SW; ++w) tot += part[w][lane];
+    counts[e] = tot;
+  }
+  // Counts are published (release, once per block) before the block is
+  // counted; only the last block acquires. Each device-scope fence writes
+  // back or invalidates the XCD's L2, so the other blocks skip the acquire.
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // this wave's stores have reached L2
   __syncthreads();
-  if (tid == 0) is_last = atomicAdd(done, 1) == (int)gridDim.x - 1;
+  if (tid == 0) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    const int last = atomicAdd(done, 1) == (int)gridDim.x - 1;
+    if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    is_last = last;
+  }
   __syncthreads();
   if (!is_last) return;
-  __threadfence();
   for (int j = tid; j < L; j += blockDim.x)
     off[j] = __hip_atomic_load(&counts[first + j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
@@ -189,7 +201,7 @@ hipError_t launch_permute(const int* ids, int T, int k, int E, int first, int L,
                      masks, done);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(expert_scan_kernel, dim3((E + kWave - 1) / kWave), dim3(256),
+  hipLaunchKernelGGL(expert_scan_kernel, dim3((E + kWave - 1) / kWave), dim3(SW * kWave),
                      (size_t)(L + 1 + 16) * 4, stream, masks, nb, E, first, L, counts, offsets,
                      base, done);
   err = hipGetLastError();

@@ -59,7 +59,9 @@ __device__ __forceinline__ void top2_below(const uint64_t (&key)[VPL], uint64_t 
 // held it moves h2 up, and when it wins a second time (its h2 already moved
 // up) it rescans its keys below the last one it gave. Lane j keeps the key
 // taken in round j.
-template <int VPL>
+// VEC (E a multiple of 4, 16-byte aligned logits, VPL >= 4): a lane loads its
+// values as groups of 4 consecutive experts, expert 4 (lane + 64 g) + c.
+template <int VPL, bool VEC>
 __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ logits, int T, int E,
                                                    int k, int* __restrict__ ids,
                                                    float* __restrict__ weights) {
@@ -68,10 +70,26 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
   if (t >= T) return;  // whole waves leave: every selection round runs on a full wave
   const float* l = logits + (size_t)t * E;
   uint64_t key[VPL];
+  if constexpr (VEC) {
+    f32x4 v[VPL / 4];
 #pragma unroll
-  for (int i = 0; i < VPL; ++i) {
-    const int e = lane + kWave * i;
-    key[i] = e < E ? make_key(l[e], e) : 0ull;  // a valid key is never 0
+    for (int g = 0; g < VPL / 4; ++g) {
+      const int e = 4 * (lane + kWave * g);
+      v[g] = e < E ? *reinterpret_cast<const f32x4*>(l + e) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int g = 0; g < VPL / 4; ++g)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int e = 4 * (lane + kWave * g) + c;
+        key[4 * g + c] = e < E ? make_key(v[g][c], e) : 0ull;  // a valid key is never 0
+      }
+  } else {
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+      const int e = lane + kWave * i;
+      key[i] = e < E ? make_key(l[e], e) : 0ull;  // a valid key is never 0
+    }
   }
   uint64_t h1, h2;
   top2_below(key, ~0ull, h1, h2);
@@ -109,8 +127,16 @@ hipError_t launch_tier(const float* logits, int T, int E, int k, int* ids, float
                        hipStream_t stream) {
   const int waves_per_block = 4;
   dim3 grid((T + waves_per_block - 1) / waves_per_block);
-  hipLaunchKernelGGL(route_kernel<VPL>, grid, dim3(waves_per_block * kWave), 0, stream, logits, T,
-                     E, k, ids, w);
+  const bool vec = VPL >= 4 && E % 4 == 0 && (reinterpret_cast<uintptr_t>(logits) & 15u) == 0;
+  if constexpr (VPL >= 4) {
+    if (vec) {
+      hipLaunchKernelGGL((route_kernel<VPL, true>), grid, dim3(waves_per_block * kWave), 0, stream,
+                         logits, T, E, k, ids, w);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((route_kernel<VPL, false>), grid, dim3(waves_per_block * kWave), 0, stream,
+                     logits, T, E, k, ids, w);
   return hipGetLastError();
 }
 
