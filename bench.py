@@ -11,7 +11,8 @@ launches on; moe_forward itself is timed over the same number of steps as a
 check. Inputs are synthetic (seeded), resident in HBM before timing starts.
 
 Prints one JSON line: tokens/s of the whole step, the grouped-FFN roofline
-(algorithmic bytes / measured duration against 8 TB/s), the oracle timed on
+(algorithmic bytes / measured duration against 8 TB/s, and against the read
+rate a plain streaming probe reaches on the same part), the oracle timed on
 the host cores as a CPU baseline, and routing microseconds at 1024 experts.
 """
 import argparse
@@ -40,6 +41,10 @@ def parse_args():
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the oracle timing (profiling runs)")
     ap.add_argument("--no-routing", action="store_true", help="skip the routing-only timings")
+    ap.add_argument("--routing-sweep", action="store_true",
+                    help="instead of the layer step: route + permute microseconds over "
+                         "T in {1, 64, 4096} x E in {8 .. 4096}, k = 8 (k = E below 8), warm and "
+                         "with the caches flushed before each call; one JSON line")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one elementwise kernel that reads 256 MiB and writes 256 MiB "
                          "(calibrates the HBM byte counters)")
@@ -66,12 +71,69 @@ def committed_traffic(workload):
     return float(kv["hbm_bytes_per_call"])
 
 
+def routing_sweep():
+    """Cost table of the routing steps (route + permute) over token counts and
+    expert counts: median microseconds per call, warm (inputs cached) and cold
+    (a 512 MiB buffer written between calls, so logits and ids come from HBM)."""
+    import torch
+
+    import routing_grouped_expert_amd as moe
+    from synth import configs
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    table = []
+    for E in (8, 16, 32, 64, 128, 256, 512, 1024, 2048, 4096):
+        k = min(8, E)
+        for T in (1, 64, 4096):
+            lg = torch.from_numpy(configs.routing_logits(T, E=E)).to(dev)
+            ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+            wts = torch.empty((T, k), dtype=torch.float32, device=dev)
+            cnt = torch.empty((E,), dtype=torch.int32, device=dev)
+            off = torch.empty((E + 1,), dtype=torch.int32, device=dev)
+            perm = torch.empty((T * k,), dtype=torch.int32, device=dev)
+            e2p = torch.empty((T * k,), dtype=torch.int32, device=dev)
+            ws = moe.alloc_workspace(T, 128, 128, E, k, E)
+
+            def call():
+                moe.route(lg, k, ids, wts, stream)
+                moe.permute(ids, E, 0, E, cnt, off, perm, e2p, ws, stream)
+
+            res = {}
+            for mode in ("warm", "cold"):
+                for _ in range(5):
+                    call()
+                times = []
+                for _ in range(50):
+                    if mode == "cold":
+                        flush.fill_(1)
+                    a = torch.cuda.Event(enable_timing=True)
+                    b = torch.cuda.Event(enable_timing=True)
+                    a.record(stream)
+                    call()
+                    b.record(stream)
+                    times.append((a, b))
+                torch.cuda.synchronize()
+                us = sorted(a.elapsed_time(b) * 1e3 for a, b in times)
+                res[mode] = {"median": round(us[25], 2), "p10": round(us[5], 2), "p90": round(us[45], 2)}
+            table.append({"E": E, "T": T, "k": k, **res})
+            print(f"E {E:5d} T {T:5d} k {k}: warm {res['warm']['median']:7.2f} us  "
+                  f"cold {res['cold']['median']:7.2f} us", file=sys.stderr, flush=True)
+    print(json.dumps({"metric": "route + permute microseconds per call", "unit": "us",
+                      "higher_is_better": False, "data": "synthetic (seeded N(0,1) logits)",
+                      "table": table}))
+
+
 def main():
     args = parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU "
               "expert-parallel path is not built.", file=sys.stderr)
         sys.exit(2)
+    if args.routing_sweep:
+        routing_sweep()
+        return
 
     import torch
 
@@ -157,6 +219,31 @@ def main():
         torch.add(src, 1.0, out=dst)  # reads 256 MiB, writes 256 MiB
         torch.cuda.synchronize()
 
+    # Achievable HBM read rate on this part: the probe library streams 2 GiB once.
+    probe_gbs = None
+    probe_path = os.path.join(ROOT, "routing_grouped_expert_amd", "libhbmprobe.so")
+    if os.path.exists(probe_path):
+        import ctypes
+        plib = ctypes.CDLL(probe_path)
+        plib.hbm_read_probe.restype = ctypes.c_int
+        plib.hbm_read_probe.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                        ctypes.c_void_p]
+        nbytes = 2 << 30
+        pbuf = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+        sink = torch.zeros(4, dtype=torch.int32, device=dev)
+        sh = ctypes.c_void_p(stream.cuda_stream)
+        rc = plib.hbm_read_probe(pbuf.data_ptr(), nbytes, sink.data_ptr(), sh)
+        if rc == 0:
+            p0, p1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            p0.record(stream)
+            for _ in range(5):
+                rc |= plib.hbm_read_probe(pbuf.data_ptr(), nbytes, sink.data_ptr(), sh)
+            p1.record(stream)
+            torch.cuda.synchronize()
+            if rc == 0:
+                probe_gbs = nbytes / (p0.elapsed_time(p1) / 5 * 1e-3) / 1e9
+        del pbuf, sink
+
     routing = None
     if not args.no_routing:
         routing = {}
@@ -228,7 +315,9 @@ def main():
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": committed_traffic(args.workload),
                      "kernel": "grouped-FFN call (plan, W1 + SwiGLU, W2 kernels)",
-                     "kernel_ms": round(ffn_ms, 4), "algorithmic_bytes": ffn_bytes},
+                     "kernel_ms": round(ffn_ms, 4), "algorithmic_bytes": ffn_bytes,
+                     "hbm_read_probe_gbs": None if probe_gbs is None else round(probe_gbs, 1),
+                     "frac_of_probe": None if probe_gbs is None else round(achieved / probe_gbs, 4)},
         "cpu_baseline": cpu,
         "forward_ms_per_step": round(forward_ms, 4),
         "layer_hbm_frac": round(layer_bytes / (elapsed / args.steps) / 1e9 / HBM_PEAK_GBS, 4),

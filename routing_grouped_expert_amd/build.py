@@ -14,6 +14,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libmoe.so")
+PROBE_SRC = os.path.join(PKG, "probe", "hbm_probe.hip")
+PROBE_OUT = os.path.join(PKG, "libhbmprobe.so")
 BUILD = os.path.join(PKG, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -35,15 +37,21 @@ def _compile(src):
     return obj
 
 
+def _link(objs, out):
+    tmp = out + ".tmp"
+    subprocess.check_call([HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC"] + objs +
+                          ["-o", tmp])
+    os.replace(tmp, out)
+
+
 def build(jobs=8):
+    """Build libmoe.so and the measurement-only libhbmprobe.so (probe/)."""
     os.makedirs(BUILD, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     with ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = OUT + ".tmp"
-    subprocess.check_call([HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC"] + objs +
-                          ["-o", tmp])
-    os.replace(tmp, OUT)
+        objs = list(ex.map(_compile, srcs + [PROBE_SRC]))
+    _link(objs[:-1], OUT)
+    _link(objs[-1:], PROBE_OUT)
     return OUT
 
 
