@@ -29,6 +29,16 @@ def test_exports_every_declared_symbol():
     assert exported == names
 
 
+def test_probe_library_exports_its_one_symbol():
+    """The measurement-only read probe is a library of its own (not part of
+    moe.h): it exports hbm_read_probe and nothing named moe_*."""
+    path = os.path.join(os.path.dirname(moe.LIB_PATH), "libhbmprobe.so")
+    L = ctypes.CDLL(path)
+    assert hasattr(L, "hbm_read_probe")
+    out = os.popen(f"nm -D --defined-only {path}").read()
+    assert not re.findall(r" T (moe_\w+)$", out, re.M)
+
+
 def test_status_strings():
     L = moe.lib()
     for code, name in moe.STATUS.items():
