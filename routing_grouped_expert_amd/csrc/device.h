@@ -62,6 +62,31 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
   return r;
 }
 
+// Maximum / minimum of 32-bit unsigned values over a full wave, wave-uniform
+// (row rotations as above; the compiler folds each move into the max / min).
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, dpp_u32<0x121>(v));
+  v = max(v, dpp_u32<0x122>(v));
+  v = max(v, dpp_u32<0x124>(v));
+  v = max(v, dpp_u32<0x128>(v));
+  const uint32_t a = __builtin_amdgcn_readlane(static_cast<int>(v), 0);
+  const uint32_t b = __builtin_amdgcn_readlane(static_cast<int>(v), 16);
+  const uint32_t c = __builtin_amdgcn_readlane(static_cast<int>(v), 32);
+  const uint32_t d = __builtin_amdgcn_readlane(static_cast<int>(v), 48);
+  return max(max(a, b), max(c, d));
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+  v = min(v, dpp_u32<0x121>(v));
+  v = min(v, dpp_u32<0x122>(v));
+  v = min(v, dpp_u32<0x124>(v));
+  v = min(v, dpp_u32<0x128>(v));
+  const uint32_t a = __builtin_amdgcn_readlane(static_cast<int>(v), 0);
+  const uint32_t b = __builtin_amdgcn_readlane(static_cast<int>(v), 16);
+  const uint32_t c = __builtin_amdgcn_readlane(static_cast<int>(v), 32);
+  const uint32_t d = __builtin_amdgcn_readlane(static_cast<int>(v), 48);
+  return min(min(a, b), min(c, d));
+}
+
 // Butterfly sum: every lane ends with the same value, summed in the same
 // fixed order on every run.
 __device__ __forceinline__ float wave_sum_f32(float v) {

@@ -10,10 +10,9 @@
 // whatever E is, and the tier table plays the role of that page's section 2
 // (valid expert-count / block-size combinations fixed at compile time).
 //
-// Selection: k rounds of a wave-wide maximum over 64-bit keys
-//   key = (order-preserving bits of the logit) << 32 | (0xFFFFFFFF - id)
-// so the larger logit wins and, on equal logits, the lower id; -0 is folded
-// onto +0 first so the two compare equal. Weights: w_j = exp(l_j - l_0) /
+// Selection: k rounds of a wave-wide maximum of the order-preserving 32-bit
+// image of the logits; on equal logits the lower id wins; -0 is folded onto
+// +0 first so the two compare equal. Weights: w_j = exp(l_j - l_0) /
 // sum_i exp(l_i - l_0) over the k selected logits (the full-softmax
 // normaliser cancels in the renormalisation).
 #include "device.h"
@@ -22,45 +21,27 @@ namespace moe {
 
 namespace {
 
-__device__ __forceinline__ uint64_t make_key(float v, int id) {
-  v = v + 0.0f;  // -0 -> +0
-  uint32_t u = __float_as_uint(v);
-  uint32_t mono = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-  return (static_cast<uint64_t>(mono) << 32) | (0xFFFFFFFFu - static_cast<uint32_t>(id));
+// Order-preserving unsigned image of a logit (-0 folded onto +0): larger
+// logit, larger value. Lanes past E hold 0, below every logit's image.
+__device__ __forceinline__ uint32_t mono(float v) {
+  const uint32_t u = __float_as_uint(v + 0.0f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float from_mono(uint32_t m) {
+  return __uint_as_float((m & 0x80000000u) ? (m & 0x7FFFFFFFu) : ~m);
 }
 
-__device__ __forceinline__ float key_value(uint64_t key) {
-  uint32_t mono = static_cast<uint32_t>(key >> 32);
-  uint32_t u = (mono & 0x80000000u) ? (mono & 0x7FFFFFFFu) : ~mono;
-  return __uint_as_float(u);
-}
-
-__device__ __forceinline__ int key_id(uint64_t key) {
-  return static_cast<int>(0xFFFFFFFFu - static_cast<uint32_t>(key));
-}
-
-// Lane-local top two of the keys below `limit` (0 = none).
-template <int VPL>
-__device__ __forceinline__ void top2_below(const uint64_t (&key)[VPL], uint64_t limit, uint64_t& h1,
-                                           uint64_t& h2) {
-  h1 = 0;
-  h2 = 0;
-#pragma unroll
-  for (int i = 0; i < VPL; ++i) {
-    const uint64_t k = key[i] < limit ? key[i] : 0ull;
-    const bool c1 = k > h1, c2 = k > h2;
-    h2 = c1 ? h1 : (c2 ? k : h2);
-    h1 = c1 ? k : h1;
-  }
-}
-
-// Selection: every lane keeps the two largest of its keys not yet taken
-// (h1 > h2). A round takes the wave-wide maximum of the h1s; the lane that
-// held it moves h2 up, and when it wins a second time (its h2 already moved
-// up) it rescans its keys below the last one it gave. Lane j keeps the key
-// taken in round j.
+// Selection: every lane keeps the two best of its entries not yet taken
+// (h1 before h2 in the order: larger value first, then lower expert). A round
+// takes the wave-wide maximum of the h1 values; when several lanes hold it,
+// the lowest of their experts (a second reduction, skipped when one lane
+// holds it). The winning lane moves h2 up, and when it wins a second time
+// (its h2 already moved up) it rescans its entries after the one just taken.
+// Lane j keeps the entry taken in round j. A lane's entries are visited in
+// increasing expert order, so "greater than" keeps the lower expert on ties.
 // VEC (E a multiple of 4, 16-byte aligned logits, VPL >= 4): a lane loads its
-// values as groups of 4 consecutive experts, expert 4 (lane + 64 g) + c.
+// values as groups of 4 consecutive experts, expert 4 (lane + 64 g) + c;
+// otherwise entry i of a lane is expert lane + 64 i.
 template <int VPL, bool VEC>
 __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ logits, int T, int E,
                                                    int k, int* __restrict__ ids,
@@ -69,7 +50,10 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
   const int t = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
   if (t >= T) return;  // whole waves leave: every selection round runs on a full wave
   const float* l = logits + (size_t)t * E;
-  uint64_t key[VPL];
+  auto expert = [&](int i) -> uint32_t {
+    return VEC ? 4 * (lane + kWave * (i / 4)) + (i % 4) : lane + kWave * i;
+  };
+  uint32_t val[VPL];
   if constexpr (VEC) {
     f32x4 v[VPL / 4];
 #pragma unroll
@@ -78,46 +62,71 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
       v[g] = e < E ? *reinterpret_cast<const f32x4*>(l + e) : f32x4{0.f, 0.f, 0.f, 0.f};
     }
 #pragma unroll
-    for (int g = 0; g < VPL / 4; ++g)
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int e = 4 * (lane + kWave * g) + c;
-        key[4 * g + c] = e < E ? make_key(v[g][c], e) : 0ull;  // a valid key is never 0
-      }
+    for (int i = 0; i < VPL; ++i) val[i] = (int)expert(i) < E ? mono(v[i / 4][i % 4]) : 0u;
   } else {
 #pragma unroll
     for (int i = 0; i < VPL; ++i) {
-      const int e = lane + kWave * i;
-      key[i] = e < E ? make_key(l[e], e) : 0ull;  // a valid key is never 0
+      const int e = expert(i);
+      val[i] = e < E ? mono(l[e]) : 0u;
     }
   }
-  uint64_t h1, h2;
-  top2_below(key, ~0ull, h1, h2);
-  bool h2_fresh = true;  // h2 is this lane's second largest key below h1
-  uint64_t mine = 0, top = 0;
+  uint32_t h1v = 0, h1e = 0, h2v = 0, h2e = 0;
+  // the lane's best two entries after (bv, be) in the selection order
+  auto top2 = [&](bool bounded, uint32_t bv, uint32_t be) {
+    h1v = 0;
+    h2v = 0;
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+      const uint32_t e = expert(i);
+      uint32_t v = val[i];
+      if (bounded) v = (v < bv || (v == bv && e > be)) ? v : 0u;
+      const bool c1 = v > h1v, c2 = v > h2v;
+      h2v = c1 ? h1v : (c2 ? v : h2v);
+      h2e = c1 ? h1e : (c2 ? e : h2e);
+      h1v = c1 ? v : h1v;
+      h1e = c1 ? e : h1e;
+    }
+  };
+  top2(false, 0u, 0u);
+  bool h2_fresh = true;  // h2 is this lane's second best below h1
+  uint32_t mine_v = 0, mine_e = 0, top_v = 0;
   for (int j = 0; j < k; ++j) {
-    const uint64_t best = wave_max_u64(h1);
-    if (j == 0) top = best;
-    if (lane == j) mine = best;
-    const bool win = h1 == best;  // keys are unique: one lane
+    const uint32_t m = wave_max_u32(h1v);
+    const bool cand = h1v == m;
+    const uint64_t cm = __builtin_amdgcn_ballot_w64(cand);
+    uint32_t be;
+    bool win;
+    if (__builtin_popcountll(cm) == 1) {
+      be = __builtin_amdgcn_readlane(static_cast<int>(h1e), __builtin_ctzll(cm));
+      win = cand;
+    } else {
+      be = wave_min_u32(cand ? h1e : 0xFFFFFFFFu);
+      win = cand && h1e == be;
+    }
+    if (j == 0) top_v = m;
+    if (lane == j) {
+      mine_v = m;
+      mine_e = be;
+    }
     const bool rescan = win && !h2_fresh;
     if (win) {
-      h1 = h2;
+      h1v = h2v;
+      h1e = h2e;
       h2_fresh = false;
     }
     if (__builtin_amdgcn_ballot_w64(rescan)) {
       if (rescan) {
-        top2_below(key, best, h1, h2);
+        top2(true, m, be);
         h2_fresh = true;
       }
     }
   }
-  const float topv = key_value(top);
-  const float ex = lane < k ? expf(key_value(mine) - topv) : 0.0f;
+  const float topf = from_mono(top_v);
+  const float ex = lane < k ? expf(from_mono(mine_v) - topf) : 0.0f;
   float s = 0.0f;  // sum in slot order
   for (int j = 0; j < k; ++j) s += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ex), j));
   if (lane < k) {
-    ids[(size_t)t * k + lane] = key_id(mine);
+    ids[(size_t)t * k + lane] = static_cast<int>(mine_e);
     weights[(size_t)t * k + lane] = ex / s;
   }
 }
