@@ -62,6 +62,14 @@ class Oracle:
         L.oracle_grouped_ffn.argtypes = [u16, i32, i32, _I32, _I32, _I32, _I32, _I32, u16, u16,
                                          f64]
         L.oracle_grouped_ffn.restype = ctypes.c_int
+        u8 = _P(np.uint8, flags="C")
+        L.oracle_e4m3_value.argtypes = [ctypes.c_uint8]
+        L.oracle_e4m3_value.restype = ctypes.c_double
+        L.oracle_expert_row_fp8.argtypes = [u16, u8, f32, u8, f32, _I32, _I32, f64]
+        L.oracle_expert_row_fp8.restype = None
+        L.oracle_grouped_ffn_fp8.argtypes = [u16, i32, i32, _I32, _I32, _I32, _I32, _I32, u8, f32,
+                                             u8, f32, f64]
+        L.oracle_grouped_ffn_fp8.restype = ctypes.c_int
         L.oracle_combine.argtypes = [f64, i32, f64, _I32, _I32, _I32, f64]
         L.oracle_combine.restype = None
         L.oracle_forward.argtypes = [u16, f32, vp, u16, u16, _I32, _I32, _I32, _I32, _I32, _I32,
@@ -133,6 +141,37 @@ class Oracle:
             pr = np.zeros(1, np.int32)
         if self.lib.oracle_grouped_ffn(x, pr, _c(offsets, np.int32), L, T, k, H, I,
                                        _c(w1, np.uint16), _c(w2, np.uint16), out) != 0:
+            raise ValueError("invalid grouped FFN arguments")
+        return out[:n]
+
+    def e4m3_value(self, code):
+        """Value of one FP8 E4M3 code (uint8)."""
+        return self.lib.oracle_e4m3_value(int(code))
+
+    def expert_row_fp8(self, xrow, w1q, w1s, w2q, w2s):
+        xrow = _c(xrow, np.uint16)
+        H = xrow.shape[0]
+        I = w2q.shape[1]
+        out = np.empty(H, np.float64)
+        self.lib.oracle_expert_row_fp8(xrow, _c(w1q, np.uint8), _c(w1s, np.float32),
+                                       _c(w2q, np.uint8), _c(w2s, np.float32), H, I, out)
+        return out
+
+    def grouped_ffn_fp8(self, x, permuted_rows, offsets, k, w1q, w1s, w2q, w2s):
+        """grouped_ffn with FP8 E4M3 weight codes and per-row fp32 scales:
+        w1q [L, 2I, H], w1s [L, 2I], w2q [L, H, I], w2s [L, H]."""
+        x = _c(x, np.uint16)
+        T, H = x.shape
+        L = len(offsets) - 1
+        I = w2q.shape[2]
+        n = int(offsets[L]) if L > 0 else 0
+        out = np.empty((max(n, 1), H), np.float64)
+        pr = _c(permuted_rows, np.int32)
+        if pr.size == 0:
+            pr = np.zeros(1, np.int32)
+        if self.lib.oracle_grouped_ffn_fp8(x, pr, _c(offsets, np.int32), L, T, k, H, I,
+                                           _c(w1q, np.uint8), _c(w1s, np.float32),
+                                           _c(w2q, np.uint8), _c(w2s, np.float32), out) != 0:
             raise ValueError("invalid grouped FFN arguments")
         return out[:n]
 
@@ -209,6 +248,18 @@ def expert_row(*a, **kw):
 
 def grouped_ffn(*a, **kw):
     return default().grouped_ffn(*a, **kw)
+
+
+def e4m3_value(*a, **kw):
+    return default().e4m3_value(*a, **kw)
+
+
+def expert_row_fp8(*a, **kw):
+    return default().expert_row_fp8(*a, **kw)
+
+
+def grouped_ffn_fp8(*a, **kw):
+    return default().grouped_ffn_fp8(*a, **kw)
 
 
 def combine(*a, **kw):

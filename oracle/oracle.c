@@ -242,6 +242,77 @@ int oracle_grouped_ffn(const uint16_t* x, const int32_t* permuted_rows, const in
 }
 
 /* ------------------------------------------------------------------------ */
+/* FP8 expert weights (the FP8 path the [P-ACT] page mentions beside bf16 and
+ * fp16, section 2: FP8 E4M3 operands). Reading: the OCP "e4m3fn" encoding
+ * (sign bit, 4-bit exponent with bias 7, 3-bit mantissa; exponent 0 holds
+ * the subnormals m/8 * 2^-6; exponent 15 with mantissa 7 is NaN; no
+ * infinities), weights only (activations stay bf16), one fp32 scale per
+ * weight row: W[r, c] = scale[r] * value(q[r, c]). */
+double oracle_e4m3_value(uint8_t b) {
+  const int sign = b >> 7, e = (b >> 3) & 15, m = b & 7;
+  double v;
+  if (e == 15 && m == 7) return NAN;
+  if (e == 0)
+    v = ldexp((double)m / 8.0, -6);
+  else
+    v = ldexp(1.0 + (double)m / 8.0, e - 7);
+  return sign ? -v : v;
+}
+
+/* The expert FFN of oracle_expert_row with dequantised weights: W1 rows
+ * [0, I) gate and [I, 2I) up, W2 [H, I], each element scale[row] * value. */
+void oracle_expert_row_fp8(const uint16_t* xrow, const uint8_t* w1q, const float* w1s,
+                           const uint8_t* w2q, const float* w2s, int32_t H, int32_t I,
+                           double* out) {
+  double* xv = (double*)malloc(sizeof(double) * (size_t)H);
+  double* a = (double*)malloc(sizeof(double) * (size_t)I);
+  for (int32_t h = 0; h < H; ++h) xv[h] = bf16_val(xrow[h]);
+  for (int32_t i = 0; i < I; ++i) {
+    const uint8_t* qg = w1q + (int64_t)i * H;
+    const uint8_t* qu = w1q + (int64_t)(I + i) * H;
+    const double sg = (double)w1s[i], su = (double)w1s[I + i];
+    double g = 0.0, u = 0.0;
+    for (int32_t h = 0; h < H; ++h) g += sg * oracle_e4m3_value(qg[h]) * xv[h];
+    for (int32_t h = 0; h < H; ++h) u += su * oracle_e4m3_value(qu[h]) * xv[h];
+    const double silu_g = g / (1.0 + exp(-g));
+    a[i] = silu_g * u;
+  }
+  for (int32_t c = 0; c < H; ++c) {
+    const uint8_t* q = w2q + (int64_t)c * I;
+    const double sc = (double)w2s[c];
+    double acc = 0.0;
+    for (int32_t i = 0; i < I; ++i) acc += sc * oracle_e4m3_value(q[i]) * a[i];
+    out[c] = acc;
+  }
+  free(xv);
+  free(a);
+}
+
+/* oracle_grouped_ffn with FP8 weights: w1q [L, 2I, H] codes, w1s [L, 2I],
+ * w2q [L, H, I] codes, w2s [L, H]. */
+int oracle_grouped_ffn_fp8(const uint16_t* x, const int32_t* permuted_rows,
+                           const int32_t* offsets, int32_t L, int32_t T, int32_t k, int32_t H,
+                           int32_t I, const uint8_t* w1q, const float* w1s, const uint8_t* w2q,
+                           const float* w2s, double* expert_out) {
+  if (L < 0 || T < 0 || k < 1 || H < 1 || I < 1) return ORC_BAD;
+  int32_t n = L > 0 ? offsets[L] : 0;
+  for (int32_t p = 0; p < n; ++p) {
+    int32_t r = permuted_rows[p];
+    if (r < 0 || r >= T * k) return ORC_BAD;
+  }
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int32_t p = 0; p < n; ++p) {
+    int32_t i = 0;
+    while (offsets[i + 1] <= p) ++i;
+    int32_t row_tok = permuted_rows[p] / k;
+    oracle_expert_row_fp8(x + (int64_t)row_tok * H, w1q + (int64_t)i * 2 * I * H,
+                          w1s + (int64_t)i * 2 * I, w2q + (int64_t)i * H * I,
+                          w2s + (int64_t)i * H, H, I, expert_out + (int64_t)p * H);
+  }
+  return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------ */
 /* Routing-weighted combine back to token order:
  *   y[t, c] = sum over j = 0 .. k-1 of w[t, j] * expert_out[e2p[t*k + j], c],
  * skipping entries with e2p = -1 (experts outside the share), j ascending.

@@ -39,8 +39,9 @@ def lib():
         L.synth_tie_levels_f32.argtypes = [u64, u32, u32, i64, vp]
         L.synth_topk_ids.argtypes = [u64, u32, i32, i32, i32, vp]
         L.synth_uniform_int.argtypes = [u64, u32, i64, i64, vp]
+        L.synth_fp8_rows.argtypes = [u64, u32, u32, u32, i64, i64, d, vp, vp]
         for f in (L.synth_normal_f32, L.synth_normal_bf16, L.synth_tie_levels_f32,
-                  L.synth_topk_ids, L.synth_uniform_int):
+                  L.synth_topk_ids, L.synth_uniform_int, L.synth_fp8_rows):
             f.restype = None
         _lib = L
     return _lib
@@ -64,6 +65,18 @@ def normal_bf16(seed, tensor, shape, sigma, first_expert=0):
         ne, per = 1, out.size
     lib().synth_normal_bf16(seed, tensor, first_expert, ne, per, float(sigma), out.ctypes.data)
     return out
+
+
+def fp8_rows(seed, tensor, shape, sigma, first_expert=0):
+    """Per-row quantised FP8 E4M3 weights for an expert-stacked [L, R, C]
+    tensor: (codes uint8 [L, R, C], scales float32 [L, R]); the weight is
+    scale * value(code). Drawn from the same normals as normal_bf16."""
+    ne, rows, cols = shape
+    q = np.empty(shape, np.uint8)
+    s = np.empty((ne, rows), np.float32)
+    lib().synth_fp8_rows(seed, tensor, first_expert, ne, rows, cols, float(sigma), q.ctypes.data,
+                         s.ctypes.data)
+    return q, s
 
 
 def tie_levels_f32(seed, tensor, shape):

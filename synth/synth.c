@@ -118,3 +118,54 @@ void synth_uniform_int(uint64_t seed, uint32_t tensor, int64_t n, int64_t m, int
 #pragma omp parallel for schedule(static)
   for (int64_t i = 0; i < n; ++i) out[i] = (int64_t)(word_at(key, i) % (uint64_t)m);
 }
+
+/* OCP FP8 E4M3 ("e4m3fn": exponent bias 7, three mantissa bits, no
+ * infinities, 0x7F and 0xFF are NaN, largest finite value 448; OCP 8-bit
+ * Floating Point Specification, 2023). A finite float is rounded to the
+ * nearest code with ties to the even code; magnitudes of 448 and above
+ * saturate to 448. Input preparation only: it makes the quantised weights
+ * that both sides then read. */
+static uint8_t f32_to_e4m3(float f) {
+  const uint8_t sign = signbit(f) ? 0x80 : 0;
+  const double a = fabs((double)f);
+  if (a >= 448.0) return sign | 0x7E;
+  if (a < 0x1p-6) return sign | (uint8_t)rint(a * 512.0); /* units of 2^-9; 8 is 2^-6 */
+  int e;
+  const double fr = frexp(a, &e); /* a = fr * 2^e, fr in [0.5, 1) */
+  double m = rint((fr * 2.0 - 1.0) * 8.0);
+  int E = e + 6; /* biased exponent: a = (1 + m/8) * 2^(E - 7) */
+  if (m == 8.0) {
+    m = 0.0;
+    E += 1;
+  }
+  return sign | (uint8_t)(E << 3) | (uint8_t)m;
+}
+
+/* Weights quantised per output row: for each of num_experts experts (ids from
+ * first_expert) and each of its rows, the fp32 normals sigma * N(0,1) at
+ * indices row * cols + c of the expert's stream (the same numbers the bf16
+ * generator rounds), scale = max |w| / 448 over the row (1 for an all-zero
+ * row), codes q = e4m3(w / scale). q is [num_experts, rows, cols], scale
+ * [num_experts, rows]; the weight the layer uses is scale * value(q). */
+void synth_fp8_rows(uint64_t seed, uint32_t tensor, uint32_t first_expert, uint32_t num_experts,
+                    int64_t rows, int64_t cols, double sigma, uint8_t* q, float* scale) {
+  const int64_t total = rows * (int64_t)num_experts;
+#pragma omp parallel for schedule(dynamic, 16)
+  for (int64_t g = 0; g < total; ++g) {
+    const uint32_t le = (uint32_t)(g / rows);
+    const int64_t r = g % rows;
+    const uint64_t key = stream_key(seed, tensor, first_expert + le);
+    float amax = 0.0f;
+    for (int64_t c = 0; c < cols; ++c) {
+      const float w = (float)(sigma * normal_at(key, r * cols + c));
+      if (fabsf(w) > amax) amax = fabsf(w);
+    }
+    const float s = amax > 0.0f ? amax / 448.0f : 1.0f;
+    scale[g] = s;
+    uint8_t* dst = q + g * cols;
+    for (int64_t c = 0; c < cols; ++c) {
+      const float w = (float)(sigma * normal_at(key, r * cols + c));
+      dst[c] = f32_to_e4m3(w / s);
+    }
+  }
+}

@@ -249,6 +249,70 @@ def pin_grouped_ffn_structure(orc):
         assert np.array_equal(out[p], want), p
 
 
+# ------------------------------------------------------------- FP8 weights
+def _e4m3_ref(codes):
+    """Values of FP8 E4M3 codes by torch's float8_e4m3fn (a library decoder)."""
+    import torch
+    c = np.ascontiguousarray(codes, np.uint8)
+    return torch.from_numpy(c.reshape(-1)).view(torch.float8_e4m3fn).double().numpy().reshape(c.shape)
+
+
+def pin_e4m3_values(orc):
+    """All 256 codes against torch's float8_e4m3fn, and the OCP FP8
+    specification's landmarks: 448 (0x7E), the smallest normal 2^-6 (0x08),
+    the smallest subnormal 2^-9 (0x01), 1 (0x38), -2 (0xC0), -0 (0x80), NaN
+    (0x7F, 0xFF)."""
+    ref = _e4m3_ref(np.arange(256))
+    got = np.array([orc.e4m3_value(c) for c in range(256)])
+    nan = np.isnan(ref)
+    assert (np.isnan(got) == nan).all() and nan.sum() == 2
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert (got[0x7E], got[0x08], got[0x01], got[0x38], got[0xC0]) == (448.0, 2.0**-6, 2.0**-9, 1.0, -2.0)
+    assert got[0x80] == 0.0 and math.copysign(1.0, got[0x80]) < 0
+
+
+def _fp8_layer(seed, T, H, I, E, k):
+    """Random codes (no NaN) and per-row power-of-two scales, plus the same
+    weights as bf16 bits: scale * value is exact in bf16 for these scales."""
+    def codes(tensor, shape):
+        c = synth.uniform_int(seed, tensor, int(np.prod(shape)), 254).astype(np.uint8)
+        c[c >= 0x7F] += 1  # skip the NaN code 0x7F (0xFF is out of range)
+        return c.reshape(shape)
+
+    def scales(rows, e0):
+        r = np.arange(rows)
+        return np.stack([2.0 ** -(5 + (7 * r + 3 * e + e0) % 5) for e in range(E)]).astype(np.float32)
+
+    x = synth.normal_bf16(seed, 70, (T, H), 1.0)
+    q1, q2 = codes(71, (E, 2 * I, H)), codes(72, (E, H, I))
+    s1, s2 = scales(2 * I, 0), scales(H, 1)
+    w1 = _bf16(_e4m3_ref(q1) * s1[:, :, None])
+    w2 = _bf16(_e4m3_ref(q2) * s2[:, :, None])
+    assert np.array_equal(synth.bf16_to_f32(w1), (_e4m3_ref(q1) * s1[:, :, None]).astype(np.float32))
+    return x, q1, s1, q2, s2, w1, w2
+
+
+def pin_fp8_ffn_vs_bf16(orc):
+    """With per-row power-of-two scales every dequantised weight scale *
+    value is a bf16 number, so the FP8 grouped FFN equals the bf16 one on
+    those bf16 weights exactly (same terms, same order); scales differ by row
+    and by expert, so a scale taken from the wrong row or expert shows."""
+    T, H, I, E, k = 7, 16, 24, 3, 2
+    x, q1, s1, q2, s2, w1, w2 = _fp8_layer(11, T, H, I, E, k)
+    ids = synth.topk_ids(11, 73, T, E, k)
+    _, offsets, perm, _ = orc.permute(ids, E, 0, E)
+    got = orc.grouped_ffn_fp8(x, perm, offsets, k, q1, s1, q2, s2)
+    want = orc.grouped_ffn(x, perm, offsets, k, w1, w2)
+    assert np.array_equal(got, want)
+    # one expert row directly, and a share (experts 1..2)
+    assert np.array_equal(orc.expert_row_fp8(x[0], q1[1], s1[1], q2[1], s2[1]),
+                          orc.expert_row(x[0], w1[1], w2[1]))
+    _, offsets, perm, _ = orc.permute(ids, E, 1, 2)
+    got = orc.grouped_ffn_fp8(x, perm, offsets, k, q1[1:], s1[1:], q2[1:], s2[1:])
+    want = orc.grouped_ffn(x, perm, offsets, k, w1[1:], w2[1:])
+    assert np.array_equal(got, want)
+
+
 # ------------------------------------------------------------------ combine
 def pin_combine(orc):
     T, k, H = 4, 2, 3

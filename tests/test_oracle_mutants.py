@@ -4,7 +4,9 @@ Each mutant changes one place of oracle.c (on the CPU, in a temporary
 directory) to a plausible slip: a tie broken the wrong way, a missing
 renormalisation, an unstable sort, swapped gate and up projections, a wrong
 sign, a transposed operand, a dropped bias, an ignored weight, an off-by-one
-in the partition, a wrong gather divisor, fp32 accumulation in the router.
+in the partition, a wrong gather divisor, fp32 accumulation in the router, a
+wrong FP8 exponent bias or subnormal scale, an FP8 weight scale from the
+wrong row or dropped.
 """
 import os
 import shutil
@@ -35,6 +37,12 @@ MUTANTS = {
     "router_fp32_accumulate": ("double acc = 0.0;\n        for (int32_t h = 0; h < H; ++h) acc += xr[h] * (double)w[h];",
                                "float acc = 0.0f;\n        for (int32_t h = 0; h < H; ++h) acc += (float)(xr[h] * (double)w[h]);"),
     "softmax_not_shifted_by_max": ("p[e] = exp((double)l[e] - m);", "p[e] = exp((double)l[e] - m) + 1e-3;"),
+    "e4m3_exponent_bias": ("v = ldexp(1.0 + (double)m / 8.0, e - 7);",
+                           "v = ldexp(1.0 + (double)m / 8.0, e - 8);"),
+    "e4m3_subnormal_scale": ("v = ldexp((double)m / 8.0, -6);", "v = ldexp((double)m / 8.0, -7);"),
+    "fp8_up_scale_from_gate_row": ("const double sg = (double)w1s[i], su = (double)w1s[I + i];",
+                                   "const double sg = (double)w1s[i], su = (double)w1s[i];"),
+    "fp8_w2_scale_dropped": ("const double sc = (double)w2s[c];", "const double sc = 1.0;"),
     "counts_local_only": ("for (int64_t r = 0; r < n; ++r) counts[ids[r]] += 1;",
                           "for (int64_t r = 0; r < n; ++r) if (ids[r] >= first && ids[r] < first + L) counts[ids[r]] += 1;"),
 }

@@ -45,3 +45,29 @@ def test_workload_share_matches_full_layer():
     full = configs.layer_inputs(configs.WORKLOADS["tiny"], first=0, L=8)
     part = configs.layer_inputs(configs.WORKLOADS["tiny"], first=3, L=2)
     assert np.array_equal(full["w1"][3:5], part["w1"]) and np.array_equal(full["w2"][3:5], part["w2"])
+
+
+def test_fp8_rows_nearest_code_and_scale():
+    """The FP8 weight generator: scale = max|w| / 448 per row, and every code
+    is the nearest E4M3 value to w / scale (ties to the even code), checked by
+    brute force over all codes against torch's float8_e4m3fn decoding."""
+    import torch
+    R, C = 6, 200
+    q, s = synth.fp8_rows(21, synth.W2, (2, R, C), 0.02, first_expert=3)
+    vals = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).double().numpy()
+    finite = ~np.isnan(vals)
+    codes = np.arange(256)[finite]
+    for e in range(2):
+        w = synth.normal_f32(21, synth.W2, (R * C,), 0.02, expert=3 + e).reshape(R, C)
+        for r in range(R):
+            amax = np.float32(np.abs(w[r]).max())
+            assert s[e, r] == np.float32(amax / np.float32(448.0))
+            y = (w[r] / s[e, r]).astype(np.float64)
+            for c in range(C):
+                d = np.abs(vals[finite] - y[c])
+                best = codes[d == d.min()]
+                if len(best) > 1:  # a tie: the even code (equal magnitudes share parity)
+                    best = best[best % 2 == 0]
+                    best = best[np.sign(vals[best]) == np.sign(y[c])] if y[c] != 0 else best
+                assert q[e, r, c] in best, (e, r, c, y[c], q[e, r, c], best)
+            assert np.abs(vals[q[e, r]]).max() == 448.0
