@@ -167,6 +167,26 @@ moe_status moe_grouped_ffn(const uint16_t* x, const int32_t* permuted_rows,
                            float* expert_out, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * moe_grouped_ffn_fp8 -- moe_grouped_ffn with FP8 expert weights: the same
+ * gather, gate/up split, SwiGLU and down projection, with each weight row
+ * stored as FP8 E4M3 codes and one fp32 scale ([P-ACT] section 2 runs the
+ * grouped projection on FP8 E4M3 operands beside bf16 / fp16). Reading: the
+ * OCP "e4m3fn" encoding (bias 7, no infinities, 0x7F / 0xFF NaN), weights
+ * only (x stays bf16), W[r, c] = scale[r] * value(code[r, c]). Codes are
+ * widened to bf16 exactly, multiplied on bf16 MFMA with fp32 accumulation,
+ * and each finished row sum is multiplied by its row's scale.
+ *   w1q  [num_local, 2I, H] uint8 codes     w1s  [num_local, 2I] fp32 scales
+ *   w2q  [num_local, H, I] uint8 codes      w2s  [num_local, H] fp32 scales
+ * Every other argument, the workspace and the errors are as for
+ * moe_grouped_ffn; w1s and w2s must not be NULL.
+ */
+moe_status moe_grouped_ffn_fp8(const uint16_t* x, const int32_t* permuted_rows,
+                               const int32_t* expert_offsets, int32_t num_local, int32_t T,
+                               int32_t k, int32_t H, int32_t I, const uint8_t* w1q,
+                               const float* w1s, const uint8_t* w2q, const float* w2s,
+                               float* expert_out, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * moe_combine -- y[t, :] = sum over j ascending of topk_weights[t, j] *
  * expert_out[expanded_to_permuted[t*k + j], :], skipping -1 entries; fp32
  * accumulation and one round-to-nearest-even to bf16 ([P-VSA] section 3

@@ -39,6 +39,8 @@ _SIGS = {
                     ctypes.c_int),
     "moe_grouped_ffn": ([_VP, _VP, _VP, _I32, _I32, _I32, _I32, _I32, _VP, _VP, _VP, _VP, _SZ,
                          _VP], ctypes.c_int),
+    "moe_grouped_ffn_fp8": ([_VP, _VP, _VP, _I32, _I32, _I32, _I32, _I32, _VP, _VP, _VP, _VP, _VP,
+                             _VP, _SZ, _VP], ctypes.c_int),
     "moe_combine": ([_VP, _VP, _VP, _I32, _I32, _I32, _VP, _VP], ctypes.c_int),
     "moe_forward": ([_VP, _VP, _VP, _VP, _VP] + [_I32] * 7 + [_VP, _VP, _VP, _VP, _VP, _SZ, _VP],
                     ctypes.c_int),
@@ -126,6 +128,19 @@ def grouped_ffn(x, permuted_rows, expert_offsets, k, w1, w2, expert_out, ws, str
         _ptr(x), _ptr(permuted_rows), _ptr(expert_offsets), L, T, k, H, I, _ptr(w1), _ptr(w2),
         _ptr(expert_out), _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
         _stream(stream)))
+
+
+def grouped_ffn_fp8(x, permuted_rows, expert_offsets, k, w1q, w1s, w2q, w2s, expert_out, ws,
+                    stream=None):
+    """moe_grouped_ffn_fp8: w1q [L, 2I, H] and w2q [L, H, I] uint8 E4M3 codes,
+    w1s [L, 2I] and w2s [L, H] fp32 row scales."""
+    T, H = x.shape
+    L = expert_offsets.shape[0] - 1
+    I = w2q.shape[-1]
+    _check("moe_grouped_ffn_fp8", lib().moe_grouped_ffn_fp8(
+        _ptr(x), _ptr(permuted_rows), _ptr(expert_offsets), L, T, k, H, I, _ptr(w1q), _ptr(w1s),
+        _ptr(w2q), _ptr(w2s), _ptr(expert_out), _ptr(ws),
+        0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def combine(expert_out, expanded_to_permuted, topk_weights, y, stream=None):

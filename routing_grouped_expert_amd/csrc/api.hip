@@ -20,6 +20,10 @@ size_t ffn_workspace_bytes(int T, int k, int I, int L);
 hipError_t launch_grouped_ffn(const uint16_t* x, const int* perm, const int* offsets, int L, int T,
                               int k, int H, int I, const uint16_t* w1, const uint16_t* w2,
                               float* out, void* ws, hipStream_t stream);
+hipError_t launch_grouped_ffn_fp8(const uint16_t* x, const int* perm, const int* offsets, int L,
+                                  int T, int k, int H, int I, const uint8_t* w1q,
+                                  const float* w1s, const uint8_t* w2q, const float* w2s,
+                                  float* out, void* ws, hipStream_t stream);
 hipError_t launch_combine(const float* eo, const int* e2p, const float* w, int T, int k, int H,
                           uint16_t* y, hipStream_t stream);
 }  // namespace moe
@@ -203,6 +207,27 @@ moe_status moe_grouped_ffn(const uint16_t* x, const int32_t* permuted_rows,
   clear_stale_error();
   return launched(moe::launch_grouped_ffn(x, permuted_rows, expert_offsets, num_local, T, k, H, I,
                                           w1, w2, expert_out, ws, as_stream(stream)));
+}
+
+moe_status moe_grouped_ffn_fp8(const uint16_t* x, const int32_t* permuted_rows,
+                               const int32_t* expert_offsets, int32_t num_local, int32_t T,
+                               int32_t k, int32_t H, int32_t I, const uint8_t* w1q,
+                               const float* w1s, const uint8_t* w2q, const float* w2s,
+                               float* expert_out, void* ws, size_t ws_bytes, void* stream) {
+  if (T < 0 || k < 1 || num_local < 0) return MOE_ERROR_INVALID_VALUE;
+  if (k > kMaxTopK || num_local > kMaxExperts || (int64_t)T * k >= kMaxIndex)
+    return MOE_ERROR_UNSUPPORTED;
+  moe_status st = check_dims(T, k, H, I);
+  if (st != MOE_SUCCESS) return st;
+  if (T == 0 || num_local == 0) return MOE_SUCCESS;
+  if (!x || !permuted_rows || !expert_offsets || !w1q || !w1s || !w2q || !w2s || !expert_out)
+    return MOE_ERROR_INVALID_VALUE;
+  const size_t need = moe::ffn_workspace_bytes(T, k, I, num_local);
+  if (!ws || ws_bytes < need || !aligned256(ws)) return MOE_ERROR_WORKSPACE;
+  clear_stale_error();
+  return launched(moe::launch_grouped_ffn_fp8(x, permuted_rows, expert_offsets, num_local, T, k, H,
+                                              I, w1q, w1s, w2q, w2s, expert_out, ws,
+                                              as_stream(stream)));
 }
 
 moe_status moe_combine(const float* expert_out, const int32_t* expanded_to_permuted,

@@ -62,6 +62,29 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
   return r;
 }
 
+// Eight FP8 E4M3 (OCP e4m3fn) weight codes, lo = codes 0..3 and hi = codes
+// 4..7 in byte order, as eight bf16 values. Every E4M3 value is a bf16 value,
+// so the conversion is exact: the hardware decoder gives fp32, whose upper
+// 16 bits are the bf16 pattern.
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_hi16(f32x2 v) {
+  return (__float_as_uint(v[1]) & 0xFFFF0000u) | (__float_as_uint(v[0]) >> 16);
+}
+__device__ __forceinline__ bf16x8 e4m3x8_to_bf16(uint32_t lo, uint32_t hi) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  typedef uint32_t u32x4_ __attribute__((ext_vector_type(4)));
+  const u32x4_ r = {pack_hi16(__builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(lo), false)),
+                    pack_hi16(__builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(lo), true)),
+                    pack_hi16(__builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(hi), false)),
+                    pack_hi16(__builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(hi), true))};
+  return __builtin_bit_cast(bf16x8, r);
+#else
+  (void)lo;
+  (void)hi;
+  return bf16x8{};
+#endif
+}
+
 // Maximum / minimum of 32-bit unsigned values over a full wave, wave-uniform
 // (row rotations as above; the compiler folds each move into the max / min).
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {

@@ -43,13 +43,46 @@ __device__ __forceinline__ bf16x8 load8_checked(const uint16_t* row, int k0, int
 constexpr int STEPS = KC / 32;  // MFMA K-steps per chunk
 
 // The A fragments of one K chunk for this lane: row `row`, columns
-// k0 + 32 s + kq .. +8 for s < STEPS (the 16x16x32 A-operand layout).
-template <bool VEC>
-__device__ __forceinline__ void load_a(bf16x8 (&a)[STEPS], const uint16_t* row, int k0, int K,
+// k0 + 32 s + kq .. +8 for s < STEPS (the 16x16x32 A-operand layout). F8:
+// the row holds FP8 E4M3 codes, 8 bytes per fragment, widened to bf16
+// exactly (the row's scale is applied to the finished sums).
+template <bool VEC, bool F8>
+__device__ __forceinline__ void load_a(bf16x8 (&a)[STEPS], const void* row, int k0, int K,
                                        bool ok, int kq) {
+  if constexpr (F8) {
+    const uint8_t* r8 = static_cast<const uint8_t*>(row);
 #pragma unroll
-  for (int s = 0; s < STEPS; ++s)
-    a[s] = VEC ? load8(row + k0 + s * 32 + kq) : load8_checked(row, k0 + s * 32 + kq, K, ok);
+    for (int s = 0; s < STEPS; ++s) {
+      const int c = k0 + s * 32 + kq;
+      uint32_t lo = 0, hi = 0;
+      if (VEC) {
+        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+        const u32x2 v = *reinterpret_cast<const u32x2*>(r8 + c);
+        lo = v[0];
+        hi = v[1];
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const uint32_t b = (ok && c + j < K) ? r8[c + j] : 0u;
+          if (j < 4) lo |= b << (8 * j);
+          else hi |= b << (8 * (j - 4));
+        }
+      }
+      a[s] = e4m3x8_to_bf16(lo, hi);
+    }
+  } else {
+    const uint16_t* r = static_cast<const uint16_t*>(row);
+#pragma unroll
+    for (int s = 0; s < STEPS; ++s)
+      a[s] = VEC ? load8(r + k0 + s * 32 + kq) : load8_checked(r, k0 + s * 32 + kq, K, ok);
+  }
+}
+
+// Element `i` of a weight array of bf16 values (F8 false) or FP8 codes.
+template <bool F8>
+__device__ __forceinline__ const void* welem(const void* base, size_t i) {
+  return F8 ? static_cast<const void*>(static_cast<const uint8_t*>(base) + i)
+            : static_cast<const void*>(static_cast<const uint16_t*>(base) + i);
 }
 
 typedef uint16_t lds_row_t[KC + PAD];
@@ -98,12 +131,13 @@ __device__ __forceinline__ void clamp_range(const int* offsets, int e, int nmax,
   end = max(beg, min(end, nmax));
 }
 
-template <int NT, bool VEC>
+template <int NT, bool VEC, bool F8>
 __global__ __launch_bounds__(256) void ffn_up_kernel(const uint16_t* __restrict__ x,
                                                      const int* __restrict__ perm,
                                                      const int* __restrict__ offsets, int k, int H,
                                                      int I, int nmax,
-                                                     const uint16_t* __restrict__ w1,
+                                                     const void* __restrict__ w1,
+                                                     const float* __restrict__ s1,
                                                      uint16_t* __restrict__ h_hi,
                                                      uint16_t* __restrict__ h_lo) {
   constexpr int NR = NT * 16;
@@ -118,8 +152,8 @@ __global__ __launch_bounds__(256) void ffn_up_kernel(const uint16_t* __restrict_
   const int arow = i0 + (lane & 15);
   const int kq = (lane >> 4) * 8;
   const bool arow_ok = arow < I;
-  const uint16_t* wg = w1 + ((size_t)e * 2 * I + (arow_ok ? arow : 0)) * H;
-  const uint16_t* wu = wg + (size_t)I * H;
+  const void* wg = welem<F8>(w1, ((size_t)e * 2 * I + (arow_ok ? arow : 0)) * H);
+  const void* wu = welem<F8>(wg, (size_t)I * H);
 
   for (int pb = beg; pb < end; pb += NR) {
     const int pc = min(NR, end - pb);
@@ -142,8 +176,8 @@ __global__ __launch_bounds__(256) void ffn_up_kernel(const uint16_t* __restrict_
     // Weight fragments of one K chunk; the next chunk's are loaded while the
     // current one is multiplied, so HBM reads stay in flight across barriers.
     bf16x8 ag[STEPS], au[STEPS], ng[STEPS], nu[STEPS];
-    load_a<VEC>(ag, wg, 0, H, arow_ok, kq);
-    load_a<VEC>(au, wu, 0, H, arow_ok, kq);
+    load_a<VEC, F8>(ag, wg, 0, H, arow_ok, kq);
+    load_a<VEC, F8>(au, wu, 0, H, arow_ok, kq);
     for (int k0 = 0; k0 < H; k0 += KC) {
       __syncthreads();
       if (VEC) {
@@ -163,8 +197,8 @@ __global__ __launch_bounds__(256) void ffn_up_kernel(const uint16_t* __restrict_
       }
       __syncthreads();
       if (k0 + KC < H) {
-        load_a<VEC>(ng, wg, k0 + KC, H, arow_ok, kq);
-        load_a<VEC>(nu, wu, k0 + KC, H, arow_ok, kq);
+        load_a<VEC, F8>(ng, wg, k0 + KC, H, arow_ok, kq);
+        load_a<VEC, F8>(nu, wu, k0 + KC, H, arow_ok, kq);
       }
       switch (ntiles) {
 #define MOE_UP_CASE(n) \
@@ -191,7 +225,12 @@ __global__ __launch_bounds__(256) void ffn_up_kernel(const uint16_t* __restrict_
       uint16_t hi[4], lo[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float g = accg[nt][j], u = accu[nt][j];
+        float g = accg[nt][j], u = accu[nt][j];
+        if (F8) {
+          const int row = ir + j < I ? ir + j : 0;
+          g *= s1[(size_t)e * 2 * I + row];
+          u *= s1[(size_t)e * 2 * I + I + row];
+        }
         const float a = g / (1.0f + expf(-g)) * u;
         hi[j] = f32_to_bf16_bits(a);
         lo[j] = f32_to_bf16_bits(a - bf16_bits_to_f32(hi[j]));
@@ -213,12 +252,13 @@ __global__ __launch_bounds__(256) void ffn_up_kernel(const uint16_t* __restrict_
   }
 }
 
-template <int NT, bool VEC>
+template <int NT, bool VEC, bool F8>
 __global__ __launch_bounds__(256) void ffn_down_kernel(const uint16_t* __restrict__ h_hi,
                                                        const uint16_t* __restrict__ h_lo,
                                                        const int* __restrict__ offsets, int H,
                                                        int I, int nmax,
-                                                       const uint16_t* __restrict__ w2,
+                                                       const void* __restrict__ w2,
+                                                       const float* __restrict__ s2,
                                                        float* __restrict__ out) {
   constexpr int NR = NT * 16;
   __shared__ __attribute__((aligned(16))) uint16_t xh[NR][KC + PAD];
@@ -232,7 +272,7 @@ __global__ __launch_bounds__(256) void ffn_down_kernel(const uint16_t* __restric
   const int arow = c0 + (lane & 15);
   const int kq = (lane >> 4) * 8;
   const bool arow_ok = arow < H;
-  const uint16_t* w = w2 + ((size_t)e * H + (arow_ok ? arow : 0)) * I;
+  const void* w = welem<F8>(w2, ((size_t)e * H + (arow_ok ? arow : 0)) * I);
 
   for (int pb = beg; pb < end; pb += NR) {
     const int pc = min(NR, end - pb);
@@ -241,7 +281,7 @@ __global__ __launch_bounds__(256) void ffn_down_kernel(const uint16_t* __restric
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
     bf16x8 a[STEPS], na[STEPS];
-    load_a<VEC>(a, w, 0, I, arow_ok, kq);
+    load_a<VEC, F8>(a, w, 0, I, arow_ok, kq);
     for (int k0 = 0; k0 < I; k0 += KC) {
       __syncthreads();
       if (VEC) {
@@ -266,7 +306,7 @@ __global__ __launch_bounds__(256) void ffn_down_kernel(const uint16_t* __restric
         }
       }
       __syncthreads();
-      if (k0 + KC < I) load_a<VEC>(na, w, k0 + KC, I, arow_ok, kq);
+      if (k0 + KC < I) load_a<VEC, F8>(na, w, k0 + KC, I, arow_ok, kq);
       switch (ntiles) {
 #define MOE_DOWN_CASE(n) \
   case n:                \
@@ -280,6 +320,14 @@ __global__ __launch_bounds__(256) void ffn_down_kernel(const uint16_t* __restric
       for (int s = 0; s < STEPS; ++s) a[s] = na[s];
     }
     const int cr = c0 + (lane >> 4) * 4;
+    if (F8) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float sc = s2[(size_t)e * H + (cr + j < H ? cr + j : 0)];
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) acc[nt][j] *= sc;
+      }
+    }
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       const int n = nt * 16 + (lane & 15);
@@ -296,28 +344,46 @@ __global__ __launch_bounds__(256) void ffn_down_kernel(const uint16_t* __restric
   }
 }
 
-template <int NT>
+template <int NT, bool F8>
 hipError_t launch_nt(const uint16_t* x, const int* perm, const int* offsets, int L, int k, int H,
-                     int I, int nmax, const uint16_t* w1, const uint16_t* w2, uint16_t* h_hi,
-                     uint16_t* h_lo, float* out, bool vec, hipStream_t stream) {
+                     int I, int nmax, const void* w1, const float* s1, const void* w2,
+                     const float* s2, uint16_t* h_hi, uint16_t* h_lo, float* out, bool vec,
+                     hipStream_t stream) {
   dim3 g1((I + BLOCK_ROWS - 1) / BLOCK_ROWS, L), g2((H + BLOCK_ROWS - 1) / BLOCK_ROWS, L);
   if (vec) {
-    hipLaunchKernelGGL((ffn_up_kernel<NT, true>), g1, dim3(256), 0, stream, x, perm, offsets, k, H,
-                       I, nmax, w1, h_hi, h_lo);
+    hipLaunchKernelGGL((ffn_up_kernel<NT, true, F8>), g1, dim3(256), 0, stream, x, perm, offsets,
+                       k, H, I, nmax, w1, s1, h_hi, h_lo);
   } else {
-    hipLaunchKernelGGL((ffn_up_kernel<NT, false>), g1, dim3(256), 0, stream, x, perm, offsets, k,
-                       H, I, nmax, w1, h_hi, h_lo);
+    hipLaunchKernelGGL((ffn_up_kernel<NT, false, F8>), g1, dim3(256), 0, stream, x, perm, offsets,
+                       k, H, I, nmax, w1, s1, h_hi, h_lo);
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   if (vec) {
-    hipLaunchKernelGGL((ffn_down_kernel<NT, true>), g2, dim3(256), 0, stream, h_hi, h_lo, offsets,
-                       H, I, nmax, w2, out);
+    hipLaunchKernelGGL((ffn_down_kernel<NT, true, F8>), g2, dim3(256), 0, stream, h_hi, h_lo,
+                       offsets, H, I, nmax, w2, s2, out);
   } else {
-    hipLaunchKernelGGL((ffn_down_kernel<NT, false>), g2, dim3(256), 0, stream, h_hi, h_lo,
-                       offsets, H, I, nmax, w2, out);
+    hipLaunchKernelGGL((ffn_down_kernel<NT, false, F8>), g2, dim3(256), 0, stream, h_hi, h_lo,
+                       offsets, H, I, nmax, w2, s2, out);
   }
   return hipGetLastError();
+}
+
+template <bool F8>
+hipError_t launch_generic(const uint16_t* x, const int* perm, const int* offsets, int L, int T,
+                          int k, int H, int I, const void* w1, const float* s1, const void* w2,
+                          const float* s2, uint16_t* h_hi, uint16_t* h_lo, float* out, bool vec,
+                          hipStream_t stream) {
+  const int nmax = T * k;
+  // A token picks an expert at most once, so an expert has at most T entries.
+  const int bound = T < nmax ? T : nmax;
+  if (bound <= 16)
+    return launch_nt<1, F8>(x, perm, offsets, L, k, H, I, nmax, w1, s1, w2, s2, h_hi, h_lo, out, vec, stream);
+  if (bound <= 32)
+    return launch_nt<2, F8>(x, perm, offsets, L, k, H, I, nmax, w1, s1, w2, s2, h_hi, h_lo, out, vec, stream);
+  if (bound <= 64)
+    return launch_nt<4, F8>(x, perm, offsets, L, k, H, I, nmax, w1, s1, w2, s2, h_hi, h_lo, out, vec, stream);
+  return launch_nt<8, F8>(x, perm, offsets, L, k, H, I, nmax, w1, s1, w2, s2, h_hi, h_lo, out, vec, stream);
 }
 }  // namespace
 
@@ -350,20 +416,26 @@ bool ffn_vector_path(const void* x, const void* w1, const void* w2, const void* 
 hipError_t launch_grouped_ffn(const uint16_t* x, const int* perm, const int* offsets, int L, int T,
                               int k, int H, int I, const uint16_t* w1, const uint16_t* w2,
                               float* out, void* ws, hipStream_t stream) {
-  const int nmax = T * k;
   const size_t half = h_array_bytes(T, k, I);
   uint16_t* h_hi = static_cast<uint16_t*>(ws);
   uint16_t* h_lo = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + half);
   if (ffn_sk_applies(x, w1, w2, T, k, L, H, I))
     return launch_grouped_ffn_sk(x, perm, offsets, L, T, k, H, I, w1, w2, h_hi, h_lo, out,
                                  static_cast<char*>(ws) + 2 * half, stream);
-  const bool vec = ffn_vector_path(x, w1, w2, ws, H, I);
-  // A token picks an expert at most once, so an expert has at most T entries.
-  const int bound = T < nmax ? T : nmax;
-  if (bound <= 16) return launch_nt<1>(x, perm, offsets, L, k, H, I, nmax, w1, w2, h_hi, h_lo, out, vec, stream);
-  if (bound <= 32) return launch_nt<2>(x, perm, offsets, L, k, H, I, nmax, w1, w2, h_hi, h_lo, out, vec, stream);
-  if (bound <= 64) return launch_nt<4>(x, perm, offsets, L, k, H, I, nmax, w1, w2, h_hi, h_lo, out, vec, stream);
-  return launch_nt<8>(x, perm, offsets, L, k, H, I, nmax, w1, w2, h_hi, h_lo, out, vec, stream);
+  return launch_generic<false>(x, perm, offsets, L, T, k, H, I, w1, nullptr, w2, nullptr, h_hi,
+                               h_lo, out, ffn_vector_path(x, w1, w2, ws, H, I), stream);
+}
+
+// FP8 E4M3 weights with per-row fp32 scales (w1s [L, 2I], w2s [L, H]).
+hipError_t launch_grouped_ffn_fp8(const uint16_t* x, const int* perm, const int* offsets, int L,
+                                  int T, int k, int H, int I, const uint8_t* w1q,
+                                  const float* w1s, const uint8_t* w2q, const float* w2s,
+                                  float* out, void* ws, hipStream_t stream) {
+  const size_t half = h_array_bytes(T, k, I);
+  uint16_t* h_hi = static_cast<uint16_t*>(ws);
+  uint16_t* h_lo = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + half);
+  return launch_generic<true>(x, perm, offsets, L, T, k, H, I, w1q, w1s, w2q, w2s, h_hi, h_lo,
+                              out, ffn_vector_path(x, w1q, w2q, ws, H, I), stream);
 }
 
 }  // namespace moe

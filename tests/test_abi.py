@@ -18,7 +18,7 @@ def _declared():
 def test_exports_every_declared_symbol():
     names = _declared()
     assert {"moe_partition", "moe_workspace_size", "moe_router_logits", "moe_route",
-            "moe_permute", "moe_grouped_ffn", "moe_combine", "moe_forward",
+            "moe_permute", "moe_grouped_ffn", "moe_grouped_ffn_fp8", "moe_combine", "moe_forward",
             "moe_status_string", "moe_last_launch_error"} <= names
     L = ctypes.CDLL(moe.LIB_PATH)
     for n in sorted(names):
@@ -104,6 +104,15 @@ def test_calls_reject_bad_arguments_without_launching():
                              None) == 1
     assert L.moe_grouped_ffn(FAKE, FAKE, FAKE, 2, 4, 2, 64, 64, FAKE, FAKE, FAKE, FAKE, 8,
                              None) == 3
+    # grouped ffn with FP8 weights: bad dims, missing scales, workspace too small
+    assert L.moe_grouped_ffn_fp8(FAKE, FAKE, FAKE, 2, 4, 2, 0, 64, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                 FAKE, 1 << 20, None) == 1
+    assert L.moe_grouped_ffn_fp8(FAKE, FAKE, FAKE, 2, 4, 2, 64, 64, FAKE, None, FAKE, FAKE, FAKE,
+                                 FAKE, 1 << 20, None) == 1
+    assert L.moe_grouped_ffn_fp8(FAKE, FAKE, FAKE, 2, 4, 2, 64, 64, FAKE, FAKE, FAKE, None, FAKE,
+                                 FAKE, 1 << 20, None) == 1
+    assert L.moe_grouped_ffn_fp8(FAKE, FAKE, FAKE, 2, 4, 2, 64, 64, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                 FAKE, 8, None) == 3
     # combine: H = 0, k = 0
     assert L.moe_combine(FAKE, FAKE, FAKE, 4, 2, 0, FAKE, None) == 1
     assert L.moe_combine(FAKE, FAKE, FAKE, 4, 0, 8, FAKE, None) == 1
