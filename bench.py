@@ -41,6 +41,9 @@ def parse_args():
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the oracle timing (profiling runs)")
     ap.add_argument("--no-routing", action="store_true", help="skip the routing-only timings")
+    ap.add_argument("--weights", default="bf16", choices=["bf16", "fp8"],
+                    help="expert weight format: bf16 (the headline), or FP8 E4M3 codes with "
+                         "per-row fp32 scales (moe_grouped_ffn_fp8; x stays bf16)")
     ap.add_argument("--routing-sweep", action="store_true",
                     help="instead of the layer step: route + permute microseconds over "
                          "T in {1, 64, 4096} x E in {8 .. 4096}, k = 8 (k = E below 8), warm and "
@@ -151,7 +154,12 @@ def main():
 
     x, wg = to_dev(d["x"]), to_dev(d["wg"])
     bias = None if d["bias"] is None else to_dev(d["bias"])
-    w1, w2 = to_dev(d["w1"]), to_dev(d["w2"])
+    fp8 = args.weights == "fp8"
+    if fp8:
+        w1q, w1s, w2q, w2s = (to_dev(a) for a in configs.fp8_weights(d))
+        w1 = w2 = None
+    else:
+        w1, w2 = to_dev(d["w1"]), to_dev(d["w2"])
     y = torch.empty((T, H), dtype=torch.int16, device=dev)
     ws = moe.alloc_workspace(T, H, I, E, k, L)
     logits = torch.empty((T, E), dtype=torch.float32, device=dev)
@@ -171,7 +179,10 @@ def main():
         moe.permute(ids, E, first, L, counts, offsets, perm, e2p, ws, stream)
         if ev0 is not None:
             ev0.record(stream)
-        moe.grouped_ffn(x, perm, offsets, k, w1, w2, eo, ws, stream)
+        if fp8:
+            moe.grouped_ffn_fp8(x, perm, offsets, k, w1q, w1s, w2q, w2s, eo, ws, stream)
+        else:
+            moe.grouped_ffn(x, perm, offsets, k, w1, w2, eo, ws, stream)
         if ev1 is not None:
             ev1.record(stream)
         moe.combine(eo, e2p, wts, y, stream)
@@ -191,24 +202,27 @@ def main():
     ffn_ms = sum(e0.elapsed_time(e1) for e0, e1 in evs) / len(evs)
 
     # moe_forward over the same number of steps (same kernels in one call)
-    for _ in range(2):
-        moe.forward(x, wg, bias, w1, w2, k, first, L, y, ws, stream=stream)
-    torch.cuda.synchronize()
-    f0 = time.perf_counter()
-    for _ in range(args.steps):
-        moe.forward(x, wg, bias, w1, w2, k, first, L, y, ws, stream=stream)
-    torch.cuda.synchronize()
-    forward_ms = (time.perf_counter() - f0) / args.steps * 1e3
+    forward_ms = None
+    if not fp8:
+        for _ in range(2):
+            moe.forward(x, wg, bias, w1, w2, k, first, L, y, ws, stream=stream)
+        torch.cuda.synchronize()
+        f0 = time.perf_counter()
+        for _ in range(args.steps):
+            moe.forward(x, wg, bias, w1, w2, k, first, L, y, ws, stream=stream)
+        torch.cuda.synchronize()
+        forward_ms = (time.perf_counter() - f0) / args.steps * 1e3
 
     cnt = counts.cpu().numpy()[first:first + L]
     n_local = int(cnt.sum())
     touched = int(np.count_nonzero(cnt))
     # Algorithmic bytes of one grouped-FFN call: each touched expert's W1 and W2
-    # once (3*I*H bf16), each local entry's gathered row (H bf16) and its fp32
-    # output row (H fp32).
-    ffn_bytes = touched * 3 * I * H * 2 + n_local * H * 2 + n_local * H * 4
+    # once (3*I*H bf16, or 3*I*H FP8 codes plus 3 row scales per I or H rows),
+    # each local entry's gathered row (H bf16) and its fp32 output row (H fp32).
+    wbytes = 3 * I * H + (2 * I + H) * 4 if fp8 else 3 * I * H * 2
+    ffn_bytes = touched * wbytes + n_local * H * 2 + n_local * H * 4
     achieved = ffn_bytes / (ffn_ms * 1e-3) / 1e9
-    layer_bytes = configs.algorithmic_bytes(cfg, cnt)
+    layer_bytes = configs.algorithmic_bytes(cfg, cnt) - (touched * 3 * I * H * 2 - touched * wbytes)
     yv = y.cpu().numpy().view(np.uint16)
     assert np.isfinite((yv.astype(np.uint32) << 16).view(np.float32)).all()
 
@@ -271,7 +285,7 @@ def main():
             routing[f"T{Tr}"] = round(a.elapsed_time(b) / n_it * 1e3, 2)
 
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not fp8:  # the oracle baseline is reported for the bf16 layer
         import oracle
         d = configs.layer_inputs(cfg)
         n_tok = min(T, 32)
@@ -304,7 +318,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "bf16" if not fp8 else "bf16 activations, fp8-e4m3 weights (per-row fp32 scales)",
         "data": "synthetic (seeded normal inputs; random-init weights of the stated shapes)",
         "config": {"workload": f"{args.workload}: T={T} H={H} I={I} E={E} top-{k}"
                                + (f" share {cfg['s']} of {cfg['S']} (experts {first}..{first + L - 1})"
@@ -313,13 +327,13 @@ def main():
                    "local_experts": L},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": committed_traffic(args.workload),
+                     "traffic": None if fp8 else committed_traffic(args.workload),
                      "kernel": "grouped-FFN call (plan, W1 + SwiGLU, W2 kernels)",
                      "kernel_ms": round(ffn_ms, 4), "algorithmic_bytes": ffn_bytes,
                      "hbm_read_probe_gbs": None if probe_gbs is None else round(probe_gbs, 1),
                      "frac_of_probe": None if probe_gbs is None else round(achieved / probe_gbs, 4)},
         "cpu_baseline": cpu,
-        "forward_ms_per_step": round(forward_ms, 4),
+        "forward_ms_per_step": None if forward_ms is None else round(forward_ms, 4),
         "layer_hbm_frac": round(layer_bytes / (elapsed / args.steps) / 1e9 / HBM_PEAK_GBS, 4),
         "routing_us_1024_experts": routing,
     }

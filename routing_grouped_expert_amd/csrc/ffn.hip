@@ -390,6 +390,13 @@ hipError_t launch_generic(const uint16_t* x, const int* perm, const int* offsets
 bool ffn_sk_applies(const void* x, const void* w1, const void* w2, int T, int k, int L, int H,
                     int I);
 size_t ffn_sk_workspace_bytes(int T, int k, int L);
+bool ffn_sk_fp8_applies(const void* x, const void* w1q, const void* w2q, int T, int k, int L,
+                        int H, int I);
+hipError_t launch_grouped_ffn_sk_fp8(const uint16_t* x, const int* perm, const int* offsets,
+                                     int L, int T, int k, int H, int I, const uint8_t* w1q,
+                                     const float* w1s, const uint8_t* w2q, const float* w2s,
+                                     uint16_t* h_hi, uint16_t* h_lo, float* out, void* ws,
+                                     hipStream_t stream);
 hipError_t launch_grouped_ffn_sk(const uint16_t* x, const int* perm, const int* offsets, int L,
                                  int T, int k, int H, int I, const uint16_t* w1,
                                  const uint16_t* w2, uint16_t* h_hi, uint16_t* h_lo, float* out,
@@ -434,6 +441,9 @@ hipError_t launch_grouped_ffn_fp8(const uint16_t* x, const int* perm, const int*
   const size_t half = h_array_bytes(T, k, I);
   uint16_t* h_hi = static_cast<uint16_t*>(ws);
   uint16_t* h_lo = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + half);
+  if (ffn_sk_fp8_applies(x, w1q, w2q, T, k, L, H, I))
+    return launch_grouped_ffn_sk_fp8(x, perm, offsets, L, T, k, H, I, w1q, w1s, w2q, w2s, h_hi,
+                                     h_lo, out, static_cast<char*>(ws) + 2 * half, stream);
   return launch_generic<true>(x, perm, offsets, L, T, k, H, I, w1q, w1s, w2q, w2s, h_hi, h_lo,
                               out, ffn_vector_path(x, w1q, w2q, ws, H, I), stream);
 }

@@ -36,6 +36,8 @@
 //       writes fp32 expert_out.
 #include "device.h"
 
+#include <type_traits>
+
 namespace moe {
 
 namespace {
@@ -56,6 +58,14 @@ constexpr int DOWN_KUNIT = 2 * 4 * 32 * DOWN_STEPS;
 // Blocks per CU of the K-split kernels.
 constexpr int UP_CAP = 1;
 constexpr int DOWN_CAP = 1;
+// FP8 weights: MFMA steps per half unit (even: a 16-byte load of codes feeds
+// two steps) and blocks per CU.
+constexpr int UP8_STEPS = 4;
+constexpr int DOWN8_STEPS = 4;
+constexpr int UP8_KUNIT = 2 * 4 * 32 * UP8_STEPS;
+constexpr int DOWN8_KUNIT = 2 * 4 * 32 * DOWN8_STEPS;
+constexpr int UP8_CAP = 2;
+constexpr int DOWN8_CAP = 1;
 constexpr int UP_RG = 2;          // 16-row gate groups (and as many up groups) per up tile
 constexpr int UP_ROWS = 16 * UP_RG;
 constexpr int DOWN_GROUPS = 8;    // 16-row groups per down tile
@@ -351,6 +361,54 @@ __device__ __forceinline__ void up_mma(const UpOps<RG, S>& r, f32x4 (&acc)[2 * R
     }
 }
 
+// FP8 E4M3 weights (8-bit codes, one fp32 scale per row, applied to the
+// finished sums): in a half unit a lane loads 16 codes per weight row, the K
+// values of two MFMA steps: 16 (lane / 16) + 0..15 of each 64-wide piece of
+// its wave's range, codes 0..7 for the even step and 8..15 for the odd one.
+// The token fragments are loaded in the same K order, so the sum over K is
+// unchanged; codes are widened to bf16 exactly just before their MFMAs.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+template <int RG, int S>
+struct UpOps8 {
+  static_assert(S % 2 == 0, "pairs of MFMA steps");
+  u32x4 g[RG][S / 2], u[RG][S / 2];
+  bf16x8 x[S];
+};
+
+template <int RG, int S>
+__device__ __forceinline__ void up_load(UpOps8<RG, S>& r, const uint8_t* wg, const uint8_t* wu,
+                                        const uint16_t* x, int H, size_t kb) {
+#pragma unroll
+  for (int q = 0; q < RG; ++q)
+#pragma unroll
+    for (int p = 0; p < S / 2; ++p)
+      r.g[q][p] = *reinterpret_cast<const u32x4*>(wg + (size_t)q * 16 * H + kb + 64 * p);
+#pragma unroll
+  for (int q = 0; q < RG; ++q)
+#pragma unroll
+    for (int p = 0; p < S / 2; ++p)
+      r.u[q][p] = *reinterpret_cast<const u32x4*>(wu + (size_t)q * 16 * H + kb + 64 * p);
+#pragma unroll
+  for (int st = 0; st < S; ++st) r.x[st] = ld8(x + kb + 64 * (st / 2) + 8 * (st % 2));
+}
+
+template <int RG, int S>
+__device__ __forceinline__ void up_mma(const UpOps8<RG, S>& r, f32x4 (&acc)[2 * RG]) {
+#pragma unroll
+  for (int p = 0; p < S / 2; ++p)
+#pragma unroll
+    for (int q = 0; q < RG; ++q) {
+      const bf16x8 g0 = e4m3x8_to_bf16(r.g[q][p][0], r.g[q][p][1]);
+      const bf16x8 g1 = e4m3x8_to_bf16(r.g[q][p][2], r.g[q][p][3]);
+      const bf16x8 u0 = e4m3x8_to_bf16(r.u[q][p][0], r.u[q][p][1]);
+      const bf16x8 u1 = e4m3x8_to_bf16(r.u[q][p][2], r.u[q][p][3]);
+      acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(g0, r.x[2 * p], acc[q], 0, 0, 0);
+      acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(g1, r.x[2 * p + 1], acc[q], 0, 0, 0);
+      acc[RG + q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(u0, r.x[2 * p], acc[RG + q], 0, 0, 0);
+      acc[RG + q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(u1, r.x[2 * p + 1], acc[RG + q], 0, 0, 0);
+    }
+}
+
 // Per-tile state of the up projection, in two stages: `issue` loads the plan
 // entries and the permutation row of a tile early (one tile ahead); `finish`
 // turns them into addresses when the tile is reached, so those loads never
@@ -359,7 +417,7 @@ struct UpRaw {
   int g, ex, tb, tc, r;
 };
 struct UpTile {
-  int g, tb, tc;
+  int g, ex, tb, tc;
   size_t wrow;  // lane's gate row (+ its K offset) in W1
   size_t xoff;  // lane's token row (+ its K offset) in x
 };
@@ -382,6 +440,7 @@ template <int RG>
 __device__ __forceinline__ void up_finish(UpTile& st, const UpRaw& raw, int k, int H, int I,
                                           int nmax, int lane, int kq) {
   st.g = raw.g;
+  st.ex = raw.ex;
   st.tb = raw.tb;
   st.tc = raw.tc;
   st.wrow = ((size_t)raw.ex * 2 * I + raw.g * (16 * RG) + (lane & 15)) * H + kq;
@@ -389,12 +448,16 @@ __device__ __forceinline__ void up_finish(UpTile& st, const UpRaw& raw, int k, i
   st.xoff = (size_t)(r / k) * H + kq;
 }
 
-template <int RG, int S>
+template <int RG, int S, bool F8>
 __global__ __launch_bounds__(256) void ffn_up_sk_kernel(
     const uint16_t* __restrict__ x, const int* __restrict__ perm, int k, int H, int I, int nmax,
-    const uint16_t* __restrict__ w1, const int* __restrict__ plan, int pmax, f32x4* slots,
-    int* counters, uint16_t* __restrict__ h_hi, uint16_t* __restrict__ h_lo, int NB) {
+    const void* __restrict__ w1v, const float* __restrict__ s1, const int* __restrict__ plan,
+    int pmax, f32x4* slots, int* counters, uint16_t* __restrict__ h_hi,
+    uint16_t* __restrict__ h_lo, int NB) {
   constexpr int KHALF = 4 * 32 * S, KUNIT = 2 * KHALF, N = 2 * RG;
+  using WT = std::conditional_t<F8, uint8_t, uint16_t>;
+  using Ops = std::conditional_t<F8, UpOps8<RG, S>, UpOps<RG, S>>;
+  const WT* w1 = static_cast<const WT*>(w1v);
   __shared__ f32x4 red[2][4][RCH][kWave];
   const PlanRO pv = plan_ro(plan, pmax);
   const int P = pv.hdr[0];
@@ -403,7 +466,7 @@ __global__ __launch_bounds__(256) void ffn_up_sk_kernel(
   const Sched rg(b, P * G, C, NB);
   if (b >= rg.nb) return;
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-  const int kq = (lane >> 4) * 8 + wave * 32 * S;
+  const int kq = (lane >> 4) * (F8 ? 16 : 8) + wave * 32 * S;
   const size_t I_H = (size_t)I * H;
 
   UpTile ts, tn;
@@ -437,7 +500,12 @@ __global__ __launch_bounds__(256) void ffn_up_sk_kernel(
           u16x4 hi, lo;
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            const float gg = acc[q][j], uu = acc[RG + q][j];
+            float gg = acc[q][j], uu = acc[RG + q][j];
+            if (F8) {
+              const size_t row = (size_t)ts.ex * 2 * I + ts.g * (16 * RG) + q * 16 + (lane >> 4) * 4 + j;
+              gg *= s1[row];
+              uu *= s1[row + I];
+            }
             const float a = gg / (1.0f + expf(-gg)) * uu;
             hi[j] = f32_to_bf16_bits(a);
             lo[j] = f32_to_bf16_bits(a - bf16_bits_to_f32(hi[j]));
@@ -457,7 +525,7 @@ __global__ __launch_bounds__(256) void ffn_up_sk_kernel(
   // tile when this unit ends one), multiply the second; finish the tile when
   // this is its last unit in the block. Every unit starts with its first
   // half in flight in `h0`, so no register changes role between units.
-  UpOps<RG, S> h0, h1;
+  Ops h0, h1;
   up_load(h0, w1 + ts.wrow, w1 + ts.wrow + I_H, x + ts.xoff, H, (size_t)rg.p0.kc * KUNIT);
   __builtin_amdgcn_sched_barrier(0);
   for (Pos p = rg.p0;;) {
@@ -516,12 +584,50 @@ __device__ __forceinline__ void down_mma(const DownOps<DG, S>& r, f32x4 (&acc)[D
     }
 }
 
+// FP8 weights for the down projection, with the K order of UpOps8.
+template <int DG, int S>
+struct DownOps8 {
+  static_assert(S % 2 == 0, "pairs of MFMA steps");
+  u32x4 a[DG][S / 2];
+  bf16x8 h[S], l[S];
+};
+
+template <int DG, int S>
+__device__ __forceinline__ void down_load(DownOps8<DG, S>& r, const uint8_t* w, int I,
+                                          const uint16_t* hh, const uint16_t* hl, size_t kb) {
+#pragma unroll
+  for (int q = 0; q < DG; ++q)
+#pragma unroll
+    for (int p = 0; p < S / 2; ++p)
+      r.a[q][p] = *reinterpret_cast<const u32x4*>(w + (size_t)q * 16 * I + kb + 64 * p);
+#pragma unroll
+  for (int st = 0; st < S; ++st) {
+    r.h[st] = ld8(hh + kb + 64 * (st / 2) + 8 * (st % 2));
+    r.l[st] = ld8(hl + kb + 64 * (st / 2) + 8 * (st % 2));
+  }
+}
+
+template <int DG, int S>
+__device__ __forceinline__ void down_mma(const DownOps8<DG, S>& r, f32x4 (&acc)[DG]) {
+#pragma unroll
+  for (int p = 0; p < S / 2; ++p)
+#pragma unroll
+    for (int q = 0; q < DG; ++q) {
+      const bf16x8 a0 = e4m3x8_to_bf16(r.a[q][p][0], r.a[q][p][1]);
+      const bf16x8 a1 = e4m3x8_to_bf16(r.a[q][p][2], r.a[q][p][3]);
+      acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, r.h[2 * p], acc[q], 0, 0, 0);
+      acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, r.l[2 * p], acc[q], 0, 0, 0);
+      acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, r.h[2 * p + 1], acc[q], 0, 0, 0);
+      acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, r.l[2 * p + 1], acc[q], 0, 0, 0);
+    }
+}
+
 // Per-tile state of the down projection (plan entries loaded a tile ahead).
 struct DownRaw {
   int g, ex, tb, tc;
 };
 struct DownTile {
-  int g, tb, tc;
+  int g, ex, tb, tc;
   size_t wrow;  // lane's first W2 row (+ its K offset)
   size_t hrow;  // lane's row of h (+ its K offset)
 };
@@ -538,6 +644,7 @@ template <int DG>
 __device__ __forceinline__ void down_finish(DownTile& st, const DownRaw& raw, int H, int I,
                                             int lane, int kq) {
   st.g = raw.g;
+  st.ex = raw.ex;
   st.tb = raw.tb;
   st.tc = raw.tc;
   st.wrow = ((size_t)raw.ex * H + raw.g * (16 * DG) + (lane & 15)) * I + kq;
@@ -545,12 +652,15 @@ __device__ __forceinline__ void down_finish(DownTile& st, const DownRaw& raw, in
   st.hrow = (size_t)(raw.tb + (n < raw.tc ? n : 0)) * I + kq;
 }
 
-template <int DG, int S>
+template <int DG, int S, bool F8>
 __global__ __launch_bounds__(256) void ffn_down_sk_kernel(
     const uint16_t* __restrict__ h_hi, const uint16_t* __restrict__ h_lo, int H, int I,
-    const uint16_t* __restrict__ w2, const int* __restrict__ plan, int pmax, f32x4* slots,
-    int* counters, float* __restrict__ out, int NB) {
+    const void* __restrict__ w2v, const float* __restrict__ s2, const int* __restrict__ plan,
+    int pmax, f32x4* slots, int* counters, float* __restrict__ out, int NB) {
   constexpr int KHALF = 4 * 32 * S, KUNIT = 2 * KHALF;
+  using WT = std::conditional_t<F8, uint8_t, uint16_t>;
+  using Ops = std::conditional_t<F8, DownOps8<DG, S>, DownOps<DG, S>>;
+  const WT* w2 = static_cast<const WT*>(w2v);
   __shared__ f32x4 red[2][4][RCH][kWave];
   const PlanRO pv = plan_ro(plan, pmax);
   const int P = pv.hdr[0];
@@ -559,7 +669,7 @@ __global__ __launch_bounds__(256) void ffn_down_sk_kernel(
   const Sched rg(b, P * G, C, NB);
   if (b >= rg.nb) return;
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-  const int kq = (lane >> 4) * 8 + wave * 32 * S;
+  const int kq = (lane >> 4) * (F8 ? 16 : 8) + wave * 32 * S;
 
   DownTile ts, tn;
   DownRaw rn;
@@ -581,6 +691,13 @@ __global__ __launch_bounds__(256) void ffn_down_sk_kernel(
       bool done = true;
       if (rg.split(tile)) done = fixup(acc, slots, counters, tile - rg.TD, C, rg.US, rg.nb, b, lane);
       const int n = lane & 15;
+      if (F8) {
+#pragma unroll
+        for (int q = 0; q < DG; ++q)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            acc[q][j] *= s2[(size_t)ts.ex * H + ts.g * (16 * DG) + q * 16 + (lane >> 4) * 4 + j];
+      }
       if (done && n < ts.tc) {
         float* o = out + (size_t)(ts.tb + n) * H + ts.g * (16 * DG) + (lane >> 4) * 4;
 #pragma unroll
@@ -592,7 +709,7 @@ __global__ __launch_bounds__(256) void ffn_down_sk_kernel(
   };
 
   // Units in two halves, as in the up projection.
-  DownOps<DG, S> h0, h1;
+  Ops h0, h1;
   down_load(h0, w2 + ts.wrow, I, h_hi + ts.hrow, h_lo + ts.hrow, (size_t)rg.p0.kc * KUNIT);
   __builtin_amdgcn_sched_barrier(0);
   for (Pos p = rg.p0;;) {
@@ -930,15 +1047,16 @@ int device_cus() {
   return cached[dev];
 }
 
-// Resident blocks of `threads` threads of `kernel` on the current device (cached).
-template <typename K>
-int resident_blocks(K kernel, int threads = 256, int cap = 8) {
+// Resident blocks of `threads` threads of kernel K on the current device
+// (cached per kernel and device).
+template <auto K>
+int resident_blocks(int threads = 256, int cap = 8) {
   static int cached[64] = {0};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
   if (cached[dev] == 0) {
     int per_cu = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess ||
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, K, threads, 0) != hipSuccess ||
         per_cu <= 0)
       per_cu = 1;
     if (per_cu > cap) per_cu = cap;  // at most 8: the workspace holds slots for 8 blocks per CU
@@ -964,21 +1082,25 @@ int pick_nt(int T, int k, int L) {
 size_t a256(size_t n) { return (n + 255) & ~(size_t)255; }
 
 template <int NT>
-int up_blocks() {
-  if constexpr (NT == 1) return resident_blocks(ffn_up_sk_kernel<UP_RG, UP_STEPS>, 256, UP_CAP);
-  else return resident_blocks(ffn_pf_kernel<NT, true>, PF_THREADS);
+int up_blocks(bool f8) {
+  if constexpr (NT == 1)
+    return f8 ? resident_blocks<ffn_up_sk_kernel<UP_RG, UP8_STEPS, true>>(256, UP8_CAP)
+              : resident_blocks<ffn_up_sk_kernel<UP_RG, UP_STEPS, false>>(256, UP_CAP);
+  else return resident_blocks<ffn_pf_kernel<NT, true>>(PF_THREADS);
 }
 template <int NT>
-int down_blocks() {
-  if constexpr (NT == 1) return resident_blocks(ffn_down_sk_kernel<DOWN_GROUPS, DOWN_STEPS>, 256, DOWN_CAP);
-  else return resident_blocks(ffn_pf_kernel<NT, false>, PF_THREADS);
+int down_blocks(bool f8) {
+  if constexpr (NT == 1)
+    return f8 ? resident_blocks<ffn_down_sk_kernel<DOWN_GROUPS, DOWN8_STEPS, true>>(256, DOWN8_CAP)
+              : resident_blocks<ffn_down_sk_kernel<DOWN_GROUPS, DOWN_STEPS, false>>(256, DOWN_CAP);
+  else return resident_blocks<ffn_pf_kernel<NT, false>>(PF_THREADS);
 }
 
-int blocks_for(int NT, bool up) {
+int blocks_for(int NT, bool up, bool f8) {
   switch (NT) {
-    case 1: return up ? up_blocks<1>() : down_blocks<1>();
-    case 4: return up ? up_blocks<4>() : down_blocks<4>();
-    default: return up ? up_blocks<8>() : down_blocks<8>();
+    case 1: return up ? up_blocks<1>(f8) : down_blocks<1>(f8);
+    case 4: return up ? up_blocks<4>(false) : down_blocks<4>(false);
+    default: return up ? up_blocks<8>(false) : down_blocks<8>(false);
   }
 }
 
@@ -993,12 +1115,12 @@ struct SkLayout {
   int pmax, nb_up, nb_down, subs;
 };
 
-SkLayout sk_layout(int T, int k, int L, int NT) {
+SkLayout sk_layout(int T, int k, int L, int NT, bool f8) {
   SkLayout o{};
   const int nmax = T * k, nr = NT * 16;
   o.pmax = L + (nmax + nr - 1) / nr + 1;
-  o.nb_up = blocks_for(NT, true);
-  o.nb_down = blocks_for(NT, false);
+  o.nb_up = blocks_for(NT, true, f8);
+  o.nb_down = blocks_for(NT, false, f8);
   const int nbm = o.nb_up > o.nb_down ? o.nb_up : o.nb_down;
   o.plan = 0;
   o.subs = NT == 1 ? 1 : PF_WAVES;
@@ -1011,9 +1133,12 @@ SkLayout sk_layout(int T, int k, int L, int NT) {
 
 template <int NT>
 hipError_t launch_sk_nt(const uint16_t* x, const int* perm, const int* offsets, int L, int T,
-                        int k, int H, int I, const uint16_t* w1, const uint16_t* w2,
-                        uint16_t* h_hi, uint16_t* h_lo, float* out, char* ws, hipStream_t stream) {
-  const SkLayout lo = sk_layout(T, k, L, NT);
+                        int k, int H, int I, const void* w1, const void* w2, const float* s1,
+                        const float* s2, uint16_t* h_hi, uint16_t* h_lo, float* out, char* ws,
+                        hipStream_t stream) {
+  // s1 / s2 non-null: FP8 weights with row scales (K-split kernels only)
+  const bool f8 = s1 != nullptr;
+  const SkLayout lo = sk_layout(T, k, L, NT, f8);
   int* plan = reinterpret_cast<int*>(ws + lo.plan);
   int* counters = reinterpret_cast<int*>(ws + lo.counters);
   f32x4* slots = reinterpret_cast<f32x4*>(ws + lo.slots);
@@ -1024,24 +1149,34 @@ hipError_t launch_sk_nt(const uint16_t* x, const int* perm, const int* offsets, 
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   if constexpr (NT == 1) {
-    hipLaunchKernelGGL((ffn_up_sk_kernel<UP_RG, UP_STEPS>), dim3(lo.nb_up), dim3(256), 0, stream, x,
-                       perm, k, H, I, nmax, w1, plan, lo.pmax, slots, counters, h_hi, h_lo,
-                       lo.nb_up);
+    if (f8)
+      hipLaunchKernelGGL((ffn_up_sk_kernel<UP_RG, UP8_STEPS, true>), dim3(lo.nb_up), dim3(256), 0,
+                         stream, x, perm, k, H, I, nmax, w1, s1, plan, lo.pmax, slots, counters,
+                         h_hi, h_lo, lo.nb_up);
+    else
+      hipLaunchKernelGGL((ffn_up_sk_kernel<UP_RG, UP_STEPS, false>), dim3(lo.nb_up), dim3(256), 0,
+                         stream, x, perm, k, H, I, nmax, w1, s1, plan, lo.pmax, slots, counters,
+                         h_hi, h_lo, lo.nb_up);
   } else {
     hipLaunchKernelGGL((ffn_pf_kernel<NT, true>), dim3(lo.nb_up), dim3(PF_THREADS), 0, stream, x, x,
-                       perm, k, H, I, nmax, w1, plan, lo.pmax, slots, counters, h_hi, h_lo,
-                       out, lo.nb_up);
+                       perm, k, H, I, nmax, static_cast<const uint16_t*>(w1), plan, lo.pmax, slots,
+                       counters, h_hi, h_lo, out, lo.nb_up);
   }
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   if constexpr (NT == 1) {
-    hipLaunchKernelGGL((ffn_down_sk_kernel<DOWN_GROUPS, DOWN_STEPS>), dim3(lo.nb_down), dim3(256), 0,
-                       stream, h_hi, h_lo, H, I, w2, plan, lo.pmax, slots, counters + lo.subs * nbm,
-                       out, lo.nb_down);
+    if (f8)
+      hipLaunchKernelGGL((ffn_down_sk_kernel<DOWN_GROUPS, DOWN8_STEPS, true>), dim3(lo.nb_down),
+                         dim3(256), 0, stream, h_hi, h_lo, H, I, w2, s2, plan, lo.pmax, slots,
+                         counters + lo.subs * nbm, out, lo.nb_down);
+    else
+      hipLaunchKernelGGL((ffn_down_sk_kernel<DOWN_GROUPS, DOWN_STEPS, false>), dim3(lo.nb_down),
+                         dim3(256), 0, stream, h_hi, h_lo, H, I, w2, s2, plan, lo.pmax, slots,
+                         counters + lo.subs * nbm, out, lo.nb_down);
   } else {
     hipLaunchKernelGGL((ffn_pf_kernel<NT, false>), dim3(lo.nb_down), dim3(PF_THREADS), 0, stream, h_hi,
-                       h_lo, perm, k, H, I, nmax, w2, plan, lo.pmax, slots, counters + lo.subs * nbm,
-                       h_hi, h_lo, out, lo.nb_down);
+                       h_lo, perm, k, H, I, nmax, static_cast<const uint16_t*>(w2), plan, lo.pmax,
+                       slots, counters + lo.subs * nbm, h_hi, h_lo, out, lo.nb_down);
   }
   return hipGetLastError();
 }
@@ -1060,7 +1195,11 @@ bool ffn_sk_applies(const void* x, const void* w1, const void* w2, int T, int k,
 }
 
 size_t ffn_sk_workspace_bytes(int T, int k, int L) {
-  return sk_layout(T, k, L, pick_nt(T, k, L)).total;
+  const int nt = pick_nt(T, k, L);
+  const size_t a = sk_layout(T, k, L, nt, false).total;
+  if (nt != 1) return a;
+  const size_t b = sk_layout(T, k, L, nt, true).total;  // the FP8 kernels' share of it
+  return a > b ? a : b;
 }
 
 hipError_t launch_grouped_ffn_sk(const uint16_t* x, const int* perm, const int* offsets, int L,
@@ -1069,10 +1208,28 @@ hipError_t launch_grouped_ffn_sk(const uint16_t* x, const int* perm, const int* 
                                  void* ws, hipStream_t stream) {
   char* w = static_cast<char*>(ws);
   switch (pick_nt(T, k, L)) {
-    case 1: return launch_sk_nt<1>(x, perm, offsets, L, T, k, H, I, w1, w2, h_hi, h_lo, out, w, stream);
-    case 4: return launch_sk_nt<4>(x, perm, offsets, L, T, k, H, I, w1, w2, h_hi, h_lo, out, w, stream);
-    default: return launch_sk_nt<8>(x, perm, offsets, L, T, k, H, I, w1, w2, h_hi, h_lo, out, w, stream);
+    case 1: return launch_sk_nt<1>(x, perm, offsets, L, T, k, H, I, w1, w2, nullptr, nullptr, h_hi, h_lo, out, w, stream);
+    case 4: return launch_sk_nt<4>(x, perm, offsets, L, T, k, H, I, w1, w2, nullptr, nullptr, h_hi, h_lo, out, w, stream);
+    default: return launch_sk_nt<8>(x, perm, offsets, L, T, k, H, I, w1, w2, nullptr, nullptr, h_hi, h_lo, out, w, stream);
   }
+}
+
+// FP8 weights (codes + row scales) on the K-split kernels: shapes for which
+// ffn_sk_fp8_applies holds.
+bool ffn_sk_fp8_applies(const void* x, const void* w1q, const void* w2q, int T, int k, int L,
+                        int H, int I) {
+  auto al = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
+  return al(x) && al(w1q) && al(w2q) && pick_nt(T, k, L) == 1 && H % UP8_KUNIT == 0 &&
+         I % DOWN8_KUNIT == 0 && I % UP_ROWS == 0 && H % DOWN_ROWS == 0;
+}
+
+hipError_t launch_grouped_ffn_sk_fp8(const uint16_t* x, const int* perm, const int* offsets,
+                                     int L, int T, int k, int H, int I, const uint8_t* w1q,
+                                     const float* w1s, const uint8_t* w2q, const float* w2s,
+                                     uint16_t* h_hi, uint16_t* h_lo, float* out, void* ws,
+                                     hipStream_t stream) {
+  return launch_sk_nt<1>(x, perm, offsets, L, T, k, H, I, w1q, w2q, w1s, w2s, h_hi, h_lo, out,
+                         static_cast<char*>(ws), stream);
 }
 
 }  // namespace moe

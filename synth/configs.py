@@ -8,7 +8,7 @@ bytes as experts 0..L-1 of the whole layer.
 """
 import numpy as np
 
-from . import BIAS, LOGITS, W1, W2, WG, X, normal_bf16, normal_f32, tie_levels_f32
+from . import BIAS, LOGITS, W1, W2, WG, X, fp8_rows, normal_bf16, normal_f32, tie_levels_f32
 
 # name -> shape. S/s: number of shares and the share this GPU runs; first/L: the
 # share's expert range as the workload states it (the partition rule itself is
@@ -62,6 +62,16 @@ def layer_inputs(cfg, T=None, H=None, I=None, seed=None, first=None, L=None):
     out["w1"] = normal_bf16(sd, W1, (L, 2 * I, H), SIGMA_W, first_expert=first)
     out["w2"] = normal_bf16(sd, W2, (L, H, I), SIGMA_W, first_expert=first)
     return out
+
+
+def fp8_weights(d):
+    """FP8 E4M3 expert weights with per-row scales for the layer drawn by
+    layer_inputs (the same normals its bf16 W1 / W2 round): returns
+    (w1q [L,2I,H] uint8, w1s [L,2I] fp32, w2q [L,H,I] uint8, w2s [L,H] fp32)."""
+    sd, H, I, first, L = d["seed"], d["H"], d["I"], d["first"], d["L"]
+    w1q, w1s = fp8_rows(sd, W1, (L, 2 * I, H), SIGMA_W, first_expert=first)
+    w2q, w2s = fp8_rows(sd, W2, (L, H, I), SIGMA_W, first_expert=first)
+    return w1q, w1s, w2q, w2s
 
 
 def routing_logits(T, E=ROUTING["E"], seed=ROUTING["seed"], ties=False):

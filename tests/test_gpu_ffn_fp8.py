@@ -68,3 +68,41 @@ def test_ffn_fp8_checked_path_ragged(H, I):
 
 def test_ffn_fp8_share_and_empty_experts():
     check_ffn_fp8(40, 128, 256, 16, 2, 3, 9)
+
+
+# K-split kernels (H and I multiples of 1024, at most 16 mean-doubled entries
+# per expert). On a 256-CU part (FP8 up kernel 512 blocks, down kernel 256):
+# tiles dealt whole (24, 1024, 1024), stream-K with cut tiles for the up
+# kernel (32, 4096, 1024), (16, 4096, 1024), (40, 2048, 1024) and the down
+# kernel (16, 1024, 4096), one whole round then cut tiles in both (40, 4096,
+# 2048).
+@pytest.mark.parametrize("T,H,I,E,k", [(24, 1024, 1024, 8, 2), (32, 4096, 1024, 8, 2),
+                                       (16, 4096, 1024, 4, 1), (16, 1024, 4096, 4, 1),
+                                       (40, 2048, 1024, 20, 2), (40, 4096, 2048, 20, 2)])
+def test_ffn_fp8_stream_k(T, H, I, E, k):
+    check_ffn_fp8(T, H, I, E, k, 0, E)
+
+
+def test_ffn_fp8_stream_k_share():
+    check_ffn_fp8(12, 1024, 1024, 12, 2, 4, 5)
+
+
+def test_ffn_fp8_decode_full_size_sampled():
+    """The decode-shaped layer at full size (T32 H4096 I14336 E8 top-2) on
+    FP8 weights, in the launch configuration bench.py times: every output row
+    of four sampled entries against the oracle's single-entry FFN."""
+    from synth import configs
+    d = configs.layer_inputs(configs.WORKLOADS["decode"])
+    T, H, I, E, k = d["T"], d["H"], d["I"], d["E"], d["k"]
+    note(f"ffn fp8 decode full size T={T} H={H} I={I} E={E} k={k}")
+    w1q, w1s, w2q, w2s = configs.fp8_weights(d)
+    ids = synth.topk_ids(d["seed"], synth.IDS, T, E, k)
+    _, offsets, perm, _ = oracle.permute(ids, E, 0, E)
+    got = run_ffn_fp8(d["x"], perm, offsets, k, w1q, w1s, w2q, w2s)
+    n = int(offsets[-1])
+    assert np.isnan(got[n:]).all()
+    for p in (0, n // 3, (2 * n) // 3, n - 1):
+        e = int(np.searchsorted(offsets, p, side="right") - 1)
+        ref = oracle.expert_row_fp8(d["x"][perm[p] // k], w1q[e], w1s[e], w2q[e], w2s[e])
+        err = np.abs(got[p].astype(np.float64) - ref)
+        assert err.max() <= 1e-4 * np.abs(ref).max(), (p, err.max() / np.abs(ref).max())
