@@ -59,6 +59,17 @@ def test_forward_odd_shapes():
     check_forward(configs.layer_inputs(cfg, T=45, H=200, I=72), what="odd shapes")
 
 
+@pytest.mark.parametrize("T,E,k,first,L", [(1, 8, 2, 0, 8), (33, 64, 1, 5, 50),
+                                            (17, 100, 4, 30, 20), (64, 200, 8, 0, 16),
+                                            (40, 384, 8, 300, 12), (64, 1000, 8, 990, 10)])
+def test_forward_small_batches(T, E, k, first, L):
+    """Up to 64 tokens with H, I multiples of the persistent FFN kernels'
+    tiles: every values-per-lane routing tier, K-split and token-staged FFN
+    passes, shares that start inside the expert range."""
+    cfg = dict(configs.WORKLOADS["fine"], E=E, k=k, first=first, L=L)
+    check_forward(configs.layer_inputs(cfg, T=T, H=512, I=1024), what="small batch")
+
+
 def test_forward_shares_sum_to_whole_layer():
     """Weights are renormalised before the share mask, so the shares' outputs
     add up to the whole layer (up to one bf16 rounding per share)."""
