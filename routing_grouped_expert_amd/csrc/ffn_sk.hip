@@ -19,8 +19,10 @@
 // counter) adds the slots in block order and finishes the tile. The order of
 // every sum is fixed by the schedule, so results do not depend on timing.
 //
-// Operands: weight rows are the MFMA A operand and stream from HBM straight
-// into VGPRs (16 rows x 64 B per load instruction); the gathered token rows
+// Operands: weight rows are the MFMA A operand and stream from HBM into VGPRs
+// as whole 128-byte lines (8 rows x 128 B per load instruction; bf16 weights
+// then pass through a small wave-private LDS tile into fragment order, see
+// slab_frags); the gathered token rows
 // (page "FlashInfer MoE optimisation: overlapping grouped activation staging
 // on Ampere and Hopper", flashinfer PR #7368, section 1: route index divided
 // by the route divisor, 128-bit loads, absent members read as zero) are the B
@@ -127,6 +129,47 @@ __global__ __launch_bounds__(1024) void ffn_plan_kernel(const int* __restrict__ 
 
 __device__ __forceinline__ bf16x8 ld8(const uint16_t* p) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(p));
+}
+
+// Full-line weight slabs (bf16 weights). Per row group a wave's weight
+// operands for two MFMA K-steps are a slab of 16 rows x 64 elements (128
+// bytes, one cache line per row). Loaded as MFMA fragments (lane l: row
+// l % 16, 16 bytes), every load instruction reads half of each of 16 lines;
+// loaded as two full-line loads (lane s: row s / 8, then 8 + s / 8, 16-byte
+// chunk s % 8) with the nontemporal policy (every weight byte is read once),
+// a plain stream of such slabs reads 6.6-7.0 TB/s on MI355X against 4.9-6.1
+// TB/s. The wave then puts the slab in fragment order through a private 2 KB
+// LDS tile: fragment st of lane l is chunk 4 st + l / 16 of row l % 16, the
+// K order the token fragments already use. In the tile, chunk c of row r
+// sits at slot c ^ (r % 8) of the row's 128 bytes, so both the writes and the
+// reads spread over the LDS banks.
+constexpr bool kFullLines = true;
+
+// The lane's offset (elements) in a slab whose rows are ld elements apart.
+__device__ __forceinline__ size_t slab_lane(int lane, size_t ld) {
+  return (size_t)(lane >> 3) * ld + (lane & 7) * 8;
+}
+
+__device__ __forceinline__ bf16x8 ldnt8(const uint16_t* p) {
+  return __builtin_bit_cast(bf16x8, __builtin_nontemporal_load(reinterpret_cast<const u16x8*>(p)));
+}
+
+// The two full-line loads of the slab whose row 0 (at the slab's K offset,
+// plus the lane's slab offset) is at p.
+__device__ __forceinline__ void slab_load(bf16x8 (&v)[2], const uint16_t* p, size_t ld) {
+  v[0] = ldnt8(p);
+  v[1] = ldnt8(p + 8 * ld);
+}
+
+// Slab -> the two MFMA fragments, in place, through the wave's tile t
+// (128 u16x8, private to the wave).
+__device__ __forceinline__ void slab_frags(bf16x8 (&v)[2], u16x8* t, int lane) {
+  const int r0 = lane >> 3, c = lane & 7;
+  t[r0 * 8 + (c ^ r0)] = __builtin_bit_cast(u16x8, v[0]);
+  t[(8 + r0) * 8 + (c ^ r0)] = __builtin_bit_cast(u16x8, v[1]);
+  const int r = lane & 15, g = lane >> 4, x = r & 7;
+  v[0] = __builtin_bit_cast(bf16x8, t[r * 8 + (g ^ x)]);
+  v[1] = __builtin_bit_cast(bf16x8, t[r * 8 + ((4 + g) ^ x)]);
 }
 
 // Block containing unit u when U units are cut into NB equal ranges
@@ -334,24 +377,42 @@ struct UpOps {
 // Loads go out row group by row group, so a lane's requests to one weight
 // row follow each other (on the down projection at the decode shape this
 // order took 176 us against 199 us for the groups interleaved step by step).
+// With full-line slabs (S = 2) g / u hold the slabs until up_mma turns them
+// into fragments.
 template <int RG, int S>
 __device__ __forceinline__ void up_load(UpOps<RG, S>& r, const uint16_t* wg, const uint16_t* wu,
                                         const uint16_t* x, int H, size_t kb) {
+  if constexpr (kFullLines) {
+    static_assert(S == 2, "a slab is two MFMA steps");
 #pragma unroll
-  for (int q = 0; q < RG; ++q)
+    for (int q = 0; q < RG; ++q) slab_load(r.g[q], wg + (size_t)q * 16 * H + kb, H);
 #pragma unroll
-    for (int st = 0; st < S; ++st) r.g[q][st] = ld8(wg + (size_t)q * 16 * H + kb + 32 * st);
+    for (int q = 0; q < RG; ++q) slab_load(r.u[q], wu + (size_t)q * 16 * H + kb, H);
+  } else {
 #pragma unroll
-  for (int q = 0; q < RG; ++q)
+    for (int q = 0; q < RG; ++q)
 #pragma unroll
-    for (int st = 0; st < S; ++st) r.u[q][st] = ld8(wu + (size_t)q * 16 * H + kb + 32 * st);
+      for (int st = 0; st < S; ++st) r.g[q][st] = ld8(wg + (size_t)q * 16 * H + kb + 32 * st);
+#pragma unroll
+    for (int q = 0; q < RG; ++q)
+#pragma unroll
+      for (int st = 0; st < S; ++st) r.u[q][st] = ld8(wu + (size_t)q * 16 * H + kb + 32 * st);
+  }
 #pragma unroll
   for (int st = 0; st < S; ++st) r.x[st] = ld8(x + kb + 32 * st);
 }
 
-// acc[q]: gate group q, acc[RG + q]: up group q.
+// acc[q]: gate group q, acc[RG + q]: up group q. t: the wave's LDS tiles
+// (2 RG of 128 u16x8) for the full-line slabs.
 template <int RG, int S>
-__device__ __forceinline__ void up_mma(const UpOps<RG, S>& r, f32x4 (&acc)[2 * RG]) {
+__device__ __forceinline__ void up_mma(UpOps<RG, S>& r, f32x4 (&acc)[2 * RG], u16x8* t, int lane) {
+  if constexpr (kFullLines) {
+#pragma unroll
+    for (int q = 0; q < RG; ++q) {
+      slab_frags(r.g[q], t + (2 * q) * 128, lane);
+      slab_frags(r.u[q], t + (2 * q + 1) * 128, lane);
+    }
+  }
 #pragma unroll
   for (int st = 0; st < S; ++st)
 #pragma unroll
@@ -393,7 +454,7 @@ __device__ __forceinline__ void up_load(UpOps8<RG, S>& r, const uint8_t* wg, con
 }
 
 template <int RG, int S>
-__device__ __forceinline__ void up_mma(const UpOps8<RG, S>& r, f32x4 (&acc)[2 * RG]) {
+__device__ __forceinline__ void up_mma(const UpOps8<RG, S>& r, f32x4 (&acc)[2 * RG], u16x8*, int) {
 #pragma unroll
   for (int p = 0; p < S / 2; ++p)
 #pragma unroll
@@ -438,12 +499,12 @@ __device__ __forceinline__ void up_issue(UpRaw& raw, int tile, int G, const Plan
 // stored, so every load of the main loop is unconditional.
 template <int RG>
 __device__ __forceinline__ void up_finish(UpTile& st, const UpRaw& raw, int k, int H, int I,
-                                          int nmax, int lane, int kq) {
+                                          int nmax, size_t wlane, int kq) {
   st.g = raw.g;
   st.ex = raw.ex;
   st.tb = raw.tb;
   st.tc = raw.tc;
-  st.wrow = ((size_t)raw.ex * 2 * I + raw.g * (16 * RG) + (lane & 15)) * H + kq;
+  st.wrow = ((size_t)raw.ex * 2 * I + raw.g * (16 * RG)) * H + wlane;
   const int r = (raw.r >= 0 && raw.r < nmax) ? raw.r : 0;
   st.xoff = (size_t)(r / k) * H + kq;
 }
@@ -459,6 +520,8 @@ __global__ __launch_bounds__(256) void ffn_up_sk_kernel(
   using Ops = std::conditional_t<F8, UpOps8<RG, S>, UpOps<RG, S>>;
   const WT* w1 = static_cast<const WT*>(w1v);
   __shared__ f32x4 red[2][4][RCH][kWave];
+  constexpr bool FL = kFullLines && !F8;
+  __shared__ u16x8 slab_t[FL ? 4 : 1][FL ? 2 * RG * 128 : 1];  // per wave: 2 RG slab tiles
   const PlanRO pv = plan_ro(plan, pmax);
   const int P = pv.hdr[0];
   const int G = I / (16 * RG), C = H / KUNIT;
@@ -467,6 +530,9 @@ __global__ __launch_bounds__(256) void ffn_up_sk_kernel(
   if (b >= rg.nb) return;
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int kq = (lane >> 4) * (F8 ? 16 : 8) + wave * 32 * S;
+  // lane's offset from a row group's first row in W1
+  const size_t wlane = FL ? slab_lane(lane, H) + wave * 32 * S : (size_t)(lane & 15) * H + kq;
+  u16x8* tw = slab_t[FL ? wave : 0];
   const size_t I_H = (size_t)I * H;
 
   UpTile ts, tn;
@@ -474,7 +540,7 @@ __global__ __launch_bounds__(256) void ffn_up_sk_kernel(
   {
     UpRaw r0;
     up_issue(r0, rg.p0.t, G, pv, perm, lane);
-    up_finish<RG>(ts, r0, k, H, I, nmax, lane, kq);
+    up_finish<RG>(ts, r0, k, H, I, nmax, wlane, kq);
   }
   up_issue(rn, rg.next_tile(rg.p0.t), G, pv, perm, lane);
   __builtin_amdgcn_sched_barrier(0);  // ahead of the weight loads
@@ -531,17 +597,17 @@ __global__ __launch_bounds__(256) void ffn_up_sk_kernel(
   for (Pos p = rg.p0;;) {
     up_load(h1, w1 + ts.wrow, w1 + ts.wrow + I_H, x + ts.xoff, H, (size_t)p.kc * KUNIT + KHALF);
     __builtin_amdgcn_sched_barrier(0);
-    up_mma(h0, acc);
+    up_mma(h0, acc, tw, lane);
     const Pos pn = rg.next(p);  // past the end: p again (loaded, unused)
     if (pn.t != p.t) {
-      up_finish<RG>(tn, rn, k, H, I, nmax, lane, kq);
+      up_finish<RG>(tn, rn, k, H, I, nmax, wlane, kq);
       up_issue(rn, rg.next_tile(pn.t), G, pv, perm, lane);  // the tile after
     } else {
       tn = ts;
     }
     up_load(h0, w1 + tn.wrow, w1 + tn.wrow + I_H, x + tn.xoff, H, (size_t)pn.kc * KUNIT);
     __builtin_amdgcn_sched_barrier(0);
-    up_mma(h1, acc);
+    up_mma(h1, acc, tw, lane);
     if (rg.ends_tile(p)) tile_end(p.t);
     if (rg.last(p)) break;
     ts = tn;
@@ -562,10 +628,16 @@ struct DownOps {
 template <int DG, int S>
 __device__ __forceinline__ void down_load(DownOps<DG, S>& r, const uint16_t* w, int I,
                                           const uint16_t* hh, const uint16_t* hl, size_t kb) {
+  if constexpr (kFullLines) {
+    static_assert(S == 2, "a slab is two MFMA steps");
 #pragma unroll
-  for (int q = 0; q < DG; ++q)
+    for (int q = 0; q < DG; ++q) slab_load(r.a[q], w + (size_t)q * 16 * I + kb, I);
+  } else {
 #pragma unroll
-    for (int st = 0; st < S; ++st) r.a[q][st] = ld8(w + (size_t)q * 16 * I + kb + 32 * st);
+    for (int q = 0; q < DG; ++q)
+#pragma unroll
+      for (int st = 0; st < S; ++st) r.a[q][st] = ld8(w + (size_t)q * 16 * I + kb + 32 * st);
+  }
 #pragma unroll
   for (int st = 0; st < S; ++st) {
     r.h[st] = ld8(hh + kb + 32 * st);
@@ -573,8 +645,13 @@ __device__ __forceinline__ void down_load(DownOps<DG, S>& r, const uint16_t* w, 
   }
 }
 
+// t: the wave's LDS tiles (DG of 128 u16x8) for the full-line slabs.
 template <int DG, int S>
-__device__ __forceinline__ void down_mma(const DownOps<DG, S>& r, f32x4 (&acc)[DG]) {
+__device__ __forceinline__ void down_mma(DownOps<DG, S>& r, f32x4 (&acc)[DG], u16x8* t, int lane) {
+  if constexpr (kFullLines) {
+#pragma unroll
+    for (int q = 0; q < DG; ++q) slab_frags(r.a[q], t + q * 128, lane);
+  }
 #pragma unroll
   for (int st = 0; st < S; ++st)
 #pragma unroll
@@ -608,7 +685,7 @@ __device__ __forceinline__ void down_load(DownOps8<DG, S>& r, const uint8_t* w, 
 }
 
 template <int DG, int S>
-__device__ __forceinline__ void down_mma(const DownOps8<DG, S>& r, f32x4 (&acc)[DG]) {
+__device__ __forceinline__ void down_mma(const DownOps8<DG, S>& r, f32x4 (&acc)[DG], u16x8*, int) {
 #pragma unroll
   for (int p = 0; p < S / 2; ++p)
 #pragma unroll
@@ -642,12 +719,12 @@ __device__ __forceinline__ void down_issue(DownRaw& raw, int tile, int G, const 
 
 template <int DG>
 __device__ __forceinline__ void down_finish(DownTile& st, const DownRaw& raw, int H, int I,
-                                            int lane, int kq) {
+                                            int lane, size_t wlane, int kq) {
   st.g = raw.g;
   st.ex = raw.ex;
   st.tb = raw.tb;
   st.tc = raw.tc;
-  st.wrow = ((size_t)raw.ex * H + raw.g * (16 * DG) + (lane & 15)) * I + kq;
+  st.wrow = ((size_t)raw.ex * H + raw.g * (16 * DG)) * I + wlane;
   const int n = lane & 15;  // slots past the entries read the first entry's row
   st.hrow = (size_t)(raw.tb + (n < raw.tc ? n : 0)) * I + kq;
 }
@@ -662,6 +739,8 @@ __global__ __launch_bounds__(256) void ffn_down_sk_kernel(
   using Ops = std::conditional_t<F8, DownOps8<DG, S>, DownOps<DG, S>>;
   const WT* w2 = static_cast<const WT*>(w2v);
   __shared__ f32x4 red[2][4][RCH][kWave];
+  constexpr bool FL = kFullLines && !F8;
+  __shared__ u16x8 slab_t[FL ? 4 : 1][FL ? DG * 128 : 1];  // per wave: DG slab tiles
   const PlanRO pv = plan_ro(plan, pmax);
   const int P = pv.hdr[0];
   const int G = H / (16 * DG), C = I / KUNIT;
@@ -670,13 +749,16 @@ __global__ __launch_bounds__(256) void ffn_down_sk_kernel(
   if (b >= rg.nb) return;
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int kq = (lane >> 4) * (F8 ? 16 : 8) + wave * 32 * S;
+  // lane's offset from a row group's first row in W2
+  const size_t wlane = FL ? slab_lane(lane, I) + wave * 32 * S : (size_t)(lane & 15) * I + kq;
+  u16x8* tw = slab_t[FL ? wave : 0];
 
   DownTile ts, tn;
   DownRaw rn;
   {
     DownRaw r0;
     down_issue(r0, rg.p0.t, G, pv);
-    down_finish<DG>(ts, r0, H, I, lane, kq);
+    down_finish<DG>(ts, r0, H, I, lane, wlane, kq);
   }
   down_issue(rn, rg.next_tile(rg.p0.t), G, pv);
 
@@ -715,17 +797,17 @@ __global__ __launch_bounds__(256) void ffn_down_sk_kernel(
   for (Pos p = rg.p0;;) {
     down_load(h1, w2 + ts.wrow, I, h_hi + ts.hrow, h_lo + ts.hrow, (size_t)p.kc * KUNIT + KHALF);
     __builtin_amdgcn_sched_barrier(0);
-    down_mma(h0, acc);
+    down_mma(h0, acc, tw, lane);
     const Pos pn = rg.next(p);
     if (pn.t != p.t) {
-      down_finish<DG>(tn, rn, H, I, lane, kq);
+      down_finish<DG>(tn, rn, H, I, lane, wlane, kq);
       down_issue(rn, rg.next_tile(pn.t), G, pv);  // the tile after
     } else {
       tn = ts;
     }
     down_load(h0, w2 + tn.wrow, I, h_hi + tn.hrow, h_lo + tn.hrow, (size_t)pn.kc * KUNIT);
     __builtin_amdgcn_sched_barrier(0);
-    down_mma(h1, acc);
+    down_mma(h1, acc, tw, lane);
     if (rg.ends_tile(p)) tile_end(p.t);
     if (rg.last(p)) break;
     ts = tn;
@@ -870,9 +952,10 @@ __device__ __forceinline__ void pf_finish(PfTile<NT>& st, const PfRaw<NT>& raw, 
   st.ntiles = (raw.tc + 15) >> 4;
   const int kq = (lane >> 4) * 8;
   const int K = UP ? H : I;
-  const int row = UP ? raw.g * PF_UP_COLS + wave * 8 * PF_GROUPS + (lane & 15)
-                     : raw.g * PF_ROWS + wave * 16 * PF_GROUPS + (lane & 15);
-  st.wrow = (UP ? ((size_t)raw.ex * 2 * I + row) : ((size_t)raw.ex * H + row)) * K + kq;
+  const int row = UP ? raw.g * PF_UP_COLS + wave * 8 * PF_GROUPS
+                     : raw.g * PF_ROWS + wave * 16 * PF_GROUPS;
+  st.wrow = (UP ? ((size_t)raw.ex * 2 * I + row) : ((size_t)raw.ex * H + row)) * K +
+            (kFullLines ? slab_lane(lane, K) : (size_t)(lane & 15) * K + kq);
 #pragma unroll
   for (int i = 0; i < PfStage<NT * 16>::PER; ++i) {
     const int n = (tid + PF_THREADS * i) / (PF_K / 8), q = (tid + PF_THREADS * i) % (PF_K / 8);
@@ -892,6 +975,7 @@ __global__ __launch_bounds__(PF_THREADS) void ffn_pf_kernel(
   constexpr int NACC = PF_GROUPS * NT;
   constexpr int NB_ARR = UP ? 1 : 2;  // B arrays: x, or h_hi and h_lo
   __shared__ __attribute__((aligned(16))) pf_row_t bs[2][NB_ARR][NR];
+  __shared__ u16x8 slab_t[kFullLines ? PF_WAVES : 1][kFullLines ? PF_GROUPS * 128 : 1];
   __shared__ int fix_flag;
   const PlanRO pv = plan_ro(plan, pmax);
   const int P = pv.hdr[0];
@@ -932,11 +1016,18 @@ __global__ __launch_bounds__(PF_THREADS) void ffn_pf_kernel(
 
   auto load_a = [&](bf16x8 (&a)[PF_GROUPS][PF_STEPS], const PfTile<NT>& t, int kc) {
     const size_t kb = (size_t)kc * PF_K;
+    if constexpr (kFullLines) {
+      static_assert(PF_STEPS == 2, "a slab is two MFMA steps");
 #pragma unroll
-    for (int q = 0; q < PF_GROUPS; ++q)
+      for (int q = 0; q < PF_GROUPS; ++q)
+        slab_load(a[q], w + t.wrow + pf_group_offset<UP>(q, H, I) + kb, K);
+    } else {
 #pragma unroll
-      for (int st = 0; st < PF_STEPS; ++st)
-        a[q][st] = ld8(w + t.wrow + pf_group_offset<UP>(q, H, I) + kb + 32 * st);
+      for (int q = 0; q < PF_GROUPS; ++q)
+#pragma unroll
+        for (int st = 0; st < PF_STEPS; ++st)
+          a[q][st] = ld8(w + t.wrow + pf_group_offset<UP>(q, H, I) + kb + 32 * st);
+    }
   };
   auto load_b = [&](PfStage<NR> (&st)[NB_ARR], const PfTile<NT>& t, int kc) {
     const size_t kb = (size_t)kc * PF_K;
@@ -1016,6 +1107,10 @@ __global__ __launch_bounds__(PF_THREADS) void ffn_pf_kernel(
     }
     load_b(ns, t2, p2.kc);
     load_a(na, t1, p1.kc);
+    if constexpr (kFullLines) {
+#pragma unroll
+      for (int q = 0; q < PF_GROUPS; ++q) slab_frags(ca[q], slab_t[wave] + q * 128, lane);
+    }
     pf_mma<NT, UP>(ca, bs[cb][0], bs[cb][NB_ARR - 1], lane, acc);
     store_b(cs, cb ^ 1);
     const bool last = sc.last(p);
