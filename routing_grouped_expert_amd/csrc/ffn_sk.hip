@@ -145,31 +145,33 @@ __device__ __forceinline__ bf16x8 ld8(const uint16_t* p) {
 // reads spread over the LDS banks.
 constexpr bool kFullLines = true;
 
-// The lane's offset (elements) in a slab whose rows are ld elements apart.
+// The lane's offset (elements) in a slab whose rows are ld elements apart;
+// E elements make a 16-byte chunk (8 bf16, or 16 FP8 codes, whose slab spans
+// the four MFMA steps of a 128-code line).
+template <int E = 8>
 __device__ __forceinline__ size_t slab_lane(int lane, size_t ld) {
-  return (size_t)(lane >> 3) * ld + (lane & 7) * 8;
+  return (size_t)(lane >> 3) * ld + (lane & 7) * E;
 }
 
-__device__ __forceinline__ bf16x8 ldnt8(const uint16_t* p) {
-  return __builtin_bit_cast(bf16x8, __builtin_nontemporal_load(reinterpret_cast<const u16x8*>(p)));
+// The two full-line loads (nontemporal) of the slab whose row 0, at the
+// slab's K offset plus the lane's slab offset, is at p.
+template <class V, class T>
+__device__ __forceinline__ void slab_load(V (&v)[2], const T* p, size_t ld) {
+  static_assert(sizeof(V) == 16, "16-byte chunks");
+  v[0] = __builtin_bit_cast(V, __builtin_nontemporal_load(reinterpret_cast<const u16x8*>(p)));
+  v[1] = __builtin_bit_cast(V, __builtin_nontemporal_load(reinterpret_cast<const u16x8*>(p + 8 * ld)));
 }
 
-// The two full-line loads of the slab whose row 0 (at the slab's K offset,
-// plus the lane's slab offset) is at p.
-__device__ __forceinline__ void slab_load(bf16x8 (&v)[2], const uint16_t* p, size_t ld) {
-  v[0] = ldnt8(p);
-  v[1] = ldnt8(p + 8 * ld);
-}
-
-// Slab -> the two MFMA fragments, in place, through the wave's tile t
-// (128 u16x8, private to the wave).
-__device__ __forceinline__ void slab_frags(bf16x8 (&v)[2], u16x8* t, int lane) {
+// Slab -> the two MFMA fragments (16 bytes each), in place, through the
+// wave's tile t (128 u16x8, private to the wave).
+template <class V>
+__device__ __forceinline__ void slab_frags(V (&v)[2], u16x8* t, int lane) {
   const int r0 = lane >> 3, c = lane & 7;
   t[r0 * 8 + (c ^ r0)] = __builtin_bit_cast(u16x8, v[0]);
   t[(8 + r0) * 8 + (c ^ r0)] = __builtin_bit_cast(u16x8, v[1]);
   const int r = lane & 15, g = lane >> 4, x = r & 7;
-  v[0] = __builtin_bit_cast(bf16x8, t[r * 8 + (g ^ x)]);
-  v[1] = __builtin_bit_cast(bf16x8, t[r * 8 + ((4 + g) ^ x)]);
+  v[0] = __builtin_bit_cast(V, t[r * 8 + (g ^ x)]);
+  v[1] = __builtin_bit_cast(V, t[r * 8 + ((4 + g) ^ x)]);
 }
 
 // Block containing unit u when U units are cut into NB equal ranges
@@ -439,22 +441,37 @@ struct UpOps8 {
 template <int RG, int S>
 __device__ __forceinline__ void up_load(UpOps8<RG, S>& r, const uint8_t* wg, const uint8_t* wu,
                                         const uint16_t* x, int H, size_t kb) {
+  if constexpr (kFullLines) {
+    static_assert(S == 4, "an FP8 slab is four MFMA steps");
 #pragma unroll
-  for (int q = 0; q < RG; ++q)
+    for (int q = 0; q < RG; ++q) slab_load(r.g[q], wg + (size_t)q * 16 * H + kb, H);
 #pragma unroll
-    for (int p = 0; p < S / 2; ++p)
-      r.g[q][p] = *reinterpret_cast<const u32x4*>(wg + (size_t)q * 16 * H + kb + 64 * p);
+    for (int q = 0; q < RG; ++q) slab_load(r.u[q], wu + (size_t)q * 16 * H + kb, H);
+  } else {
 #pragma unroll
-  for (int q = 0; q < RG; ++q)
+    for (int q = 0; q < RG; ++q)
 #pragma unroll
-    for (int p = 0; p < S / 2; ++p)
-      r.u[q][p] = *reinterpret_cast<const u32x4*>(wu + (size_t)q * 16 * H + kb + 64 * p);
+      for (int p = 0; p < S / 2; ++p)
+        r.g[q][p] = *reinterpret_cast<const u32x4*>(wg + (size_t)q * 16 * H + kb + 64 * p);
+#pragma unroll
+    for (int q = 0; q < RG; ++q)
+#pragma unroll
+      for (int p = 0; p < S / 2; ++p)
+        r.u[q][p] = *reinterpret_cast<const u32x4*>(wu + (size_t)q * 16 * H + kb + 64 * p);
+  }
 #pragma unroll
   for (int st = 0; st < S; ++st) r.x[st] = ld8(x + kb + 64 * (st / 2) + 8 * (st % 2));
 }
 
 template <int RG, int S>
-__device__ __forceinline__ void up_mma(const UpOps8<RG, S>& r, f32x4 (&acc)[2 * RG], u16x8*, int) {
+__device__ __forceinline__ void up_mma(UpOps8<RG, S>& r, f32x4 (&acc)[2 * RG], u16x8* t, int lane) {
+  if constexpr (kFullLines) {
+#pragma unroll
+    for (int q = 0; q < RG; ++q) {
+      slab_frags(r.g[q], t + (2 * q) * 128, lane);
+      slab_frags(r.u[q], t + (2 * q + 1) * 128, lane);
+    }
+  }
 #pragma unroll
   for (int p = 0; p < S / 2; ++p)
 #pragma unroll
@@ -520,7 +537,7 @@ __global__ __launch_bounds__(256) void ffn_up_sk_kernel(
   using Ops = std::conditional_t<F8, UpOps8<RG, S>, UpOps<RG, S>>;
   const WT* w1 = static_cast<const WT*>(w1v);
   __shared__ f32x4 red[2][4][RCH][kWave];
-  constexpr bool FL = kFullLines && !F8;
+  constexpr bool FL = kFullLines;
   __shared__ u16x8 slab_t[FL ? 4 : 1][FL ? 2 * RG * 128 : 1];  // per wave: 2 RG slab tiles
   const PlanRO pv = plan_ro(plan, pmax);
   const int P = pv.hdr[0];
@@ -531,7 +548,8 @@ __global__ __launch_bounds__(256) void ffn_up_sk_kernel(
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int kq = (lane >> 4) * (F8 ? 16 : 8) + wave * 32 * S;
   // lane's offset from a row group's first row in W1
-  const size_t wlane = FL ? slab_lane(lane, H) + wave * 32 * S : (size_t)(lane & 15) * H + kq;
+  const size_t wlane = FL ? slab_lane<F8 ? 16 : 8>(lane, H) + wave * 32 * S
+                          : (size_t)(lane & 15) * H + kq;
   u16x8* tw = slab_t[FL ? wave : 0];
   const size_t I_H = (size_t)I * H;
 
@@ -672,11 +690,17 @@ struct DownOps8 {
 template <int DG, int S>
 __device__ __forceinline__ void down_load(DownOps8<DG, S>& r, const uint8_t* w, int I,
                                           const uint16_t* hh, const uint16_t* hl, size_t kb) {
+  if constexpr (kFullLines) {
+    static_assert(S == 4, "an FP8 slab is four MFMA steps");
 #pragma unroll
-  for (int q = 0; q < DG; ++q)
+    for (int q = 0; q < DG; ++q) slab_load(r.a[q], w + (size_t)q * 16 * I + kb, I);
+  } else {
 #pragma unroll
-    for (int p = 0; p < S / 2; ++p)
-      r.a[q][p] = *reinterpret_cast<const u32x4*>(w + (size_t)q * 16 * I + kb + 64 * p);
+    for (int q = 0; q < DG; ++q)
+#pragma unroll
+      for (int p = 0; p < S / 2; ++p)
+        r.a[q][p] = *reinterpret_cast<const u32x4*>(w + (size_t)q * 16 * I + kb + 64 * p);
+  }
 #pragma unroll
   for (int st = 0; st < S; ++st) {
     r.h[st] = ld8(hh + kb + 64 * (st / 2) + 8 * (st % 2));
@@ -685,7 +709,11 @@ __device__ __forceinline__ void down_load(DownOps8<DG, S>& r, const uint8_t* w, 
 }
 
 template <int DG, int S>
-__device__ __forceinline__ void down_mma(const DownOps8<DG, S>& r, f32x4 (&acc)[DG], u16x8*, int) {
+__device__ __forceinline__ void down_mma(DownOps8<DG, S>& r, f32x4 (&acc)[DG], u16x8* t, int lane) {
+  if constexpr (kFullLines) {
+#pragma unroll
+    for (int q = 0; q < DG; ++q) slab_frags(r.a[q], t + q * 128, lane);
+  }
 #pragma unroll
   for (int p = 0; p < S / 2; ++p)
 #pragma unroll
@@ -739,7 +767,7 @@ __global__ __launch_bounds__(256) void ffn_down_sk_kernel(
   using Ops = std::conditional_t<F8, DownOps8<DG, S>, DownOps<DG, S>>;
   const WT* w2 = static_cast<const WT*>(w2v);
   __shared__ f32x4 red[2][4][RCH][kWave];
-  constexpr bool FL = kFullLines && !F8;
+  constexpr bool FL = kFullLines;
   __shared__ u16x8 slab_t[FL ? 4 : 1][FL ? DG * 128 : 1];  // per wave: DG slab tiles
   const PlanRO pv = plan_ro(plan, pmax);
   const int P = pv.hdr[0];
@@ -750,7 +778,8 @@ __global__ __launch_bounds__(256) void ffn_down_sk_kernel(
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int kq = (lane >> 4) * (F8 ? 16 : 8) + wave * 32 * S;
   // lane's offset from a row group's first row in W2
-  const size_t wlane = FL ? slab_lane(lane, I) + wave * 32 * S : (size_t)(lane & 15) * I + kq;
+  const size_t wlane = FL ? slab_lane<F8 ? 16 : 8>(lane, I) + wave * 32 * S
+                          : (size_t)(lane & 15) * I + kq;
   u16x8* tw = slab_t[FL ? wave : 0];
 
   DownTile ts, tn;
