@@ -38,24 +38,35 @@
 //       writes fp32 expert_out.
 #include "device.h"
 
+#include <algorithm>
 #include <type_traits>
 
 namespace moe {
 
 namespace {
 // Tile shapes, measured on MI355X at the decode shape (T32 H4096 I14336 E8
-// top-2; up kernel / down kernel, microseconds):
+// top-2; up kernel / down kernel, microseconds). With fragment-layout weight
+// loads:
 //   up   1 gate group, 4 blocks per CU 354; 2 groups, 1 block per CU 320;
 //        2 groups, 2 blocks 392; 4 groups, 1 block 354
 //   down 8 groups, 1 block per CU 174; 4 groups 180-184; 16 groups 179;
 //        the 4-group tiles of units of 4 steps, 2 blocks per CU 176
-// A CU holding fewer, taller tiles keeps fewer weight rows open at once, and
-// the token bytes per weight byte shrink with the tile height.
+// With full-line slabs (two boxes):
+//   up   2 groups x 2 steps 296-298; 1 group x 4 steps 269-271 (2 blocks per
+//        CU 277); 1 x 8 270; 1 x 2, 2 blocks 279; 2 x 4 304
+//   down 8 groups x 2 steps 147 / 166; 8 x 4 146 / 170; 4 x 2, 2 blocks 155;
+//        4 x 4 158; 2 x 8 168
+// A CU holding fewer weight rows open at once, each read in longer runs,
+// streams faster; the token bytes per weight byte grow as the tile narrows
+// but come from L2.
 // MFMA K-steps (of 32) per wave per half unit; a unit is two halves, each
-// spanning the 4 waves.
-constexpr int UP_STEPS = 2;
+// spanning the 4 waves. The up projection takes 4 steps when H is a multiple
+// of its 1024-wide unit, else 2.
+constexpr int UP_STEPS = 4;
+constexpr int UP_STEPS_SHORT = 2;
 constexpr int DOWN_STEPS = 2;
 constexpr int UP_KUNIT = 2 * 4 * 32 * UP_STEPS;
+constexpr int UP_KUNIT_SHORT = 2 * 4 * 32 * UP_STEPS_SHORT;
 constexpr int DOWN_KUNIT = 2 * 4 * 32 * DOWN_STEPS;
 // Blocks per CU of the K-split kernels.
 constexpr int UP_CAP = 1;
@@ -68,7 +79,7 @@ constexpr int UP8_KUNIT = 2 * 4 * 32 * UP8_STEPS;
 constexpr int DOWN8_KUNIT = 2 * 4 * 32 * DOWN8_STEPS;
 constexpr int UP8_CAP = 2;
 constexpr int DOWN8_CAP = 1;
-constexpr int UP_RG = 2;          // 16-row gate groups (and as many up groups) per up tile
+constexpr int UP_RG = 1;          // 16-row gate groups (and as many up groups) per up tile
 constexpr int UP_ROWS = 16 * UP_RG;
 constexpr int DOWN_GROUPS = 8;    // 16-row groups per down tile
 constexpr int DOWN_ROWS = 16 * DOWN_GROUPS;
@@ -385,11 +396,17 @@ template <int RG, int S>
 __device__ __forceinline__ void up_load(UpOps<RG, S>& r, const uint16_t* wg, const uint16_t* wu,
                                         const uint16_t* x, int H, size_t kb) {
   if constexpr (kFullLines) {
-    static_assert(S == 2, "a slab is two MFMA steps");
+    static_assert(S % 2 == 0, "a slab is two MFMA steps");
 #pragma unroll
-    for (int q = 0; q < RG; ++q) slab_load(r.g[q], wg + (size_t)q * 16 * H + kb, H);
+    for (int q = 0; q < RG; ++q)
 #pragma unroll
-    for (int q = 0; q < RG; ++q) slab_load(r.u[q], wu + (size_t)q * 16 * H + kb, H);
+      for (int j = 0; j < S / 2; ++j)
+        slab_load(*reinterpret_cast<bf16x8(*)[2]>(&r.g[q][2 * j]), wg + (size_t)q * 16 * H + kb + 64 * j, H);
+#pragma unroll
+    for (int q = 0; q < RG; ++q)
+#pragma unroll
+      for (int j = 0; j < S / 2; ++j)
+        slab_load(*reinterpret_cast<bf16x8(*)[2]>(&r.u[q][2 * j]), wu + (size_t)q * 16 * H + kb + 64 * j, H);
   } else {
 #pragma unroll
     for (int q = 0; q < RG; ++q)
@@ -405,15 +422,17 @@ __device__ __forceinline__ void up_load(UpOps<RG, S>& r, const uint16_t* wg, con
 }
 
 // acc[q]: gate group q, acc[RG + q]: up group q. t: the wave's LDS tiles
-// (2 RG of 128 u16x8) for the full-line slabs.
+// (RG S of 128 u16x8) for the full-line slabs.
 template <int RG, int S>
 __device__ __forceinline__ void up_mma(UpOps<RG, S>& r, f32x4 (&acc)[2 * RG], u16x8* t, int lane) {
   if constexpr (kFullLines) {
 #pragma unroll
-    for (int q = 0; q < RG; ++q) {
-      slab_frags(r.g[q], t + (2 * q) * 128, lane);
-      slab_frags(r.u[q], t + (2 * q + 1) * 128, lane);
-    }
+    for (int q = 0; q < RG; ++q)
+#pragma unroll
+      for (int j = 0; j < S / 2; ++j) {
+        slab_frags(*reinterpret_cast<bf16x8(*)[2]>(&r.g[q][2 * j]), t + ((2 * q) * (S / 2) + j) * 128, lane);
+        slab_frags(*reinterpret_cast<bf16x8(*)[2]>(&r.u[q][2 * j]), t + ((2 * q + 1) * (S / 2) + j) * 128, lane);
+      }
   }
 #pragma unroll
   for (int st = 0; st < S; ++st)
@@ -538,7 +557,8 @@ __global__ __launch_bounds__(256) void ffn_up_sk_kernel(
   const WT* w1 = static_cast<const WT*>(w1v);
   __shared__ f32x4 red[2][4][RCH][kWave];
   constexpr bool FL = kFullLines;
-  __shared__ u16x8 slab_t[FL ? 4 : 1][FL ? 2 * RG * 128 : 1];  // per wave: 2 RG slab tiles
+  constexpr int NSLAB = F8 ? 2 * RG : RG * S;  // slab tiles per wave
+  __shared__ u16x8 slab_t[FL ? 4 : 1][FL ? NSLAB * 128 : 1];
   const PlanRO pv = plan_ro(plan, pmax);
   const int P = pv.hdr[0];
   const int G = I / (16 * RG), C = H / KUNIT;
@@ -647,9 +667,12 @@ template <int DG, int S>
 __device__ __forceinline__ void down_load(DownOps<DG, S>& r, const uint16_t* w, int I,
                                           const uint16_t* hh, const uint16_t* hl, size_t kb) {
   if constexpr (kFullLines) {
-    static_assert(S == 2, "a slab is two MFMA steps");
+    static_assert(S % 2 == 0, "a slab is two MFMA steps");
 #pragma unroll
-    for (int q = 0; q < DG; ++q) slab_load(r.a[q], w + (size_t)q * 16 * I + kb, I);
+    for (int q = 0; q < DG; ++q)
+#pragma unroll
+      for (int j = 0; j < S / 2; ++j)
+        slab_load(*reinterpret_cast<bf16x8(*)[2]>(&r.a[q][2 * j]), w + (size_t)q * 16 * I + kb + 64 * j, I);
   } else {
 #pragma unroll
     for (int q = 0; q < DG; ++q)
@@ -663,12 +686,15 @@ __device__ __forceinline__ void down_load(DownOps<DG, S>& r, const uint16_t* w, 
   }
 }
 
-// t: the wave's LDS tiles (DG of 128 u16x8) for the full-line slabs.
+// t: the wave's LDS tiles (DG S / 2 of 128 u16x8) for the full-line slabs.
 template <int DG, int S>
 __device__ __forceinline__ void down_mma(DownOps<DG, S>& r, f32x4 (&acc)[DG], u16x8* t, int lane) {
   if constexpr (kFullLines) {
 #pragma unroll
-    for (int q = 0; q < DG; ++q) slab_frags(r.a[q], t + q * 128, lane);
+    for (int q = 0; q < DG; ++q)
+#pragma unroll
+      for (int j = 0; j < S / 2; ++j)
+        slab_frags(*reinterpret_cast<bf16x8(*)[2]>(&r.a[q][2 * j]), t + (q * (S / 2) + j) * 128, lane);
   }
 #pragma unroll
   for (int st = 0; st < S; ++st)
@@ -768,7 +794,8 @@ __global__ __launch_bounds__(256) void ffn_down_sk_kernel(
   const WT* w2 = static_cast<const WT*>(w2v);
   __shared__ f32x4 red[2][4][RCH][kWave];
   constexpr bool FL = kFullLines;
-  __shared__ u16x8 slab_t[FL ? 4 : 1][FL ? DG * 128 : 1];  // per wave: DG slab tiles
+  constexpr int NSLAB = F8 ? DG : DG * S / 2;  // slab tiles per wave
+  __shared__ u16x8 slab_t[FL ? 4 : 1][FL ? NSLAB * 128 : 1];
   const PlanRO pv = plan_ro(plan, pmax);
   const int P = pv.hdr[0];
   const int G = H / (16 * DG), C = I / KUNIT;
@@ -1209,7 +1236,8 @@ template <int NT>
 int up_blocks(bool f8) {
   if constexpr (NT == 1)
     return f8 ? resident_blocks<ffn_up_sk_kernel<UP_RG, UP8_STEPS, true>>(256, UP8_CAP)
-              : resident_blocks<ffn_up_sk_kernel<UP_RG, UP_STEPS, false>>(256, UP_CAP);
+              : std::min(resident_blocks<ffn_up_sk_kernel<UP_RG, UP_STEPS, false>>(256, UP_CAP),
+                         resident_blocks<ffn_up_sk_kernel<UP_RG, UP_STEPS_SHORT, false>>(256, UP_CAP));
   else return resident_blocks<ffn_pf_kernel<NT, true>>(PF_THREADS);
 }
 template <int NT>
@@ -1277,10 +1305,14 @@ hipError_t launch_sk_nt(const uint16_t* x, const int* perm, const int* offsets, 
       hipLaunchKernelGGL((ffn_up_sk_kernel<UP_RG, UP8_STEPS, true>), dim3(lo.nb_up), dim3(256), 0,
                          stream, x, perm, k, H, I, nmax, w1, s1, plan, lo.pmax, slots, counters,
                          h_hi, h_lo, lo.nb_up);
-    else
+    else if (H % UP_KUNIT == 0)
       hipLaunchKernelGGL((ffn_up_sk_kernel<UP_RG, UP_STEPS, false>), dim3(lo.nb_up), dim3(256), 0,
                          stream, x, perm, k, H, I, nmax, w1, s1, plan, lo.pmax, slots, counters,
                          h_hi, h_lo, lo.nb_up);
+    else
+      hipLaunchKernelGGL((ffn_up_sk_kernel<UP_RG, UP_STEPS_SHORT, false>), dim3(lo.nb_up),
+                         dim3(256), 0, stream, x, perm, k, H, I, nmax, w1, s1, plan, lo.pmax,
+                         slots, counters, h_hi, h_lo, lo.nb_up);
   } else {
     hipLaunchKernelGGL((ffn_pf_kernel<NT, true>), dim3(lo.nb_up), dim3(PF_THREADS), 0, stream, x, x,
                        perm, k, H, I, nmax, static_cast<const uint16_t*>(w1), plan, lo.pmax, slots,
@@ -1311,7 +1343,8 @@ bool ffn_sk_applies(const void* x, const void* w1, const void* w2, int T, int k,
   auto al = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
   if (!(al(x) && al(w1) && al(w2))) return false;
   if (pick_nt(T, k, L) == 1)
-    return H % UP_KUNIT == 0 && I % DOWN_KUNIT == 0 && I % UP_ROWS == 0 && H % DOWN_ROWS == 0;
+    return H % UP_KUNIT_SHORT == 0 && I % DOWN_KUNIT == 0 && I % UP_ROWS == 0 &&
+           H % DOWN_ROWS == 0;
   // the staged kernels address token rows with 32-bit byte offsets below 2^31
   const size_t lim = (size_t)1 << 31;
   return H % PF_K == 0 && I % PF_K == 0 && H % PF_ROWS == 0 && I % PF_UP_COLS == 0 &&
