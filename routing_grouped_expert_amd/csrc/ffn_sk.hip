@@ -1021,8 +1021,12 @@ __device__ __forceinline__ void pf_finish(PfTile<NT>& st, const PfRaw<NT>& raw, 
   }
 }
 
+// With 4 token tiles, at most 128 VGPRs, so that two blocks share a CU: the
+// down projection then took 1477 us against 1617 us with one block per CU
+// (fine-grained shape; a few addresses spill to scratch); the up projection
+// fits 128 anyway.
 template <int NT, bool UP>
-__global__ __launch_bounds__(PF_THREADS) void ffn_pf_kernel(
+__global__ __launch_bounds__(PF_THREADS, NT <= 4 ? 4 : 1) void ffn_pf_kernel(
     const uint16_t* __restrict__ b0src, const uint16_t* __restrict__ b1src,
     const int* __restrict__ perm, int k, int H, int I, int nmax, const uint16_t* __restrict__ w,
     const int* __restrict__ plan, int pmax, f32x4* slots, int* counters,
