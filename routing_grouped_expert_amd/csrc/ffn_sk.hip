@@ -1143,16 +1143,21 @@ __global__ __launch_bounds__(PF_THREADS, NT <= 4 ? 4 : 1) void ffn_pf_kernel(
 
   // prologue: chunk p0's token rows in LDS buffer 0 and its weights in
   // registers; chunk p1's token rows in flight
-  bf16x8 a0[PF_GROUPS][PF_STEPS], a1[PF_GROUPS][PF_STEPS];
+  // A3: the up projection with 8 token tiles (238 VGPRs) fetches its weights
+  // two units ahead, through three register sets (share 0: 882 us against
+  // 911 us one unit ahead); the others stay at one unit ahead.
+  constexpr bool A3 = UP && NT >= 8;
+  bf16x8 a0[PF_GROUPS][PF_STEPS], a1[PF_GROUPS][PF_STEPS], a2[A3 ? PF_GROUPS : 1][PF_STEPS];
   PfStage<NR> sb0[NB_ARR], sb1[NB_ARR];
   load_b(sb1, t0, p0.kc);
   load_a(a0, t0, p0.kc);
+  if constexpr (A3) load_a(a1, t1, p1.kc);
   store_b(sb1, 0);
   load_b(sb0, t1, p1.kc);
   __syncthreads();
 
-  // One unit: issue chunk p2's token rows and chunk p1's weights, multiply
-  // chunk p (weights `ca`, token rows in LDS buffer `cb`), write chunk p1's
+  // One unit: issue chunk p2's token rows and chunk p1's (A3: p2's) weights,
+  // multiply chunk p (weights `ca`, token rows in LDS buffer `cb`), write chunk p1's
   // token rows (`cs`, loaded a step earlier) into the other buffer, finish the
   // tile if p ends it here, and synchronise the block. Returns false after
   // the block's last unit.
@@ -1166,7 +1171,8 @@ __global__ __launch_bounds__(PF_THREADS, NT <= 4 ? 4 : 1) void ffn_pf_kernel(
       t2 = t1;
     }
     load_b(ns, t2, p2.kc);
-    load_a(na, t1, p1.kc);
+    if constexpr (A3) load_a(na, t2, p2.kc);
+    else load_a(na, t1, p1.kc);
     if constexpr (kFullLines) {
 #pragma unroll
       for (int q = 0; q < PF_GROUPS; ++q) slab_frags(ca[q], slab_t[wave] + q * 128, lane);
@@ -1185,7 +1191,14 @@ __global__ __launch_bounds__(PF_THREADS, NT <= 4 ? 4 : 1) void ffn_pf_kernel(
   };
 
   Pos p = p0;
-  while (step(a0, a1, sb0, sb1, 0, p) && step(a1, a0, sb1, sb0, 1, p)) {
+  if constexpr (A3) {
+    while (step(a0, a2, sb0, sb1, 0, p) && step(a1, a0, sb1, sb0, 1, p) &&
+           step(a2, a1, sb0, sb1, 0, p) && step(a0, a2, sb1, sb0, 1, p) &&
+           step(a1, a0, sb0, sb1, 0, p) && step(a2, a1, sb1, sb0, 1, p)) {
+    }
+  } else {
+    while (step(a0, a1, sb0, sb1, 0, p) && step(a1, a0, sb1, sb0, 1, p)) {
+    }
   }
 }
 
