@@ -936,25 +936,46 @@ __device__ __forceinline__ void pf_stage_store(const PfStage<NR>& st, pf_row_t* 
   }
 }
 
+// A lane's weight operands of one chunk: bf16, a full-line slab per group
+// (two MFMA fragments once through the LDS tile); FP8, 16 codes per group in
+// fragment layout (lane l: row l % 16, codes 16 (l / 16) .. + 15 of the
+// 64-wide chunk; codes + 0..7 feed the first MFMA step, + 8..15 the second,
+// and the token fragments are read in that K order).
+template <bool F8>
+struct PfA {
+  bf16x8 v[PF_GROUPS][PF_STEPS];
+};
+template <>
+struct PfA<true> {
+  u32x4 v[PF_GROUPS];
+};
+
 // acc[q * NT + nt] += A(group q) * B(token tile nt) over one chunk; the down
 // projection multiplies both halves (hi, lo) of the intermediate.
-template <int NT, bool UP>
-__device__ __forceinline__ void pf_mma(const bf16x8 (&a)[PF_GROUPS][PF_STEPS], const pf_row_t* b0,
-                                       const pf_row_t* b1, int lane, f32x4* acc) {
+template <int NT, bool UP, bool F8>
+__device__ __forceinline__ void pf_mma(const PfA<F8>& a, const pf_row_t* b0, const pf_row_t* b1,
+                                       int lane, f32x4* acc) {
 #pragma unroll
   for (int st = 0; st < PF_STEPS; ++st) {
+    bf16x8 w[PF_GROUPS];
+#pragma unroll
+    for (int q = 0; q < PF_GROUPS; ++q) {
+      if constexpr (F8) w[q] = e4m3x8_to_bf16(a.v[q][2 * st], a.v[q][2 * st + 1]);
+      else w[q] = a.v[q][st];
+    }
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      const int n = nt * 16 + (lane & 15), c = st * 32 + (lane >> 4) * 8;
+      const int n = nt * 16 + (lane & 15);
+      const int c = F8 ? (lane >> 4) * 16 + st * 8 : st * 32 + (lane >> 4) * 8;
       const bf16x8 h = *reinterpret_cast<const bf16x8*>(&b0[n][c]);
 #pragma unroll
       for (int q = 0; q < PF_GROUPS; ++q)
-        acc[q * NT + nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[q][st], h, acc[q * NT + nt], 0, 0, 0);
+        acc[q * NT + nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w[q], h, acc[q * NT + nt], 0, 0, 0);
       if (!UP) {
         const bf16x8 l = *reinterpret_cast<const bf16x8*>(&b1[n][c]);
 #pragma unroll
         for (int q = 0; q < PF_GROUPS; ++q)
-          acc[q * NT + nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[q][st], l, acc[q * NT + nt], 0, 0, 0);
+          acc[q * NT + nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w[q], l, acc[q * NT + nt], 0, 0, 0);
       }
     }
   }
@@ -985,7 +1006,7 @@ __device__ __forceinline__ void pf_issue(PfRaw<NT>& raw, int tile, int G, const 
 
 template <int NT>
 struct PfTile {
-  int g, tb, tc, ntiles;
+  int g, ex, tb, tc, ntiles;
   size_t wrow;                               // this lane's first weight row (+ K offset)
   uint32_t voff[PfStage<NT * 16>::PER];      // staged B rows (+ this thread's column), bytes
 };
@@ -999,10 +1020,11 @@ __device__ __forceinline__ size_t pf_group_offset(int q, int H, int I) {
   return UP ? (size_t)((q % HALF) * 16 + (q / HALF) * I) * H : (size_t)q * 16 * I;
 }
 
-template <int NT, bool UP>
+template <int NT, bool UP, bool F8>
 __device__ __forceinline__ void pf_finish(PfTile<NT>& st, const PfRaw<NT>& raw, int k, int H,
                                           int I, int nmax, int wave, int lane, int tid) {
   st.g = raw.g;
+  st.ex = raw.ex;
   st.tb = raw.tb;
   st.tc = raw.tc;
   st.ntiles = (raw.tc + 15) >> 4;
@@ -1011,7 +1033,8 @@ __device__ __forceinline__ void pf_finish(PfTile<NT>& st, const PfRaw<NT>& raw, 
   const int row = UP ? raw.g * PF_UP_COLS + wave * 8 * PF_GROUPS
                      : raw.g * PF_ROWS + wave * 16 * PF_GROUPS;
   st.wrow = (UP ? ((size_t)raw.ex * 2 * I + row) : ((size_t)raw.ex * H + row)) * K +
-            (kFullLines ? slab_lane(lane, K) : (size_t)(lane & 15) * K + kq);
+            (F8 ? (size_t)(lane & 15) * K + (lane >> 4) * 16
+                : (kFullLines ? slab_lane(lane, K) : (size_t)(lane & 15) * K + kq));
 #pragma unroll
   for (int i = 0; i < PfStage<NT * 16>::PER; ++i) {
     const int n = (tid + PF_THREADS * i) / (PF_K / 8), q = (tid + PF_THREADS * i) % (PF_K / 8);
@@ -1025,17 +1048,23 @@ __device__ __forceinline__ void pf_finish(PfTile<NT>& st, const PfRaw<NT>& raw, 
 // down projection then took 1477 us against 1617 us with one block per CU
 // (fine-grained shape; a few addresses spill to scratch); the up projection
 // fits 128 anyway.
-template <int NT, bool UP>
+// F8: FP8 E4M3 weight codes with one fp32 scale per row (wscale), applied to
+// the finished sums.
+template <int NT, bool UP, bool F8>
 __global__ __launch_bounds__(PF_THREADS, NT <= 4 ? 4 : 1) void ffn_pf_kernel(
     const uint16_t* __restrict__ b0src, const uint16_t* __restrict__ b1src,
-    const int* __restrict__ perm, int k, int H, int I, int nmax, const uint16_t* __restrict__ w,
-    const int* __restrict__ plan, int pmax, f32x4* slots, int* counters,
-    uint16_t* __restrict__ h_hi, uint16_t* __restrict__ h_lo, float* __restrict__ out, int NB) {
+    const int* __restrict__ perm, int k, int H, int I, int nmax, const void* __restrict__ wv,
+    const float* __restrict__ wscale, const int* __restrict__ plan, int pmax, f32x4* slots,
+    int* counters, uint16_t* __restrict__ h_hi, uint16_t* __restrict__ h_lo,
+    float* __restrict__ out, int NB) {
+  using WT = std::conditional_t<F8, uint8_t, uint16_t>;
+  const WT* w = static_cast<const WT*>(wv);
+  constexpr bool FL = kFullLines && !F8;  // bf16 slabs through the wave's LDS tile
   constexpr int NR = NT * 16;
   constexpr int NACC = PF_GROUPS * NT;
   constexpr int NB_ARR = UP ? 1 : 2;  // B arrays: x, or h_hi and h_lo
   __shared__ __attribute__((aligned(16))) pf_row_t bs[2][NB_ARR][NR];
-  __shared__ u16x8 slab_t[kFullLines ? PF_WAVES : 1][kFullLines ? PF_GROUPS * 128 : 1];
+  __shared__ u16x8 slab_t[FL ? PF_WAVES : 1][FL ? PF_GROUPS * 128 : 1];
   __shared__ int fix_flag;
   const PlanRO pv = plan_ro(plan, pmax);
   const int P = pv.hdr[0];
@@ -1060,10 +1089,10 @@ __global__ __launch_bounds__(PF_THREADS, NT <= 4 ? 4 : 1) void ffn_pf_kernel(
   {
     PfRaw<NT> r0;
     pf_issue<NT, UP>(r0, p0.t, G, pv, perm, tid);
-    pf_finish<NT, UP>(t0, r0, k, H, I, nmax, wave, lane, tid);
+    pf_finish<NT, UP, F8>(t0, r0, k, H, I, nmax, wave, lane, tid);
     if (p1.t != p0.t) {
       pf_issue<NT, UP>(r0, p1.t, G, pv, perm, tid);
-      pf_finish<NT, UP>(t1, r0, k, H, I, nmax, wave, lane, tid);
+      pf_finish<NT, UP, F8>(t1, r0, k, H, I, nmax, wave, lane, tid);
     } else {
       t1 = t0;
     }
@@ -1074,19 +1103,23 @@ __global__ __launch_bounds__(PF_THREADS, NT <= 4 ? 4 : 1) void ffn_pf_kernel(
 #pragma unroll
   for (int i = 0; i < NACC; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto load_a = [&](bf16x8 (&a)[PF_GROUPS][PF_STEPS], const PfTile<NT>& t, int kc) {
+  auto load_a = [&](PfA<F8>& a, const PfTile<NT>& t, int kc) {
     const size_t kb = (size_t)kc * PF_K;
-    if constexpr (kFullLines) {
+    if constexpr (F8) {
+#pragma unroll
+      for (int q = 0; q < PF_GROUPS; ++q)
+        a.v[q] = *reinterpret_cast<const u32x4*>(w + t.wrow + pf_group_offset<UP>(q, H, I) + kb);
+    } else if constexpr (kFullLines) {
       static_assert(PF_STEPS == 2, "a slab is two MFMA steps");
 #pragma unroll
       for (int q = 0; q < PF_GROUPS; ++q)
-        slab_load(a[q], w + t.wrow + pf_group_offset<UP>(q, H, I) + kb, K);
+        slab_load(a.v[q], w + t.wrow + pf_group_offset<UP>(q, H, I) + kb, K);
     } else {
 #pragma unroll
       for (int q = 0; q < PF_GROUPS; ++q)
 #pragma unroll
         for (int st = 0; st < PF_STEPS; ++st)
-          a[q][st] = ld8(w + t.wrow + pf_group_offset<UP>(q, H, I) + kb + 32 * st);
+          a.v[q][st] = ld8(w + t.wrow + pf_group_offset<UP>(q, H, I) + kb + 32 * st);
     }
   };
   auto load_b = [&](PfStage<NR> (&st)[NB_ARR], const PfTile<NT>& t, int kc) {
@@ -1118,7 +1151,13 @@ __global__ __launch_bounds__(PF_THREADS, NT <= 4 ? 4 : 1) void ffn_pf_kernel(
             u16x4 hi, lo;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-              const float gg = acc[q * NT + nt][j], uu = acc[(q + PF_GROUPS / 2) * NT + nt][j];
+              float gg = acc[q * NT + nt][j], uu = acc[(q + PF_GROUPS / 2) * NT + nt][j];
+              if constexpr (F8) {
+                const size_t row = (size_t)t0.ex * 2 * I + t0.g * PF_UP_COLS +
+                                   wave * 8 * PF_GROUPS + q * 16 + (lane >> 4) * 4 + j;
+                gg *= wscale[row];
+                uu *= wscale[row + I];
+              }
               const float a = gg / (1.0f + expf(-gg)) * uu;
               hi[j] = f32_to_bf16_bits(a);
               lo[j] = f32_to_bf16_bits(a - bf16_bits_to_f32(hi[j]));
@@ -1132,7 +1171,12 @@ __global__ __launch_bounds__(PF_THREADS, NT <= 4 ? 4 : 1) void ffn_pf_kernel(
 #pragma unroll
           for (int q = 0; q < PF_GROUPS; ++q) {
             const int row = t0.g * PF_ROWS + wave * 16 * PF_GROUPS + q * 16 + (lane >> 4) * 4;
-            *reinterpret_cast<f32x4*>(out + (size_t)(t0.tb + n) * H + row) = acc[q * NT + nt];
+            f32x4 v = acc[q * NT + nt];
+            if constexpr (F8) {
+#pragma unroll
+              for (int j = 0; j < 4; ++j) v[j] *= wscale[(size_t)t0.ex * H + row + j];
+            }
+            *reinterpret_cast<f32x4*>(out + (size_t)(t0.tb + n) * H + row) = v;
           }
         }
       }
@@ -1147,7 +1191,7 @@ __global__ __launch_bounds__(PF_THREADS, NT <= 4 ? 4 : 1) void ffn_pf_kernel(
   // two units ahead, through three register sets (share 0: 882 us against
   // 911 us one unit ahead); the others stay at one unit ahead.
   constexpr bool A3 = UP && NT >= 8;
-  bf16x8 a0[PF_GROUPS][PF_STEPS], a1[PF_GROUPS][PF_STEPS], a2[A3 ? PF_GROUPS : 1][PF_STEPS];
+  PfA<F8> a0, a1, a2;  // a2: A3 only
   PfStage<NR> sb0[NB_ARR], sb1[NB_ARR];
   load_b(sb1, t0, p0.kc);
   load_a(a0, t0, p0.kc);
@@ -1161,11 +1205,11 @@ __global__ __launch_bounds__(PF_THREADS, NT <= 4 ? 4 : 1) void ffn_pf_kernel(
   // token rows (`cs`, loaded a step earlier) into the other buffer, finish the
   // tile if p ends it here, and synchronise the block. Returns false after
   // the block's last unit.
-  auto step = [&](bf16x8 (&ca)[PF_GROUPS][PF_STEPS], bf16x8 (&na)[PF_GROUPS][PF_STEPS],
-                  PfStage<NR> (&cs)[NB_ARR], PfStage<NR> (&ns)[NB_ARR], int cb, Pos& p) -> bool {
+  auto step = [&](PfA<F8>& ca, PfA<F8>& na, PfStage<NR> (&cs)[NB_ARR],
+                  PfStage<NR> (&ns)[NB_ARR], int cb, Pos& p) -> bool {
     const Pos p2 = sc.next(p1);
     if (p2.t != p1.t) {
-      pf_finish<NT, UP>(t2, rn, k, H, I, nmax, wave, lane, tid);
+      pf_finish<NT, UP, F8>(t2, rn, k, H, I, nmax, wave, lane, tid);
       pf_issue<NT, UP>(rn, sc.next_tile(p2.t), G, pv, perm, tid);
     } else {
       t2 = t1;
@@ -1173,11 +1217,11 @@ __global__ __launch_bounds__(PF_THREADS, NT <= 4 ? 4 : 1) void ffn_pf_kernel(
     load_b(ns, t2, p2.kc);
     if constexpr (A3) load_a(na, t2, p2.kc);
     else load_a(na, t1, p1.kc);
-    if constexpr (kFullLines) {
+    if constexpr (FL) {
 #pragma unroll
-      for (int q = 0; q < PF_GROUPS; ++q) slab_frags(ca[q], slab_t[wave] + q * 128, lane);
+      for (int q = 0; q < PF_GROUPS; ++q) slab_frags(ca.v[q], slab_t[wave] + q * 128, lane);
     }
-    pf_mma<NT, UP>(ca, bs[cb][0], bs[cb][NB_ARR - 1], lane, acc);
+    pf_mma<NT, UP, F8>(ca, bs[cb][0], bs[cb][NB_ARR - 1], lane, acc);
     store_b(cs, cb ^ 1);
     const bool last = sc.last(p);
     if (sc.ends_tile(p)) tile_end(p);
@@ -1255,21 +1299,25 @@ int up_blocks(bool f8) {
     return f8 ? resident_blocks<ffn_up_sk_kernel<UP_RG, UP8_STEPS, true>>(256, UP8_CAP)
               : std::min(resident_blocks<ffn_up_sk_kernel<UP_RG, UP_STEPS, false>>(256, UP_CAP),
                          resident_blocks<ffn_up_sk_kernel<UP_RG, UP_STEPS_SHORT, false>>(256, UP_CAP));
-  else return resident_blocks<ffn_pf_kernel<NT, true>>(PF_THREADS);
+  else
+    return f8 ? resident_blocks<ffn_pf_kernel<NT, true, true>>(PF_THREADS)
+              : resident_blocks<ffn_pf_kernel<NT, true, false>>(PF_THREADS);
 }
 template <int NT>
 int down_blocks(bool f8) {
   if constexpr (NT == 1)
     return f8 ? resident_blocks<ffn_down_sk_kernel<DOWN_GROUPS, DOWN8_STEPS, true>>(256, DOWN8_CAP)
               : resident_blocks<ffn_down_sk_kernel<DOWN_GROUPS, DOWN_STEPS, false>>(256, DOWN_CAP);
-  else return resident_blocks<ffn_pf_kernel<NT, false>>(PF_THREADS);
+  else
+    return f8 ? resident_blocks<ffn_pf_kernel<NT, false, true>>(PF_THREADS)
+              : resident_blocks<ffn_pf_kernel<NT, false, false>>(PF_THREADS);
 }
 
 int blocks_for(int NT, bool up, bool f8) {
   switch (NT) {
     case 1: return up ? up_blocks<1>(f8) : down_blocks<1>(f8);
-    case 4: return up ? up_blocks<4>(false) : down_blocks<4>(false);
-    default: return up ? up_blocks<8>(false) : down_blocks<8>(false);
+    case 4: return up ? up_blocks<4>(f8) : down_blocks<4>(f8);
+    default: return up ? up_blocks<8>(f8) : down_blocks<8>(f8);
   }
 }
 
@@ -1305,7 +1353,7 @@ hipError_t launch_sk_nt(const uint16_t* x, const int* perm, const int* offsets, 
                         int k, int H, int I, const void* w1, const void* w2, const float* s1,
                         const float* s2, uint16_t* h_hi, uint16_t* h_lo, float* out, char* ws,
                         hipStream_t stream) {
-  // s1 / s2 non-null: FP8 weights with row scales (K-split kernels only)
+  // s1 / s2 non-null: FP8 weight codes with row scales
   const bool f8 = s1 != nullptr;
   const SkLayout lo = sk_layout(T, k, L, NT, f8);
   int* plan = reinterpret_cast<int*>(ws + lo.plan);
@@ -1331,9 +1379,14 @@ hipError_t launch_sk_nt(const uint16_t* x, const int* perm, const int* offsets, 
                          dim3(256), 0, stream, x, perm, k, H, I, nmax, w1, s1, plan, lo.pmax,
                          slots, counters, h_hi, h_lo, lo.nb_up);
   } else {
-    hipLaunchKernelGGL((ffn_pf_kernel<NT, true>), dim3(lo.nb_up), dim3(PF_THREADS), 0, stream, x, x,
-                       perm, k, H, I, nmax, static_cast<const uint16_t*>(w1), plan, lo.pmax, slots,
-                       counters, h_hi, h_lo, out, lo.nb_up);
+    if (f8)
+      hipLaunchKernelGGL((ffn_pf_kernel<NT, true, true>), dim3(lo.nb_up), dim3(PF_THREADS), 0,
+                         stream, x, x, perm, k, H, I, nmax, w1, s1, plan, lo.pmax, slots,
+                         counters, h_hi, h_lo, out, lo.nb_up);
+    else
+      hipLaunchKernelGGL((ffn_pf_kernel<NT, true, false>), dim3(lo.nb_up), dim3(PF_THREADS), 0,
+                         stream, x, x, perm, k, H, I, nmax, w1, s1, plan, lo.pmax, slots,
+                         counters, h_hi, h_lo, out, lo.nb_up);
   }
   err = hipGetLastError();
   if (err != hipSuccess) return err;
@@ -1347,9 +1400,14 @@ hipError_t launch_sk_nt(const uint16_t* x, const int* perm, const int* offsets, 
                          dim3(256), 0, stream, h_hi, h_lo, H, I, w2, s2, plan, lo.pmax, slots,
                          counters + lo.subs * nbm, out, lo.nb_down);
   } else {
-    hipLaunchKernelGGL((ffn_pf_kernel<NT, false>), dim3(lo.nb_down), dim3(PF_THREADS), 0, stream, h_hi,
-                       h_lo, perm, k, H, I, nmax, static_cast<const uint16_t*>(w2), plan, lo.pmax,
-                       slots, counters + lo.subs * nbm, h_hi, h_lo, out, lo.nb_down);
+    if (f8)
+      hipLaunchKernelGGL((ffn_pf_kernel<NT, false, true>), dim3(lo.nb_down), dim3(PF_THREADS), 0,
+                         stream, h_hi, h_lo, perm, k, H, I, nmax, w2, s2, plan, lo.pmax, slots,
+                         counters + lo.subs * nbm, h_hi, h_lo, out, lo.nb_down);
+    else
+      hipLaunchKernelGGL((ffn_pf_kernel<NT, false, false>), dim3(lo.nb_down), dim3(PF_THREADS), 0,
+                         stream, h_hi, h_lo, perm, k, H, I, nmax, w2, s2, plan, lo.pmax, slots,
+                         counters + lo.subs * nbm, h_hi, h_lo, out, lo.nb_down);
   }
   return hipGetLastError();
 }
@@ -1371,7 +1429,6 @@ bool ffn_sk_applies(const void* x, const void* w1, const void* w2, int T, int k,
 size_t ffn_sk_workspace_bytes(int T, int k, int L) {
   const int nt = pick_nt(T, k, L);
   const size_t a = sk_layout(T, k, L, nt, false).total;
-  if (nt != 1) return a;
   const size_t b = sk_layout(T, k, L, nt, true).total;  // the FP8 kernels' share of it
   return a > b ? a : b;
 }
@@ -1388,13 +1445,19 @@ hipError_t launch_grouped_ffn_sk(const uint16_t* x, const int* perm, const int* 
   }
 }
 
-// FP8 weights (codes + row scales) on the K-split kernels: shapes for which
-// ffn_sk_fp8_applies holds.
+// FP8 weights (codes + row scales) on the persistent kernels (K-split or
+// staged, by the entries per expert): shapes for which ffn_sk_fp8_applies
+// holds.
 bool ffn_sk_fp8_applies(const void* x, const void* w1q, const void* w2q, int T, int k, int L,
                         int H, int I) {
   auto al = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
-  return al(x) && al(w1q) && al(w2q) && pick_nt(T, k, L) == 1 && H % UP8_KUNIT == 0 &&
-         I % DOWN8_KUNIT == 0 && I % UP_ROWS == 0 && H % DOWN_ROWS == 0;
+  if (!(al(x) && al(w1q) && al(w2q))) return false;
+  if (pick_nt(T, k, L) == 1)
+    return H % UP8_KUNIT == 0 && I % DOWN8_KUNIT == 0 && I % UP_ROWS == 0 && H % DOWN_ROWS == 0;
+  // the staged kernels address token rows with 32-bit byte offsets below 2^31
+  const size_t lim = (size_t)1 << 31;
+  return H % PF_K == 0 && I % PF_K == 0 && H % PF_ROWS == 0 && I % PF_UP_COLS == 0 &&
+         (size_t)T * H * 2 < lim && (size_t)T * k * I * 2 < lim;
 }
 
 hipError_t launch_grouped_ffn_sk_fp8(const uint16_t* x, const int* perm, const int* offsets,
@@ -1402,8 +1465,12 @@ hipError_t launch_grouped_ffn_sk_fp8(const uint16_t* x, const int* perm, const i
                                      const float* w1s, const uint8_t* w2q, const float* w2s,
                                      uint16_t* h_hi, uint16_t* h_lo, float* out, void* ws,
                                      hipStream_t stream) {
-  return launch_sk_nt<1>(x, perm, offsets, L, T, k, H, I, w1q, w2q, w1s, w2s, h_hi, h_lo, out,
-                         static_cast<char*>(ws), stream);
+  char* w = static_cast<char*>(ws);
+  switch (pick_nt(T, k, L)) {
+    case 1: return launch_sk_nt<1>(x, perm, offsets, L, T, k, H, I, w1q, w2q, w1s, w2s, h_hi, h_lo, out, w, stream);
+    case 4: return launch_sk_nt<4>(x, perm, offsets, L, T, k, H, I, w1q, w2q, w1s, w2s, h_hi, h_lo, out, w, stream);
+    default: return launch_sk_nt<8>(x, perm, offsets, L, T, k, H, I, w1q, w2q, w1s, w2s, h_hi, h_lo, out, w, stream);
+  }
 }
 
 }  // namespace moe

@@ -55,7 +55,8 @@ def check_ffn_fp8(T, H, I, E, k, first, L, seed=1, ids=None):
     assert np.isnan(got[n:]).all()
 
 
-# generic kernels: one to eight 16-token tiles, a second pass
+# one to eight 16-token tiles, a second pass: the generic kernels for the
+# first two (H below the K-split unit), the staged kernels for the others
 @pytest.mark.parametrize("T,E,k", [(12, 4, 2), (30, 8, 2), (60, 6, 2), (300, 2, 1)])
 def test_ffn_fp8_tiles(T, E, k):
     check_ffn_fp8(T, 256, 384, E, k, 0, E)
@@ -104,5 +105,49 @@ def test_ffn_fp8_decode_full_size_sampled():
     for p in (0, n // 3, (2 * n) // 3, n - 1):
         e = int(np.searchsorted(offsets, p, side="right") - 1)
         ref = oracle.expert_row_fp8(d["x"][perm[p] // k], w1q[e], w1s[e], w2q[e], w2s[e])
+        err = np.abs(got[p].astype(np.float64) - ref)
+        assert err.max() <= 1e-4 * np.abs(ref).max(), (p, err.max() / np.abs(ref).max())
+
+
+# Staged (prefill) kernels on FP8 codes: 4 token tiles per pass (128, 512,
+# 512, 16, 4), 8 tiles dealt in whole rounds (4096 tokens, 512 experts), a
+# whole round then cut tiles (3200 tokens, 300 experts), skewed experts with
+# several passes, a share with empty experts.
+def test_ffn_fp8_prefill_four_tiles():
+    check_ffn_fp8(128, 512, 512, 16, 4, 0, 16)
+
+
+def test_ffn_fp8_prefill_whole_rounds():
+    check_ffn_fp8(4096, 512, 256, 512, 8, 0, 512)
+
+
+def test_ffn_fp8_prefill_rounds_then_cuts():
+    check_ffn_fp8(3200, 512, 256, 300, 8, 0, 300)
+
+
+def test_ffn_fp8_prefill_skewed():
+    T, E, k = 300, 6, 2
+    ids = np.stack([np.full(T, 2, np.int32), (3 + np.arange(T, dtype=np.int32) % 3)], 1)
+    check_ffn_fp8(T, 512, 256, E, k, 0, E, ids=ids)
+
+
+def test_ffn_fp8_prefill_share():
+    check_ffn_fp8(384, 512, 256, 20, 4, 5, 6)
+
+
+def test_ffn_fp8_share0_full_size_sampled():
+    """The share-0 prefill shape at full size (T4096 H7168 I2048, experts 0..76
+    of 384, top-8) on FP8 codes, in the staged kernels bench.py times: every
+    output row of five sampled entries against the oracle's single-entry FFN."""
+    T, H, I, E, k, first, L = 4096, 7168, 2048, 384, 8, 0, 77
+    note(f"ffn fp8 share-0 full size T={T} H={H} I={I} E={E} k={k} share=({first},{L})")
+    x, w1q, w1s, w2q, w2s, ids = layer_fp8(7, T, H, I, E, k, first, L)
+    _, offsets, perm, _ = oracle.permute(ids, E, first, L)
+    got = run_ffn_fp8(x, perm, offsets, k, w1q, w1s, w2q, w2s)
+    n = int(offsets[-1])
+    assert np.isnan(got[n:]).all()
+    for p in (0, n // 4, n // 2, (3 * n) // 4, n - 1):
+        e = int(np.searchsorted(offsets, p, side="right") - 1)
+        ref = oracle.expert_row_fp8(x[perm[p] // k], w1q[e], w1s[e], w2q[e], w2s[e])
         err = np.abs(got[p].astype(np.float64) - ref)
         assert err.max() <= 1e-4 * np.abs(ref).max(), (p, err.max() / np.abs(ref).max())
