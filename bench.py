@@ -55,10 +55,16 @@ def parse_args():
 
 
 def ffn_source_digest():
+    """Digest of the grouped-FFN code (ffn.hip, ffn_sk.hip, device.h) with
+    line comments, trailing blanks and empty lines removed, so that editing a
+    comment does not retire the committed counter summary."""
     h = hashlib.sha256()
     for name in ("ffn.hip", "ffn_sk.hip", "device.h"):
-        with open(os.path.join(ROOT, "routing_grouped_expert_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "routing_grouped_expert_amd", "csrc", name)) as f:
+            for line in f:
+                code = re.sub(r"//.*$", "", line).rstrip()
+                if code:
+                    h.update(code.encode() + b"\n")
     return h.hexdigest()[:16]
 
 

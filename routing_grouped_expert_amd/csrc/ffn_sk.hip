@@ -1,23 +1,26 @@
-// Grouped expert FFN, persistent "stream-K" schedule for the 16-byte /
-// 256-element fast path.
+// Grouped expert FFN: persistent kernels for the 16-byte fast path. The
+// K-split kernels (one 16-token tile per pass: decode) and the staged
+// kernels (4 or 8 token tiles per pass, token rows staged in LDS: prefill)
+// share the schedule below.
 //
 // Why: the expert weights are streamed once and every config is HBM-bound, so
 // the kernel time is (weight bytes) / (bandwidth actually sustained). A grid
 // of equal blocks that does not divide evenly into the resident block slots
 // leaves a last partial round with too few loads in flight. Here exactly the
-// resident number of blocks NB is launched and the work is cut into equal
-// contiguous ranges of units:
+// resident number of blocks NB is launched and the work is cut into units:
 //   tile = (pass, row group)   pass = up to NT*16 tokens of one expert
-//   unit = (tile, K chunk of 512 (up) or 1024 (down)), taken in two halves;
-//          the 4 waves of a block take a quarter of each half.
-// (With fewer units than resident blocks only the first U blocks take part,
-// so every participating block owns at least one unit.)
-// A block runs its units in order, adding its waves' partial sums in LDS in a
-// fixed order (wave 0, 1, 2, 3) at the end of each tile. A tile covered by
-// one block is finished directly; a tile cut between blocks leaves one
-// partial per block in a slot, and the block that arrives last (atomic
-// counter) adds the slots in block order and finishes the tile. The order of
-// every sum is fixed by the schedule, so results do not depend on timing.
+//   unit = (tile, K chunk): K-split kernels 1024 (up; 512 when H is not a
+//          multiple of 1024) or 512 (down), taken in two halves, the 4 waves
+//          of a block taking a quarter of each half; staged kernels 64.
+// Tiles are dealt in whole rounds; when the rounds come out uneven, the last
+// tiles are cut into equal contiguous unit ranges (stream-K; see Sched).
+// A block runs its units in order; the K-split kernels add their waves'
+// partial sums in LDS in a fixed order (wave 0, 1, 2, 3) at the end of each
+// tile. A tile covered by one block is finished directly; a tile cut between
+// blocks leaves one partial per block in a slot, and the block that arrives
+// last (atomic counter) adds the slots in block order and finishes the tile.
+// The order of every sum is fixed by the schedule, so results do not depend
+// on timing.
 //
 // Operands: weight rows are the MFMA A operand and stream from HBM into VGPRs
 // as whole 128-byte lines (8 rows x 128 B per load instruction; bf16 weights
@@ -30,12 +33,12 @@
 // half unit are issued before the current half's MFMAs (section 2 of the same
 // page: the weight stream starts first and overlaps the activation gather).
 //
-// up:   tile rows = 16 gate rows + the 16 matching up rows; the finished tile
-//       applies SwiGLU and writes a = silu(g) * u as hi = bf16(a),
-//       lo = bf16(a - hi) (a is never rounded to bf16 alone).
-// down: tile rows = 64 rows of W2 (4 groups of 16 sharing each B fragment);
-//       B = hi and lo, two MFMAs into one fp32 accumulator; the finished tile
-//       writes fp32 expert_out.
+// up:   K-split tile rows = 16 gate rows + the 16 matching up rows; the
+//       finished tile applies SwiGLU and writes a = silu(g) * u as
+//       hi = bf16(a), lo = bf16(a - hi) (a is never rounded to bf16 alone).
+// down: K-split tile rows = 128 rows of W2 (8 groups of 16 sharing each B
+//       fragment); B = hi and lo, two MFMAs into one fp32 accumulator; the
+//       finished tile writes fp32 expert_out.
 #include "device.h"
 
 #include <algorithm>
@@ -877,16 +880,20 @@ __global__ __launch_bounds__(256) void ffn_down_sk_kernel(
 // chunks. The chunk of the pass's token rows (B operand, up to 128 tokens) is
 // staged once per block in LDS and read by all 8 waves, so each token byte
 // brought in serves 256 weight rows. Token rows are loaded two chunks ahead
-// (registers, then one of two LDS buffers) and weights one chunk ahead, so no
-// wait in a step is for a load issued in the same step. Up tiles hold 128 gate
-// rows and the matching 128 up rows (a wave: 16 of each), so SwiGLU is applied
-// in the epilogue.
+// (registers, then one of two LDS buffers) and weights one chunk ahead (two
+// for the up projection with 8 token tiles), so no wait in a step is for a
+// load issued in the same step. Up tiles hold 128 gate rows and the matching
+// 128 up rows (a wave: 16 of each), so SwiGLU is applied in the epilogue.
+// bf16 weights arrive as one full-line slab per group and chunk; FP8 codes
+// (16 per lane and group, fragment layout) are widened to bf16 just before
+// the MFMAs and the row scales applied to the finished sums.
 //
-// On this chip the vector-memory path of a CU moves about 10 bytes per clock
-// whatever the access pattern, and weights and token rows share it: the
-// token-row bytes per weight byte (tokens / tile rows, doubled for the hi + lo
-// intermediate of the down projection) set how close the weights stream comes
-// to the HBM rate, hence the tall tiles.
+// Weights and token rows share a CU's vector-memory path: the token-row bytes
+// per weight byte (tokens / tile rows, doubled for the hi + lo intermediate
+// of the down projection) limit how close the weights stream comes to the
+// HBM rate, hence the tall tiles; at the share-0 shape the MFMA phase of each
+// chunk, which the weight loads one chunk ahead do not fully cover, costs
+// more than the token traffic.
 constexpr int PF_WAVES = 8;
 constexpr int PF_THREADS = PF_WAVES * kWave;
 constexpr int PF_K = 64;
