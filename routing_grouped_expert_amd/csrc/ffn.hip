@@ -1,4 +1,7 @@
-// Grouped expert FFN on bf16 MFMA (v_mfma_f32_16x16x32_bf16, fp32 accumulate).
+// Grouped expert FFN on bf16 MFMA (v_mfma_f32_16x16x32_bf16, fp32 accumulate):
+// the entry points and the generic kernels. Shapes on the 16-byte fast path
+// go to the persistent kernels of ffn_sk.hip (K-split for few entries per
+// expert, staged for many); the generic kernels below take every other shape.
 //
 // Page "FlashInfer MoE optimisation: overlapping grouped activation staging
 // on Ampere and Hopper" (flashinfer PR #7368):
