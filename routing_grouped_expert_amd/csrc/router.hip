@@ -125,9 +125,11 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(const uint16_t* __rest
 // barrier per chunk and no wait on HBM inside it. Rows past T or E load the
 // last valid row (their results are never stored), so every load is
 // unconditional.
-// Measured at share 0 (T4096 H7168 E384): 394-398 us, against 406-427 us
-// with K-major tiles filled by 2- and 4-byte transposing stores, and 414 us
-// with 64 x 64 wave tiles (225 VGPRs, 2 blocks per CU).
+// Measured at share 0 (T4096 H7168 E384): 394-416 us, against 406-427 us
+// with K-major tiles filled by 2- and 4-byte transposing stores, 414 us with
+// 64 x 64 wave tiles (225 VGPRs, 2 blocks per CU), 414-427 us with 64-wide
+// chunks (half the barriers; 170 VGPRs, 2 blocks per CU), and no change when
+// the K slices were chosen to fill whole rounds of resident blocks.
 constexpr int FT = 128;              // tokens per block tile
 constexpr int XLD = MK + 8, WLD = MK + 4;  // LDS row lengths (elements)
 // At most 168 registers (3 blocks per CU; the kernel takes 122, so 4 fit).
