@@ -208,16 +208,20 @@ def main():
     ffn_ms = sum(e0.elapsed_time(e1) for e0, e1 in evs) / len(evs)
 
     # moe_forward over the same number of steps (same kernels in one call)
-    forward_ms = None
-    if not fp8:
-        for _ in range(2):
+    def forward():
+        if fp8:
+            moe.forward_fp8(x, wg, bias, w1q, w1s, w2q, w2s, k, first, L, y, ws, stream=stream)
+        else:
             moe.forward(x, wg, bias, w1, w2, k, first, L, y, ws, stream=stream)
-        torch.cuda.synchronize()
-        f0 = time.perf_counter()
-        for _ in range(args.steps):
-            moe.forward(x, wg, bias, w1, w2, k, first, L, y, ws, stream=stream)
-        torch.cuda.synchronize()
-        forward_ms = (time.perf_counter() - f0) / args.steps * 1e3
+
+    for _ in range(2):
+        forward()
+    torch.cuda.synchronize()
+    f0 = time.perf_counter()
+    for _ in range(args.steps):
+        forward()
+    torch.cuda.synchronize()
+    forward_ms = (time.perf_counter() - f0) / args.steps * 1e3
 
     cnt = counts.cpu().numpy()[first:first + L]
     n_local = int(cnt.sum())

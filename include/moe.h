@@ -219,6 +219,23 @@ moe_status moe_forward(const uint16_t* x, const float* w_gate, const float* rout
                        float* logits_out, int32_t* topk_ids_out, float* topk_weights_out,
                        void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * moe_forward_fp8 -- moe_forward with the FP8 expert weights of
+ * moe_grouped_ffn_fp8 (E4M3 codes and one fp32 scale per row, [P-ACT]
+ * section 2): router, route, permute and combine as in moe_forward, the
+ * grouped FFN as in moe_grouped_ffn_fp8.
+ *   w1q [num_local, 2I, H] uint8, w1s [num_local, 2I] fp32,
+ *   w2q [num_local, H, I] uint8, w2s [num_local, H] fp32 (local experts)
+ * Every other argument, the workspace (moe_workspace_size) and the errors
+ * are as for moe_forward.
+ */
+moe_status moe_forward_fp8(const uint16_t* x, const float* w_gate, const float* router_bias,
+                           const uint8_t* w1q, const float* w1s, const uint8_t* w2q,
+                           const float* w2s, int32_t T, int32_t H, int32_t I, int32_t E,
+                           int32_t k, int32_t first_expert, int32_t num_local, uint16_t* y,
+                           float* logits_out, int32_t* topk_ids_out, float* topk_weights_out,
+                           void* ws, size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

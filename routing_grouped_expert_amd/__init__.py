@@ -44,6 +44,8 @@ _SIGS = {
     "moe_combine": ([_VP, _VP, _VP, _I32, _I32, _I32, _VP, _VP], ctypes.c_int),
     "moe_forward": ([_VP, _VP, _VP, _VP, _VP] + [_I32] * 7 + [_VP, _VP, _VP, _VP, _VP, _SZ, _VP],
                     ctypes.c_int),
+    "moe_forward_fp8": ([_VP] * 7 + [_I32] * 7 + [_VP, _VP, _VP, _VP, _VP, _SZ, _VP],
+                        ctypes.c_int),
 }
 
 
@@ -159,6 +161,20 @@ def forward(x, w_gate, router_bias, w1, w2, k, first_expert, num_local, y, ws, l
     _check("moe_forward", lib().moe_forward(
         _ptr(x), _ptr(w_gate), _ptr(router_bias), _ptr(w1), _ptr(w2), T, H, I, E, k,
         first_expert, num_local, _ptr(y), _ptr(logits_out), _ptr(topk_ids_out),
+        _ptr(topk_weights_out), _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
+        _stream(stream)))
+
+
+def forward_fp8(x, w_gate, router_bias, w1q, w1s, w2q, w2s, k, first_expert, num_local, y, ws,
+                logits_out=None, topk_ids_out=None, topk_weights_out=None, stream=None):
+    """moe_forward_fp8: the layer with FP8 expert weights (codes and row scales
+    as for grouped_ffn_fp8)."""
+    T, H = x.shape
+    E = w_gate.shape[0]
+    I = w2q.shape[-1]
+    _check("moe_forward_fp8", lib().moe_forward_fp8(
+        _ptr(x), _ptr(w_gate), _ptr(router_bias), _ptr(w1q), _ptr(w1s), _ptr(w2q), _ptr(w2s), T,
+        H, I, E, k, first_expert, num_local, _ptr(y), _ptr(logits_out), _ptr(topk_ids_out),
         _ptr(topk_weights_out), _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
         _stream(stream)))
 

@@ -105,6 +105,48 @@ Layout layout(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k, int64_t L) 
 
 bool aligned256(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 255u) == 0; }
 
+// The layer for one expert share: router logits, route, permute, the grouped
+// FFN that `ffn` launches (bf16 or FP8 weights), combine. Arguments are
+// checked before any launch; weights_given says whether the FFN's weight
+// pointers are all non-NULL.
+template <class Ffn>
+moe_status forward_layer(const uint16_t* x, const float* w_gate, const float* router_bias,
+                         int32_t T, int32_t H, int32_t I, int32_t E, int32_t k,
+                         int32_t first_expert, int32_t num_local, uint16_t* y, float* logits_out,
+                         int32_t* topk_ids_out, float* topk_weights_out, void* ws,
+                         size_t ws_bytes, void* stream, bool weights_given, Ffn ffn) {
+  moe_status st = check_common(T, E, k);
+  if (st == MOE_SUCCESS) st = check_share(E, first_expert, num_local);
+  if (st == MOE_SUCCESS) st = check_dims(T, k, H, I);
+  if (st != MOE_SUCCESS) return st;
+  if ((int64_t)T * E >= kMaxIndex || (int64_t)E * H >= kMaxIndex) return MOE_ERROR_UNSUPPORTED;
+  if (T == 0) return MOE_SUCCESS;
+  if (!x || !w_gate || !y || (num_local > 0 && !weights_given)) return MOE_ERROR_INVALID_VALUE;
+  const Layout lo = layout(T, H, I, E, k, num_local);
+  if (!ws || ws_bytes < lo.total || !aligned256(ws)) return MOE_ERROR_WORKSPACE;
+  char* base = static_cast<char*>(ws);
+  float* logits = logits_out ? logits_out : reinterpret_cast<float*>(base + lo.logits);
+  int32_t* ids = topk_ids_out ? topk_ids_out : reinterpret_cast<int32_t*>(base + lo.ids);
+  float* wts = topk_weights_out ? topk_weights_out : reinterpret_cast<float*>(base + lo.weights);
+  int32_t* counts = reinterpret_cast<int32_t*>(base + lo.counts);
+  int32_t* offsets = reinterpret_cast<int32_t*>(base + lo.offsets);
+  int32_t* perm = reinterpret_cast<int32_t*>(base + lo.perm);
+  int32_t* e2p = reinterpret_cast<int32_t*>(base + lo.e2p);
+  float* eo = reinterpret_cast<float*>(base + lo.expert_out);
+  hipStream_t s = as_stream(stream);
+
+  clear_stale_error();
+  hipError_t err =
+      moe::launch_router_logits(x, w_gate, router_bias, T, H, E, logits, base + lo.router_ws, s);
+  if (err == hipSuccess) err = moe::launch_route(logits, T, E, k, ids, wts, s);
+  if (err == hipSuccess)
+    err = moe::launch_permute(ids, T, k, E, first_expert, num_local, counts, offsets, perm, e2p,
+                              base + lo.permute_ws, s);
+  if (err == hipSuccess && num_local > 0) err = ffn(perm, offsets, eo, base + lo.ffn_ws, s);
+  if (err == hipSuccess) err = moe::launch_combine(eo, e2p, wts, T, k, H, y, s);
+  return launched(err);
+}
+
 }  // namespace
 
 extern "C" {
@@ -247,38 +289,28 @@ moe_status moe_forward(const uint16_t* x, const float* w_gate, const float* rout
                        int32_t E, int32_t k, int32_t first_expert, int32_t num_local, uint16_t* y,
                        float* logits_out, int32_t* topk_ids_out, float* topk_weights_out,
                        void* ws, size_t ws_bytes, void* stream) {
-  moe_status st = check_common(T, E, k);
-  if (st == MOE_SUCCESS) st = check_share(E, first_expert, num_local);
-  if (st == MOE_SUCCESS) st = check_dims(T, k, H, I);
-  if (st != MOE_SUCCESS) return st;
-  if ((int64_t)T * E >= kMaxIndex || (int64_t)E * H >= kMaxIndex) return MOE_ERROR_UNSUPPORTED;
-  if (T == 0) return MOE_SUCCESS;
-  if (!x || !w_gate || !y || (num_local > 0 && (!w1 || !w2))) return MOE_ERROR_INVALID_VALUE;
-  const Layout lo = layout(T, H, I, E, k, num_local);
-  if (!ws || ws_bytes < lo.total || !aligned256(ws)) return MOE_ERROR_WORKSPACE;
-  char* base = static_cast<char*>(ws);
-  float* logits = logits_out ? logits_out : reinterpret_cast<float*>(base + lo.logits);
-  int32_t* ids = topk_ids_out ? topk_ids_out : reinterpret_cast<int32_t*>(base + lo.ids);
-  float* wts = topk_weights_out ? topk_weights_out : reinterpret_cast<float*>(base + lo.weights);
-  int32_t* counts = reinterpret_cast<int32_t*>(base + lo.counts);
-  int32_t* offsets = reinterpret_cast<int32_t*>(base + lo.offsets);
-  int32_t* perm = reinterpret_cast<int32_t*>(base + lo.perm);
-  int32_t* e2p = reinterpret_cast<int32_t*>(base + lo.e2p);
-  float* eo = reinterpret_cast<float*>(base + lo.expert_out);
-  hipStream_t s = as_stream(stream);
+  return forward_layer(
+      x, w_gate, router_bias, T, H, I, E, k, first_expert, num_local, y, logits_out,
+      topk_ids_out, topk_weights_out, ws, ws_bytes, stream, w1 && w2,
+      [&](const int32_t* perm, const int32_t* offsets, float* eo, void* fws, hipStream_t s) {
+        return moe::launch_grouped_ffn(x, perm, offsets, num_local, T, k, H, I, w1, w2, eo, fws,
+                                       s);
+      });
+}
 
-  clear_stale_error();
-  hipError_t err =
-      moe::launch_router_logits(x, w_gate, router_bias, T, H, E, logits, base + lo.router_ws, s);
-  if (err == hipSuccess) err = moe::launch_route(logits, T, E, k, ids, wts, s);
-  if (err == hipSuccess)
-    err = moe::launch_permute(ids, T, k, E, first_expert, num_local, counts, offsets, perm, e2p,
-                              base + lo.permute_ws, s);
-  if (err == hipSuccess && num_local > 0)
-    err = moe::launch_grouped_ffn(x, perm, offsets, num_local, T, k, H, I, w1, w2, eo,
-                                  base + lo.ffn_ws, s);
-  if (err == hipSuccess) err = moe::launch_combine(eo, e2p, wts, T, k, H, y, s);
-  return launched(err);
+moe_status moe_forward_fp8(const uint16_t* x, const float* w_gate, const float* router_bias,
+                           const uint8_t* w1q, const float* w1s, const uint8_t* w2q,
+                           const float* w2s, int32_t T, int32_t H, int32_t I, int32_t E,
+                           int32_t k, int32_t first_expert, int32_t num_local, uint16_t* y,
+                           float* logits_out, int32_t* topk_ids_out, float* topk_weights_out,
+                           void* ws, size_t ws_bytes, void* stream) {
+  return forward_layer(
+      x, w_gate, router_bias, T, H, I, E, k, first_expert, num_local, y, logits_out,
+      topk_ids_out, topk_weights_out, ws, ws_bytes, stream, w1q && w1s && w2q && w2s,
+      [&](const int32_t* perm, const int32_t* offsets, float* eo, void* fws, hipStream_t s) {
+        return moe::launch_grouped_ffn_fp8(x, perm, offsets, num_local, T, k, H, I, w1q, w1s, w2q,
+                                           w2s, eo, fws, s);
+      });
 }
 
 }  // extern "C"

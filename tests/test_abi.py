@@ -19,7 +19,7 @@ def test_exports_every_declared_symbol():
     names = _declared()
     assert {"moe_partition", "moe_workspace_size", "moe_router_logits", "moe_route",
             "moe_permute", "moe_grouped_ffn", "moe_grouped_ffn_fp8", "moe_combine", "moe_forward",
-            "moe_status_string", "moe_last_launch_error"} <= names
+            "moe_forward_fp8", "moe_status_string", "moe_last_launch_error"} <= names
     L = ctypes.CDLL(moe.LIB_PATH)
     for n in sorted(names):
         assert hasattr(L, n), n
@@ -123,5 +123,12 @@ def test_calls_reject_bad_arguments_without_launching():
                          None, FAKE, 256, None) == 3
     assert L.moe_forward(FAKE, FAKE, None, FAKE, FAKE, 4, 64, 64, 8, 2, 0, 8, None, None, None,
                          None, FAKE, 1 << 30, None) == 1
+    # forward with FP8 weights: share past E, a missing scale, workspace too small
+    assert L.moe_forward_fp8(FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, 4, 64, 64, 8, 2, 4, 5,
+                             FAKE, None, None, None, FAKE, 1 << 30, None) == 1
+    assert L.moe_forward_fp8(FAKE, FAKE, None, FAKE, None, FAKE, FAKE, 4, 64, 64, 8, 2, 0, 8,
+                             FAKE, None, None, None, FAKE, 1 << 30, None) == 1
+    assert L.moe_forward_fp8(FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, 4, 64, 64, 8, 2, 0, 8,
+                             FAKE, None, None, None, FAKE, 256, None) == 3
     assert L.moe_router_logits(FAKE, FAKE, None, 4, 0, 8, FAKE, None, 0, None) == 1
     assert L.moe_router_logits(FAKE, FAKE, None, 100, 64, 8, FAKE, None, 0, None) == 3
