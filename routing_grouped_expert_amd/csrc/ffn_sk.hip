@@ -957,11 +957,13 @@ struct PfA<true> {
   u32x4 v[PF_GROUPS];
 };
 
-// acc[q * NT + nt] += A(group q) * B(token tile nt) over one chunk; the down
-// projection multiplies both halves (hi, lo) of the intermediate.
-template <int NT, bool UP, bool F8>
+// acc[q * NT + nt] += A(group q) * B(token tile nt) over one chunk for the
+// first NV token tiles (the others hold no entry of the pass and keep zero
+// sums); the down projection multiplies both halves (hi, lo) of the
+// intermediate.
+template <int NT, int NV, bool UP, bool F8>
 __device__ __forceinline__ void pf_mma(const PfA<F8>& a, const pf_row_t* b0, const pf_row_t* b1,
-                                       int lane, f32x4* acc) {
+                                       int lane, f32x4* acc, int nv) {
 #pragma unroll
   for (int st = 0; st < PF_STEPS; ++st) {
     bf16x8 w[PF_GROUPS];
@@ -971,7 +973,8 @@ __device__ __forceinline__ void pf_mma(const PfA<F8>& a, const pf_row_t* b0, con
       else w[q] = a.v[q][st];
     }
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
+    for (int nt = 0; nt < NV; ++nt) {
+      if (nt >= nv) break;
       const int n = nt * 16 + (lane & 15);
       const int c = F8 ? (lane >> 4) * 16 + st * 8 : st * 32 + (lane >> 4) * 8;
       const bf16x8 h = *reinterpret_cast<const bf16x8*>(&b0[n][c]);
@@ -1053,8 +1056,7 @@ __device__ __forceinline__ void pf_finish(PfTile<NT>& st, const PfRaw<NT>& raw, 
 
 // With 4 token tiles, at most 128 VGPRs, so that two blocks share a CU: the
 // down projection then took 1477 us against 1617 us with one block per CU
-// (fine-grained shape; a few addresses spill to scratch); the up projection
-// fits 128 anyway.
+// (fine-grained shape); the up projection fits 128 anyway.
 // F8: FP8 E4M3 weight codes with one fp32 scale per row (wscale), applied to
 // the finished sums.
 template <int NT, bool UP, bool F8>
@@ -1228,7 +1230,14 @@ __global__ __launch_bounds__(PF_THREADS, NT <= 4 ? 4 : 1) void ffn_pf_kernel(
 #pragma unroll
       for (int q = 0; q < PF_GROUPS; ++q) slab_frags(ca.v[q], slab_t[wave] + q * 128, lane);
     }
-    pf_mma<NT, UP, F8>(ca, bs[cb][0], bs[cb][NB_ARR - 1], lane, acc);
+    // Token tiles of the pass that hold entries; the MFMAs and LDS reads of
+    // the others are skipped (their sums stay zero). Passes are often far
+    // from full: at the fine-grained shape 1 or 2 of 4 tiles, at share 0
+    // 4 to 7 of 8 (share 0: 1.42 ms against 1.52-1.56 ms for the call). The
+    // test sits inside the tile loop: dispatching to kernels unrolled for
+    // fewer tiles made every variant spill.
+    const int nv = __builtin_amdgcn_readfirstlane(t0.ntiles);
+    pf_mma<NT, NT, UP, F8>(ca, bs[cb][0], bs[cb][NB_ARR - 1], lane, acc, nv);
     store_b(cs, cb ^ 1);
     const bool last = sc.last(p);
     if (sc.ends_tile(p)) tile_end(p);
