@@ -1198,8 +1198,11 @@ __global__ __launch_bounds__(PF_THREADS, NT <= 4 ? 4 : 1) void ffn_pf_kernel(
   // registers; chunk p1's token rows in flight
   // A3: the up projection with 8 token tiles (238 VGPRs) fetches its weights
   // two units ahead, through three register sets (share 0: 882 us against
-  // 911 us one unit ahead); the others stay at one unit ahead.
-  constexpr bool A3 = UP && NT >= 8;
+  // 911 us one unit ahead), and so do the FP8 kernels, whose register sets
+  // are small (fine-grained FP8 call: 2.26 ms against 2.31 ms; share 0
+  // unchanged); the others stay at one unit ahead (the bf16 down projection
+  // at 8 tiles measured the same either way).
+  constexpr bool A3 = (UP && NT >= 8) || F8;
   PfA<F8> a0, a1, a2;  // a2: A3 only
   PfStage<NR> sb0[NB_ARR], sb1[NB_ARR];
   load_b(sb1, t0, p0.kc);
