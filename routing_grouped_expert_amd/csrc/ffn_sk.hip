@@ -75,7 +75,8 @@ constexpr int DOWN_KUNIT = 2 * 4 * 32 * DOWN_STEPS;
 constexpr int UP_CAP = 1;
 constexpr int DOWN_CAP = 1;
 // FP8 weights: MFMA steps per half unit (even: a 16-byte load of codes feeds
-// two steps) and blocks per CU.
+// two steps) and blocks per CU (the up kernel at 3 blocks per CU, which its
+// 100 VGPRs and 48 KB of LDS allow: 174 us against 169 us at 2, decode shape).
 constexpr int UP8_STEPS = 4;
 constexpr int DOWN8_STEPS = 4;
 constexpr int UP8_KUNIT = 2 * 4 * 32 * UP8_STEPS;
