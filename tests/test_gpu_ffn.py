@@ -121,6 +121,24 @@ def test_ffn_prefill_skewed():
     check_ffn(T, 512, 256, E, k, 0, E, ids=ids)
 
 
+def partial_pass_ids(counts, seed=3):
+    """Top-1 selections with the given entries per expert, tokens shuffled:
+    passes that fill every number of 16-token tiles."""
+    ids = np.repeat(np.arange(len(counts), dtype=np.int32), counts)
+    return np.random.default_rng(seed).permutation(ids).reshape(-1, 1)
+
+
+# Passes of the staged kernels multiply only their token tiles that hold
+# entries: 8-tile passes holding 1 to 8 tiles (an expert of 169 entries takes
+# a full pass and a 3-tile one), and 4-tile passes holding 1 to 4.
+@pytest.mark.parametrize("counts", [[1, 17, 33, 49, 65, 81, 97, 169],
+                                    [1, 16, 17, 32, 33, 48, 49, 64, 63, 50, 31, 18, 15, 2, 40,
+                                     33]])
+def test_ffn_prefill_partial_passes(counts):
+    ids = partial_pass_ids(counts)
+    check_ffn(len(ids), 512, 256, len(counts), 1, 0, len(counts), ids=ids)
+
+
 def test_ffn_prefill_share():
     check_ffn(384, 512, 256, 20, 4, 5, 6)
 

@@ -67,6 +67,16 @@ def test_ffn_fp8_checked_path_ragged(H, I):
     check_ffn_fp8(37, H, I, 5, 2, 0, 5)
 
 
+@pytest.mark.parametrize("counts", [[1, 17, 33, 49, 65, 81, 97, 169],
+                                    [1, 16, 17, 32, 33, 48, 49, 64, 63, 50, 31, 18, 15, 2, 40,
+                                     33]])
+def test_ffn_fp8_prefill_partial_passes(counts):
+    """Staged passes holding every number of their 8 (or 4) token tiles."""
+    ids = np.repeat(np.arange(len(counts), dtype=np.int32), counts)
+    ids = np.random.default_rng(3).permutation(ids).reshape(-1, 1)
+    check_ffn_fp8(len(ids), 512, 256, len(counts), 1, 0, len(counts), ids=ids)
+
+
 def test_ffn_fp8_share_and_empty_experts():
     check_ffn_fp8(40, 128, 256, 16, 2, 3, 9)
 
