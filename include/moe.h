@@ -37,8 +37,8 @@
  *  - T = 0 is valid and launches nothing.
  *  - Limits: 1 <= E <= 4096, 1 <= k <= min(E, 32), H >= 1, I >= 1,
  *    T * k < 2^31, T * k * max(H, I) < 2^31 elements.
- *  - Fast path: 16-byte aligned x / w1 / w2 / workspace and H, I multiples of
- *    128. Any other shape or alignment runs a correct element-wise path
+ *  - Fast path: 16-byte aligned x / w1 / w2 / expert_out / workspace and H, I
+ *    multiples of 128. Any other shape or alignment runs a correct element-wise path
  *    instead of failing ([P-ACT] section 1: the 128-bit vector gather keeps a
  *    scalar fallback for unaligned inputs).
  */

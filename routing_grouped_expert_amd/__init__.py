@@ -77,6 +77,39 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+def _need(t, name, shape, esize, optional=False):
+    """Raise ValueError unless t is a contiguous GPU tensor of `shape` whose
+    elements are `esize` bytes (None allowed when optional). Checked before
+    every call, so a host tensor, a strided view or a wrong shape never
+    reaches a kernel."""
+    if t is None:
+        if optional:
+            return
+        raise ValueError(f"{name} is required")
+    if not getattr(t, "is_cuda", False):
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.element_size() != esize:
+        raise ValueError(f"{name} must have {esize}-byte elements, not {t.element_size()}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _need_ws(ws):
+    if ws is None:
+        return 0
+    if not getattr(ws, "is_cuda", False) or not ws.is_contiguous():
+        raise ValueError("ws must be a contiguous GPU tensor")
+    return ws.numel() * ws.element_size()
+
+
+def _dims(t, name, nd):
+    if t is None or t.dim() != nd:
+        raise ValueError(f"{name} must be a {nd}-d tensor")
+    return tuple(t.shape)
+
+
 def _stream(stream):
     if stream is None:
         import torch
@@ -100,83 +133,133 @@ def workspace_size(T, H, I, E, k, num_local):
 
 
 def router_logits(x, w_gate, bias, logits, ws, stream=None):
-    T, H = x.shape
-    E = w_gate.shape[0]
+    T, H = _dims(x, "x", 2)
+    E = _dims(w_gate, "w_gate", 2)[0]
+    _need(x, "x", (T, H), 2)
+    _need(w_gate, "w_gate", (E, H), 4)
+    _need(bias, "bias", (E,), 4, optional=True)
+    _need(logits, "logits", (T, E), 4)
+    nws = _need_ws(ws)
     _check("moe_router_logits", lib().moe_router_logits(
-        _ptr(x), _ptr(w_gate), _ptr(bias), T, H, E, _ptr(logits), _ptr(ws),
-        0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
+        _ptr(x), _ptr(w_gate), _ptr(bias), T, H, E, _ptr(logits), _ptr(ws), nws,
+        _stream(stream)))
 
 
 def route(logits, k, topk_ids, topk_weights, stream=None):
-    T, E = logits.shape
+    T, E = _dims(logits, "logits", 2)
+    _need(logits, "logits", (T, E), 4)
+    _need(topk_ids, "topk_ids", (T, k), 4)
+    _need(topk_weights, "topk_weights", (T, k), 4)
     _check("moe_route", lib().moe_route(_ptr(logits), T, E, k, _ptr(topk_ids),
                                         _ptr(topk_weights), _stream(stream)))
 
 
 def permute(topk_ids, num_experts, first_expert, num_local, expert_counts, expert_offsets,
             permuted_rows, expanded_to_permuted, ws, stream=None):
-    T, k = topk_ids.shape
+    T, k = _dims(topk_ids, "topk_ids", 2)
+    _need(topk_ids, "topk_ids", (T, k), 4)
+    _need(expert_counts, "expert_counts", (num_experts,), 4)
+    _need(expert_offsets, "expert_offsets", (num_local + 1,), 4)
+    _need(permuted_rows, "permuted_rows", (T * k,), 4)
+    _need(expanded_to_permuted, "expanded_to_permuted", (T * k,), 4)
+    nws = _need_ws(ws)
     _check("moe_permute", lib().moe_permute(
         _ptr(topk_ids), T, k, num_experts, first_expert, num_local, _ptr(expert_counts),
-        _ptr(expert_offsets), _ptr(permuted_rows), _ptr(expanded_to_permuted), _ptr(ws),
-        0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
+        _ptr(expert_offsets), _ptr(permuted_rows), _ptr(expanded_to_permuted), _ptr(ws), nws,
+        _stream(stream)))
+
+
+def _ffn_common(x, permuted_rows, expert_offsets, k, w2, expert_out):
+    T, H = _dims(x, "x", 2)
+    L = _dims(expert_offsets, "expert_offsets", 1)[0] - 1
+    I = _dims(w2, "w2", 3)[2]
+    _need(x, "x", (T, H), 2)
+    _need(permuted_rows, "permuted_rows", (T * k,), 4)
+    _need(expert_offsets, "expert_offsets", (L + 1,), 4)
+    _need(expert_out, "expert_out", (T * k, H), 4)
+    return T, H, L, I
 
 
 def grouped_ffn(x, permuted_rows, expert_offsets, k, w1, w2, expert_out, ws, stream=None):
-    T, H = x.shape
-    L = expert_offsets.shape[0] - 1
-    I = w2.shape[-1]
+    T, H, L, I = _ffn_common(x, permuted_rows, expert_offsets, k, w2, expert_out)
+    _need(w1, "w1", (L, 2 * I, H), 2)
+    _need(w2, "w2", (L, H, I), 2)
+    nws = _need_ws(ws)
     _check("moe_grouped_ffn", lib().moe_grouped_ffn(
         _ptr(x), _ptr(permuted_rows), _ptr(expert_offsets), L, T, k, H, I, _ptr(w1), _ptr(w2),
-        _ptr(expert_out), _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
-        _stream(stream)))
+        _ptr(expert_out), _ptr(ws), nws, _stream(stream)))
 
 
 def grouped_ffn_fp8(x, permuted_rows, expert_offsets, k, w1q, w1s, w2q, w2s, expert_out, ws,
                     stream=None):
     """moe_grouped_ffn_fp8: w1q [L, 2I, H] and w2q [L, H, I] uint8 E4M3 codes,
     w1s [L, 2I] and w2s [L, H] fp32 row scales."""
-    T, H = x.shape
-    L = expert_offsets.shape[0] - 1
-    I = w2q.shape[-1]
+    T, H, L, I = _ffn_common(x, permuted_rows, expert_offsets, k, w2q, expert_out)
+    _need(w1q, "w1q", (L, 2 * I, H), 1)
+    _need(w1s, "w1s", (L, 2 * I), 4)
+    _need(w2q, "w2q", (L, H, I), 1)
+    _need(w2s, "w2s", (L, H), 4)
+    nws = _need_ws(ws)
     _check("moe_grouped_ffn_fp8", lib().moe_grouped_ffn_fp8(
         _ptr(x), _ptr(permuted_rows), _ptr(expert_offsets), L, T, k, H, I, _ptr(w1q), _ptr(w1s),
-        _ptr(w2q), _ptr(w2s), _ptr(expert_out), _ptr(ws),
-        0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
+        _ptr(w2q), _ptr(w2s), _ptr(expert_out), _ptr(ws), nws, _stream(stream)))
 
 
 def combine(expert_out, expanded_to_permuted, topk_weights, y, stream=None):
-    T, k = topk_weights.shape
-    H = y.shape[1]
+    T, k = _dims(topk_weights, "topk_weights", 2)
+    H = _dims(y, "y", 2)[1]
+    _need(topk_weights, "topk_weights", (T, k), 4)
+    _need(y, "y", (T, H), 2)
+    _need(expert_out, "expert_out", (T * k, H), 4)
+    _need(expanded_to_permuted, "expanded_to_permuted", (T * k,), 4)
     _check("moe_combine", lib().moe_combine(_ptr(expert_out), _ptr(expanded_to_permuted),
                                             _ptr(topk_weights), T, k, H, _ptr(y),
                                             _stream(stream)))
 
 
+def _forward_common(x, w_gate, router_bias, k, y, logits_out, topk_ids_out, topk_weights_out):
+    T, H = _dims(x, "x", 2)
+    E = _dims(w_gate, "w_gate", 2)[0]
+    _need(x, "x", (T, H), 2)
+    _need(w_gate, "w_gate", (E, H), 4)
+    _need(router_bias, "router_bias", (E,), 4, optional=True)
+    _need(y, "y", (T, H), 2)
+    _need(logits_out, "logits_out", (T, E), 4, optional=True)
+    _need(topk_ids_out, "topk_ids_out", (T, k), 4, optional=True)
+    _need(topk_weights_out, "topk_weights_out", (T, k), 4, optional=True)
+    return T, H, E
+
+
 def forward(x, w_gate, router_bias, w1, w2, k, first_expert, num_local, y, ws, logits_out=None,
             topk_ids_out=None, topk_weights_out=None, stream=None):
-    T, H = x.shape
-    E = w_gate.shape[0]
-    I = w2.shape[-1]
+    T, H, E = _forward_common(x, w_gate, router_bias, k, y, logits_out, topk_ids_out,
+                              topk_weights_out)
+    I = _dims(w2, "w2", 3)[2]
+    _need(w1, "w1", (num_local, 2 * I, H), 2)
+    _need(w2, "w2", (num_local, H, I), 2)
+    nws = _need_ws(ws)
     _check("moe_forward", lib().moe_forward(
         _ptr(x), _ptr(w_gate), _ptr(router_bias), _ptr(w1), _ptr(w2), T, H, I, E, k,
         first_expert, num_local, _ptr(y), _ptr(logits_out), _ptr(topk_ids_out),
-        _ptr(topk_weights_out), _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
-        _stream(stream)))
+        _ptr(topk_weights_out), _ptr(ws), nws, _stream(stream)))
 
 
 def forward_fp8(x, w_gate, router_bias, w1q, w1s, w2q, w2s, k, first_expert, num_local, y, ws,
                 logits_out=None, topk_ids_out=None, topk_weights_out=None, stream=None):
     """moe_forward_fp8: the layer with FP8 expert weights (codes and row scales
     as for grouped_ffn_fp8)."""
-    T, H = x.shape
-    E = w_gate.shape[0]
-    I = w2q.shape[-1]
+    T, H, E = _forward_common(x, w_gate, router_bias, k, y, logits_out, topk_ids_out,
+                              topk_weights_out)
+    I = _dims(w2q, "w2q", 3)[2]
+    _need(w1q, "w1q", (num_local, 2 * I, H), 1)
+    _need(w1s, "w1s", (num_local, 2 * I), 4)
+    _need(w2q, "w2q", (num_local, H, I), 1)
+    _need(w2s, "w2s", (num_local, H), 4)
+    nws = _need_ws(ws)
     _check("moe_forward_fp8", lib().moe_forward_fp8(
         _ptr(x), _ptr(w_gate), _ptr(router_bias), _ptr(w1q), _ptr(w1s), _ptr(w2q), _ptr(w2s), T,
         H, I, E, k, first_expert, num_local, _ptr(y), _ptr(logits_out), _ptr(topk_ids_out),
-        _ptr(topk_weights_out), _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
-        _stream(stream)))
+        _ptr(topk_weights_out), _ptr(ws), nws, _stream(stream)))
 
 
 def alloc_workspace(T, H, I, E, k, num_local, device="cuda"):

@@ -390,11 +390,11 @@ hipError_t launch_generic(const uint16_t* x, const int* perm, const int* offsets
 }
 }  // namespace
 
-bool ffn_sk_applies(const void* x, const void* w1, const void* w2, int T, int k, int L, int H,
-                    int I);
+bool ffn_sk_applies(const void* x, const void* w1, const void* w2, const void* out, int T, int k,
+                    int L, int H, int I);
 size_t ffn_sk_workspace_bytes(int T, int k, int L);
-bool ffn_sk_fp8_applies(const void* x, const void* w1q, const void* w2q, int T, int k, int L,
-                        int H, int I);
+bool ffn_sk_fp8_applies(const void* x, const void* w1q, const void* w2q, const void* out, int T,
+                        int k, int L, int H, int I);
 hipError_t launch_grouped_ffn_sk_fp8(const uint16_t* x, const int* perm, const int* offsets,
                                      int L, int T, int k, int H, int I, const uint8_t* w1q,
                                      const float* w1s, const uint8_t* w2q, const float* w2s,
@@ -417,9 +417,10 @@ size_t ffn_workspace_bytes(int T, int k, int I, int L) {
   return 2 * h_array_bytes(T, k, I) + ffn_sk_workspace_bytes(T, k, L);
 }
 
-bool ffn_vector_path(const void* x, const void* w1, const void* w2, const void* ws, int H, int I) {
+bool ffn_vector_path(const void* x, const void* w1, const void* w2, const void* ws,
+                     const void* out, int H, int I) {
   auto al = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
-  return al(x) && al(w1) && al(w2) && al(ws) && H % KC == 0 && I % KC == 0 &&
+  return al(x) && al(w1) && al(w2) && al(ws) && al(out) && H % KC == 0 && I % KC == 0 &&
          H % BLOCK_ROWS == 0 && I % BLOCK_ROWS == 0;
 }
 
@@ -429,11 +430,11 @@ hipError_t launch_grouped_ffn(const uint16_t* x, const int* perm, const int* off
   const size_t half = h_array_bytes(T, k, I);
   uint16_t* h_hi = static_cast<uint16_t*>(ws);
   uint16_t* h_lo = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + half);
-  if (ffn_sk_applies(x, w1, w2, T, k, L, H, I))
+  if (ffn_sk_applies(x, w1, w2, out, T, k, L, H, I))
     return launch_grouped_ffn_sk(x, perm, offsets, L, T, k, H, I, w1, w2, h_hi, h_lo, out,
                                  static_cast<char*>(ws) + 2 * half, stream);
   return launch_generic<false>(x, perm, offsets, L, T, k, H, I, w1, nullptr, w2, nullptr, h_hi,
-                               h_lo, out, ffn_vector_path(x, w1, w2, ws, H, I), stream);
+                               h_lo, out, ffn_vector_path(x, w1, w2, ws, out, H, I), stream);
 }
 
 // FP8 E4M3 weights with per-row fp32 scales (w1s [L, 2I], w2s [L, H]).
@@ -444,11 +445,11 @@ hipError_t launch_grouped_ffn_fp8(const uint16_t* x, const int* perm, const int*
   const size_t half = h_array_bytes(T, k, I);
   uint16_t* h_hi = static_cast<uint16_t*>(ws);
   uint16_t* h_lo = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + half);
-  if (ffn_sk_fp8_applies(x, w1q, w2q, T, k, L, H, I))
+  if (ffn_sk_fp8_applies(x, w1q, w2q, out, T, k, L, H, I))
     return launch_grouped_ffn_sk_fp8(x, perm, offsets, L, T, k, H, I, w1q, w1s, w2q, w2s, h_hi,
                                      h_lo, out, static_cast<char*>(ws) + 2 * half, stream);
   return launch_generic<true>(x, perm, offsets, L, T, k, H, I, w1q, w1s, w2q, w2s, h_hi, h_lo,
-                              out, ffn_vector_path(x, w1q, w2q, ws, H, I), stream);
+                              out, ffn_vector_path(x, w1q, w2q, ws, out, H, I), stream);
 }
 
 }  // namespace moe

@@ -389,6 +389,7 @@ __device__ bool fixup_block(f32x4 (&part)[N], f32x4* slots, int* counters, long 
 template <int RG, int S>
 struct UpOps {
   bf16x8 g[RG][S], u[RG][S], x[S];
+  bool xz;  // the lane's entry is out of range: its token fragment reads as zero
 };
 
 // Loads go out row group by row group, so a lane's requests to one weight
@@ -398,7 +399,8 @@ struct UpOps {
 // into fragments.
 template <int RG, int S>
 __device__ __forceinline__ void up_load(UpOps<RG, S>& r, const uint16_t* wg, const uint16_t* wu,
-                                        const uint16_t* x, int H, size_t kb) {
+                                        const uint16_t* x, int H, size_t kb, bool xz) {
+  r.xz = xz;
   if constexpr (kFullLines) {
     static_assert(S % 2 == 0, "a slab is two MFMA steps");
 #pragma unroll
@@ -429,6 +431,8 @@ __device__ __forceinline__ void up_load(UpOps<RG, S>& r, const uint16_t* wg, con
 // (RG S of 128 u16x8) for the full-line slabs.
 template <int RG, int S>
 __device__ __forceinline__ void up_mma(UpOps<RG, S>& r, f32x4 (&acc)[2 * RG], u16x8* t, int lane) {
+#pragma unroll
+  for (int st = 0; st < S; ++st) r.x[st] = r.xz ? bf16x8{} : r.x[st];
   if constexpr (kFullLines) {
 #pragma unroll
     for (int q = 0; q < RG; ++q)
@@ -459,11 +463,13 @@ struct UpOps8 {
   static_assert(S % 2 == 0, "pairs of MFMA steps");
   u32x4 g[RG][S / 2], u[RG][S / 2];
   bf16x8 x[S];
+  bool xz;  // as in UpOps
 };
 
 template <int RG, int S>
 __device__ __forceinline__ void up_load(UpOps8<RG, S>& r, const uint8_t* wg, const uint8_t* wu,
-                                        const uint16_t* x, int H, size_t kb) {
+                                        const uint16_t* x, int H, size_t kb, bool xz) {
+  r.xz = xz;
   if constexpr (kFullLines) {
     static_assert(S == 4, "an FP8 slab is four MFMA steps");
 #pragma unroll
@@ -488,6 +494,8 @@ __device__ __forceinline__ void up_load(UpOps8<RG, S>& r, const uint8_t* wg, con
 
 template <int RG, int S>
 __device__ __forceinline__ void up_mma(UpOps8<RG, S>& r, f32x4 (&acc)[2 * RG], u16x8* t, int lane) {
+#pragma unroll
+  for (int st = 0; st < S; ++st) r.x[st] = r.xz ? bf16x8{} : r.x[st];
   if constexpr (kFullLines) {
 #pragma unroll
     for (int q = 0; q < RG; ++q) {
@@ -521,6 +529,7 @@ struct UpTile {
   int g, ex, tb, tc;
   size_t wrow;  // lane's gate row (+ its K offset) in W1
   size_t xoff;  // lane's token row (+ its K offset) in x
+  bool xz;      // the lane's entry is outside [0, T k): a zero row
 };
 
 __device__ __forceinline__ void up_issue(UpRaw& raw, int tile, int G, const PlanRO& pv,
@@ -536,7 +545,9 @@ __device__ __forceinline__ void up_issue(UpRaw& raw, int tile, int G, const Plan
 
 // Token slots past the pass's entries read a valid row (the first entry's):
 // MFMA output column n depends only on B column n and those columns are never
-// stored, so every load of the main loop is unconditional.
+// stored, so every load of the main loop is unconditional. An entry whose
+// expanded index is outside [0, T k) reads token 0's row, and its fragment is
+// replaced by zeros before the MFMAs (a zero row, as the interface states).
 template <int RG>
 __device__ __forceinline__ void up_finish(UpTile& st, const UpRaw& raw, int k, int H, int I,
                                           int nmax, size_t wlane, int kq) {
@@ -545,7 +556,8 @@ __device__ __forceinline__ void up_finish(UpTile& st, const UpRaw& raw, int k, i
   st.tb = raw.tb;
   st.tc = raw.tc;
   st.wrow = ((size_t)raw.ex * 2 * I + raw.g * (16 * RG)) * H + wlane;
-  const int r = (raw.r >= 0 && raw.r < nmax) ? raw.r : 0;
+  st.xz = !(raw.r >= 0 && raw.r < nmax);
+  const int r = st.xz ? 0 : raw.r;
   st.xoff = (size_t)(r / k) * H + kq;
 }
 
@@ -634,10 +646,10 @@ __global__ __launch_bounds__(256) void ffn_up_sk_kernel(
   // this is its last unit in the block. Every unit starts with its first
   // half in flight in `h0`, so no register changes role between units.
   Ops h0, h1;
-  up_load(h0, w1 + ts.wrow, w1 + ts.wrow + I_H, x + ts.xoff, H, (size_t)rg.p0.kc * KUNIT);
+  up_load(h0, w1 + ts.wrow, w1 + ts.wrow + I_H, x + ts.xoff, H, (size_t)rg.p0.kc * KUNIT, ts.xz);
   __builtin_amdgcn_sched_barrier(0);
   for (Pos p = rg.p0;;) {
-    up_load(h1, w1 + ts.wrow, w1 + ts.wrow + I_H, x + ts.xoff, H, (size_t)p.kc * KUNIT + KHALF);
+    up_load(h1, w1 + ts.wrow, w1 + ts.wrow + I_H, x + ts.xoff, H, (size_t)p.kc * KUNIT + KHALF, ts.xz);
     __builtin_amdgcn_sched_barrier(0);
     up_mma(h0, acc, tw, lane);
     const Pos pn = rg.next(p);  // past the end: p again (loaded, unused)
@@ -647,7 +659,7 @@ __global__ __launch_bounds__(256) void ffn_up_sk_kernel(
     } else {
       tn = ts;
     }
-    up_load(h0, w1 + tn.wrow, w1 + tn.wrow + I_H, x + tn.xoff, H, (size_t)pn.kc * KUNIT);
+    up_load(h0, w1 + tn.wrow, w1 + tn.wrow + I_H, x + tn.xoff, H, (size_t)pn.kc * KUNIT, tn.xz);
     __builtin_amdgcn_sched_barrier(0);
     up_mma(h1, acc, tw, lane);
     if (rg.ends_tile(p)) tile_end(p.t);
@@ -1050,8 +1062,12 @@ __device__ __forceinline__ void pf_finish(PfTile<NT>& st, const PfRaw<NT>& raw, 
   for (int i = 0; i < PfStage<NT * 16>::PER; ++i) {
     const int n = (tid + PF_THREADS * i) / (PF_K / 8), q = (tid + PF_THREADS * i) % (PF_K / 8);
     int r = raw.r[i];
-    if (UP) r = (r >= 0 && r < nmax) ? r / k : 0;
-    st.voff[i] = n < raw.tc ? (uint32_t)((r * K + q * 8) * 2) : kPadOffset;
+    bool ok = n < raw.tc;
+    if (UP) {  // an expanded index outside [0, T k) gathers a zero row
+      ok = ok && r >= 0 && r < nmax;
+      r = ok ? r / k : 0;
+    }
+    st.voff[i] = ok ? (uint32_t)((r * K + q * 8) * 2) : kPadOffset;
   }
 }
 
@@ -1435,10 +1451,10 @@ hipError_t launch_sk_nt(const uint16_t* x, const int* perm, const int* offsets, 
 }
 }  // namespace
 
-bool ffn_sk_applies(const void* x, const void* w1, const void* w2, int T, int k, int L, int H,
-                    int I) {
+bool ffn_sk_applies(const void* x, const void* w1, const void* w2, const void* out, int T, int k,
+                    int L, int H, int I) {
   auto al = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
-  if (!(al(x) && al(w1) && al(w2))) return false;
+  if (!(al(x) && al(w1) && al(w2) && al(out))) return false;
   if (pick_nt(T, k, L) == 1)
     return H % UP_KUNIT_SHORT == 0 && I % DOWN_KUNIT == 0 && I % UP_ROWS == 0 &&
            H % DOWN_ROWS == 0;
@@ -1470,10 +1486,10 @@ hipError_t launch_grouped_ffn_sk(const uint16_t* x, const int* perm, const int* 
 // FP8 weights (codes + row scales) on the persistent kernels (K-split or
 // staged, by the entries per expert): shapes for which ffn_sk_fp8_applies
 // holds.
-bool ffn_sk_fp8_applies(const void* x, const void* w1q, const void* w2q, int T, int k, int L,
-                        int H, int I) {
+bool ffn_sk_fp8_applies(const void* x, const void* w1q, const void* w2q, const void* out, int T,
+                        int k, int L, int H, int I) {
   auto al = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
-  if (!(al(x) && al(w1q) && al(w2q))) return false;
+  if (!(al(x) && al(w1q) && al(w2q) && al(out))) return false;
   if (pick_nt(T, k, L) == 1)
     return H % UP8_KUNIT == 0 && I % DOWN8_KUNIT == 0 && I % UP_ROWS == 0 && H % DOWN_ROWS == 0;
   // the staged kernels address token rows with 32-bit byte offsets below 2^31

@@ -35,12 +35,14 @@ ROUTING = dict(E=1024, k=8, T=(1, 64, 4096), seed=1003)
 SIGMA_X, SIGMA_WG, SIGMA_W, SIGMA_BIAS, SIGMA_LOGITS = 1.0, 0.1, 0.02, 1.0, 1.0
 
 
-def layer_inputs(cfg, T=None, H=None, I=None, seed=None, first=None, L=None):
+def layer_inputs(cfg, T=None, H=None, I=None, seed=None, first=None, L=None, weights=True):
     """Draw x, W_g, bias, W1, W2 for a workload, optionally at reduced sizes.
 
     Returns a dict of numpy arrays: x [T,H] bf16 bits, wg [E,H] fp32,
     bias [E] fp32 or None, w1 [L,2I,H] bf16 bits (rows [0,I) gate, [I,2I) up),
-    w2 [L,H,I] bf16 bits, plus the scalar shape fields.
+    w2 [L,H,I] bf16 bits, plus the scalar shape fields. weights=False leaves
+    w1 and w2 out (None): x, W_g and the bias do not depend on them, so a
+    larger token batch can reuse expert weights drawn earlier.
     """
     c = dict(cfg)
     if T is not None:
@@ -59,8 +61,8 @@ def layer_inputs(cfg, T=None, H=None, I=None, seed=None, first=None, L=None):
     out["x"] = normal_bf16(sd, X, (T, H), SIGMA_X)
     out["wg"] = normal_f32(sd, WG, (E, H), SIGMA_WG)
     out["bias"] = normal_f32(sd, BIAS, (E,), SIGMA_BIAS) if c.get("bias") else None
-    out["w1"] = normal_bf16(sd, W1, (L, 2 * I, H), SIGMA_W, first_expert=first)
-    out["w2"] = normal_bf16(sd, W2, (L, H, I), SIGMA_W, first_expert=first)
+    out["w1"] = normal_bf16(sd, W1, (L, 2 * I, H), SIGMA_W, first_expert=first) if weights else None
+    out["w2"] = normal_bf16(sd, W2, (L, H, I), SIGMA_W, first_expert=first) if weights else None
     return out
 
 

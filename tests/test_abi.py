@@ -132,3 +132,54 @@ def test_calls_reject_bad_arguments_without_launching():
                              FAKE, None, None, None, FAKE, 256, None) == 3
     assert L.moe_router_logits(FAKE, FAKE, None, 4, 0, 8, FAKE, None, 0, None) == 1
     assert L.moe_router_logits(FAKE, FAKE, None, 100, 64, 8, FAKE, None, 0, None) == 3
+
+
+class _FakeGpuTensor:
+    """Stands in for a torch GPU tensor on the host: the binding's checks read
+    only these attributes, and every case below fails them before any call
+    reaches the library."""
+
+    def __init__(self, shape, esize=4, contiguous=True, cuda=True):
+        self.shape, self._es, self._c, self.is_cuda = tuple(shape), esize, contiguous, cuda
+
+    def dim(self):
+        return len(self.shape)
+
+    def is_contiguous(self):
+        return self._c
+
+    def element_size(self):
+        return self._es
+
+    def numel(self):
+        n = 1
+        for d in self.shape:
+            n *= d
+        return n
+
+    def data_ptr(self):
+        raise AssertionError("a rejected call must not reach the library")
+
+
+def test_binding_rejects_bad_tensors_before_calling():
+    F = _FakeGpuTensor
+    T, E, k = 8, 16, 2
+    lg, ids, w = F((T, E)), F((T, k)), F((T, k))
+    cases = [
+        lambda: moe.route(F((T, E), cuda=False), k, ids, w),          # host tensor
+        lambda: moe.route(F((T, E), contiguous=False), k, ids, w),    # strided view
+        lambda: moe.route(F((T, E), esize=2), k, ids, w),             # 16-bit logits
+        lambda: moe.route(lg, k, F((T, k + 1)), w),                   # wrong shape
+        lambda: moe.permute(ids, E, 0, E, F((E,)), F((E,)), F((T * k,)), F((T * k,)), None),
+        lambda: moe.combine(F((T * k, 64)), F((T * k,)), w, F((T, 64), esize=4)),
+        lambda: moe.grouped_ffn(F((T, 64), esize=2), F((T * k,)), F((4 + 1,)), k,
+                                F((3, 128, 64), esize=2), F((4, 64, 64), esize=2),
+                                F((T * k, 64)), None),                # w1 with too few experts
+        lambda: moe.forward(F((T, 64), esize=2), F((E, 64)), None, F((E, 128, 64), esize=2),
+                            F((E, 64, 64), esize=2), k, 0, E, F((T, 64), esize=2), None,
+                            topk_ids_out=F((T, k + 1))),
+        lambda: moe.router_logits(F((T, 64), esize=2), F((E, 63)), None, lg, None),
+    ]
+    for i, c in enumerate(cases):
+        with pytest.raises(ValueError):
+            c()

@@ -20,6 +20,14 @@ from gpu_util import bf16_to_f64, dev, empty, host, note, sync, torch
 pytestmark = pytest.mark.gpu
 
 
+def pad_rows(perm, n):
+    """permuted_rows as the library takes it: [T * k], the local entries
+    first (positions past them are never read)."""
+    out = np.full(n, -1, np.int32)
+    out[:len(perm)] = perm
+    return out
+
+
 def layer(seed, T, H, I, E, k, first, L):
     x = synth.normal_bf16(seed, synth.X, (T, H), 1.0)
     w1 = synth.normal_bf16(seed, synth.W1, (L, 2 * I, H), 0.02, first_expert=first)
@@ -28,18 +36,20 @@ def layer(seed, T, H, I, E, k, first, L):
     return x, w1, w2, ids
 
 
-def run_ffn(x, perm, offsets, k, w1, w2, x_offset=0):
+def run_ffn(x, perm, offsets, k, w1, w2, x_offset=0, out_offset=0):
     """x_offset > 0 places x at an element offset inside a larger buffer (not
-    16-byte aligned), which takes the checked element-wise path."""
+    16-byte aligned), which takes the checked element-wise path; out_offset
+    does the same for expert_out."""
     t = torch()
     T, H = x.shape
     L = len(offsets) - 1
     I = w2.shape[2]
     xb = dev(np.concatenate([np.zeros(x_offset, np.uint16), x.reshape(-1)]))
     xd = xb[x_offset:].view(T, H)
-    out = t.full((T * k, H), float("nan"), dtype=t.float32, device="cuda:0")
+    ob = t.full((T * k * H + out_offset,), float("nan"), dtype=t.float32, device="cuda:0")
+    out = ob[out_offset:].view(T * k, H)
     ws = moe.alloc_workspace(T, H, I, 1 + L, k, L)
-    pd = dev(perm if len(perm) else np.zeros(1, np.int32))
+    pd = dev(pad_rows(perm, T * k))
     moe.grouped_ffn(xd, pd, dev(offsets), k, dev(w1), dev(w2), out, ws)
     sync()
     return host(out)
@@ -189,3 +199,54 @@ def test_combine(T, E, k, H, first, L):
     assert (np.abs(got - ref) <= 0.5 * ulp + slack).all()
     if L == 0:
         assert (got == 0).all()
+
+
+def test_ffn_checked_path_misaligned_out():
+    """expert_out 4 bytes past a 16-byte boundary: the element-wise path."""
+    note("ffn misaligned expert_out")
+    x, w1, w2, ids = layer(4, 24, 256, 256, 4, 2, 0, 4)
+    _, offsets, perm, _ = oracle.permute(ids, 4, 0, 4)
+    got = run_ffn(x, perm, offsets, 2, w1, w2, out_offset=1)
+    n = offsets[-1]
+    ref = oracle.grouped_ffn(x, perm, offsets, 2, w1, w2)
+    err = np.abs(got[:n].astype(np.float64) - ref)
+    assert err.max() <= 1e-4 * np.abs(ref).max()
+    assert np.isnan(got[n:]).all()
+
+
+# An entry whose expanded index lies outside [0, T k) gathers a zero row on
+# every path: the element-wise kernels (ragged H), the K-split kernels (one
+# 16-token tile per pass) and the staged kernels (token rows in LDS).
+@pytest.mark.parametrize("T,H,I,E,k", [(37, 200, 72, 5, 2), (32, 4096, 1024, 8, 2),
+                                       (256, 512, 512, 8, 2)])
+def test_ffn_out_of_range_rows_are_zero(T, H, I, E, k):
+    note(f"ffn out-of-range rows T={T} H={H} I={I} E={E} k={k}")
+    x, w1, w2, ids = layer(5, T, H, I, E, k, 0, E)
+    _, offsets, perm, _ = oracle.permute(ids, E, 0, E)
+    n = int(offsets[-1])
+    ref = oracle.grouped_ffn(x, perm, offsets, k, w1, w2)
+    bad = [0, n // 2, n - 1]  # first entry of expert 0, a middle one, the last one
+    perm2 = perm.copy()
+    perm2[bad[0]], perm2[bad[1]], perm2[bad[2]] = T * k, -1, T * k + 77
+    got = run_ffn(x, perm2, offsets, k, w1, w2)
+    assert (got[bad] == 0).all()
+    keep = np.setdiff1d(np.arange(n), bad)
+    err = np.abs(got[keep].astype(np.float64) - ref[keep])
+    assert err.max() <= 1e-4 * np.abs(ref).max()
+    assert np.isnan(got[n:]).all()
+
+
+# The fixed order of every sum (in-block wave order, cross-block fixup in
+# block order) makes the output bitwise repeatable, with tiles cut between
+# blocks: the K-split up kernel cut by stream-K, and the staged kernels with a
+# whole round followed by cut tiles.
+@pytest.mark.parametrize("T,H,I,E,k", [(32, 4096, 1024, 8, 2), (40, 4096, 2048, 20, 2),
+                                       (3200, 512, 256, 300, 8)])
+def test_ffn_bitwise_repeatable(T, H, I, E, k):
+    note(f"ffn repeatability T={T} H={H} I={I} E={E} k={k}")
+    x, w1, w2, ids = layer(6, T, H, I, E, k, 0, E)
+    _, offsets, perm, _ = oracle.permute(ids, E, 0, E)
+    n = int(offsets[-1])
+    runs = [run_ffn(x, perm, offsets, k, w1, w2)[:n] for _ in range(3)]
+    for r in runs[1:]:
+        assert np.array_equal(r.view(np.uint32), runs[0].view(np.uint32))

@@ -18,6 +18,14 @@ from gpu_util import dev, host, note, sync, torch
 pytestmark = pytest.mark.gpu
 
 
+def pad_rows(perm, n):
+    """permuted_rows as the library takes it: [T * k], the local entries
+    first (positions past them are never read)."""
+    out = np.full(n, -1, np.int32)
+    out[:len(perm)] = perm
+    return out
+
+
 def layer_fp8(seed, T, H, I, E, k, first, L):
     x = synth.normal_bf16(seed, synth.X, (T, H), 1.0)
     w1q, w1s = synth.fp8_rows(seed, synth.W1, (L, 2 * I, H), 0.02, first_expert=first)
@@ -32,7 +40,7 @@ def run_ffn_fp8(x, perm, offsets, k, w1q, w1s, w2q, w2s):
     L = len(offsets) - 1
     out = t.full((T * k, H), float("nan"), dtype=t.float32, device="cuda:0")
     ws = moe.alloc_workspace(T, H, w2q.shape[2], 1 + L, k, L)
-    pd = dev(perm if len(perm) else np.zeros(1, np.int32))
+    pd = dev(pad_rows(perm, T * k))
     moe.grouped_ffn_fp8(dev(x), pd, dev(offsets), k, dev(w1q), dev(w1s), dev(w2q), dev(w2s), out,
                         ws)
     sync()
