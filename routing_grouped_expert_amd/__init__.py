@@ -46,13 +46,23 @@ _SIGS = {
                     ctypes.c_int),
     "moe_forward_fp8": ([_VP] * 7 + [_I32] * 7 + [_VP, _VP, _VP, _VP, _VP, _SZ, _VP],
                         ctypes.c_int),
+    "moe_forward_no_alloc": ([_VP, _VP, _VP, _VP, _VP] + [_I32] * 7 + [_VP, _VP, _VP, _VP, _VP],
+                             ctypes.c_int),
 }
+
+NO_ALLOC_SCRATCH_BYTES = 128 << 20
 
 
 def lib():
-    """Load libmoe.so (built in place by routing_grouped_expert_amd.build)."""
+    """Load libmoe.so (built in place by routing_grouped_expert_amd.build).
+
+    torch is imported first: it carries its own HIP runtime under the same
+    soname as the system one that libmoe.so names, and whichever is loaded
+    first serves the whole process. Loading the library first would hand
+    torch a runtime it was not built against (it then finds no GPU)."""
     global _lib
     if _lib is None:
+        import torch  # noqa: F401  (see above)
         if not os.path.exists(LIB_PATH):
             from . import build
             build.build()
@@ -260,6 +270,22 @@ def forward_fp8(x, w_gate, router_bias, w1q, w1s, w2q, w2s, k, first_expert, num
         _ptr(x), _ptr(w_gate), _ptr(router_bias), _ptr(w1q), _ptr(w1s), _ptr(w2q), _ptr(w2s), T,
         H, I, E, k, first_expert, num_local, _ptr(y), _ptr(logits_out), _ptr(topk_ids_out),
         _ptr(topk_weights_out), _ptr(ws), nws, _stream(stream)))
+
+
+def forward_no_alloc(x, w_gate, router_bias, w1, w2, k, first_expert, num_local, y,
+                     logits_out=None, topk_ids_out=None, topk_weights_out=None, stream=None):
+    """moe_forward_no_alloc: the layer on the library's own device scratch
+    (no workspace argument; sizes whose workspace exceeds
+    NO_ALLOC_SCRATCH_BYTES are rejected)."""
+    T, H, E = _forward_common(x, w_gate, router_bias, k, y, logits_out, topk_ids_out,
+                              topk_weights_out)
+    I = _dims(w2, "w2", 3)[2]
+    _need(w1, "w1", (num_local, 2 * I, H), 2)
+    _need(w2, "w2", (num_local, H, I), 2)
+    _check("moe_forward_no_alloc", lib().moe_forward_no_alloc(
+        _ptr(x), _ptr(w_gate), _ptr(router_bias), _ptr(w1), _ptr(w2), T, H, I, E, k,
+        first_expert, num_local, _ptr(y), _ptr(logits_out), _ptr(topk_ids_out),
+        _ptr(topk_weights_out), _stream(stream)))
 
 
 def alloc_workspace(T, H, I, E, k, num_local, device="cuda"):

@@ -183,3 +183,21 @@ def test_binding_rejects_bad_tensors_before_calling():
     for i, c in enumerate(cases):
         with pytest.raises(ValueError):
             c()
+
+
+def test_library_shares_torchs_hip_runtime():
+    """Loading the library imports torch first, so the process holds one HIP
+    runtime (torch's) and libmoe.so binds to it."""
+    import subprocess
+    import sys
+    code = ("import routing_grouped_expert_amd as m, sys; m.lib(); "
+            "import torch, os; "
+            "maps = open('/proc/self/maps').read(); "
+            "paths = {l.split()[-1] for l in maps.splitlines() if 'libamdhip64' in l}; "
+            "print(len(paths), sorted(paths))")
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True,
+                         cwd=os.path.dirname(os.path.dirname(moe.LIB_PATH)), timeout=300)
+    assert out.returncode == 0, out.stderr
+    n = int(out.stdout.split()[0])
+    assert n == 1, out.stdout
+    assert "torch" in out.stdout, out.stdout
