@@ -38,9 +38,9 @@
  *  - Limits: 1 <= E <= 4096, 1 <= k <= min(E, 32), H >= 1, I >= 1,
  *    T * k < 2^31, T * k * max(H, I) < 2^31 elements.
  *  - Fast path: 16-byte aligned x / w1 / w2 / expert_out / workspace and H, I
- *    multiples of 128. Any other shape or alignment runs a correct element-wise path
- *    instead of failing ([P-ACT] section 1: the 128-bit vector gather keeps a
- *    scalar fallback for unaligned inputs).
+ *    multiples of 128. Any other shape or alignment runs a correct
+ *    element-wise path instead of failing ([P-ACT] section 1: the 128-bit
+ *    vector gather keeps a scalar fallback for unaligned inputs).
  */
 #ifndef MOE_H
 #define MOE_H
@@ -235,6 +235,35 @@ moe_status moe_forward_fp8(const uint16_t* x, const float* w_gate, const float* 
                            int32_t k, int32_t first_expert, int32_t num_local, uint16_t* y,
                            float* logits_out, int32_t* topk_ids_out, float* topk_weights_out,
                            void* ws, size_t ws_bytes, void* stream);
+
+/* Size of the device scratch array behind moe_forward_no_alloc (bytes). */
+#define MOE_NO_ALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+
+/*
+ * moe_forward_no_alloc -- moe_forward without a workspace argument, for
+ * callers that cannot allocate device memory (code under stream capture,
+ * tight serving loops, hosts that forbid allocation). The workspace is a
+ * device array of MOE_NO_ALLOC_SCRATCH_BYTES inside the library; each GPU
+ * holds its own copy from the first call on it until the process ends. No
+ * call allocates or frees memory.
+ *   Every argument, output and error is as for moe_forward, plus:
+ *   MOE_ERROR_WORKSPACE when moe_workspace_size for these sizes exceeds
+ *   MOE_NO_ALLOC_SCRATCH_BYTES (128 MiB): decode-shaped layers (8.5 MiB at
+ *   T 32, H 4096, I 14336, 8 experts, top-2) fit; shapes with more than
+ *   about 16 entries per expert, whose FFN stages token rows in LDS and keeps
+ *   ~130 MiB of cross-block partial sums, do not.
+ *   MOE_ERROR_LAUNCH when the array's device address cannot be obtained.
+ * Every call on one GPU uses that GPU's one array: calls that overlap on the
+ * same GPU (concurrent streams or host threads) race and must be ordered by
+ * the caller. The array keeps the last call's contents; every value a call
+ * reads from it is written earlier in the same call.
+ */
+moe_status moe_forward_no_alloc(const uint16_t* x, const float* w_gate,
+                                const float* router_bias, const uint16_t* w1,
+                                const uint16_t* w2, int32_t T, int32_t H, int32_t I, int32_t E,
+                                int32_t k, int32_t first_expert, int32_t num_local, uint16_t* y,
+                                float* logits_out, int32_t* topk_ids_out,
+                                float* topk_weights_out, void* stream);
 
 #ifdef __cplusplus
 }

@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <mutex>
 
 namespace moe {
 size_t router_workspace_bytes(int T, int H, int E);
@@ -145,6 +146,42 @@ moe_status forward_layer(const uint16_t* x, const float* w_gate, const float* ro
   if (err == hipSuccess && num_local > 0) err = ffn(perm, offsets, eo, base + lo.ffn_ws, s);
   if (err == hipSuccess) err = moe::launch_combine(eo, e2p, wts, T, k, H, y, s);
   return launched(err);
+}
+
+// ---- scratch for moe_forward_no_alloc ---------------------------------
+// A file-scope device array that stands in for the workspace of callers that
+// cannot allocate. Each GPU the library runs on holds its own copy until the
+// process ends. In host code `scratch` names a host-side stand-in, not the
+// device memory: its device address is taken once per device with
+// hipGetSymbolAddress (with that device current) and only that address is
+// ever handed to kernels.
+static __device__ __align__(256) unsigned char scratch[MOE_NO_ALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch array (nullptr on failure;
+// *err then holds the HIP error).
+void* scratch_address(hipError_t* err) {
+  int dev = 0;
+  *err = hipGetDevice(&dev);
+  if (*err != hipSuccess) return nullptr;
+  if (dev < 0 || dev >= kMaxDevices) {
+    *err = hipErrorInvalidDevice;
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    *err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (*err != hipSuccess || !p) {
+      if (*err == hipSuccess) *err = hipErrorInvalidSymbol;
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  return g_scratch_ptr[dev];
 }
 
 }  // namespace
@@ -311,6 +348,30 @@ moe_status moe_forward_fp8(const uint16_t* x, const float* w_gate, const float* 
         return moe::launch_grouped_ffn_fp8(x, perm, offsets, num_local, T, k, H, I, w1q, w1s, w2q,
                                            w2s, eo, fws, s);
       });
+}
+
+moe_status moe_forward_no_alloc(const uint16_t* x, const float* w_gate,
+                                const float* router_bias, const uint16_t* w1,
+                                const uint16_t* w2, int32_t T, int32_t H, int32_t I, int32_t E,
+                                int32_t k, int32_t first_expert, int32_t num_local, uint16_t* y,
+                                float* logits_out, int32_t* topk_ids_out,
+                                float* topk_weights_out, void* stream) {
+  moe_status st = check_common(T, E, k);
+  if (st == MOE_SUCCESS) st = check_share(E, first_expert, num_local);
+  if (st == MOE_SUCCESS) st = check_dims(T, k, H, I);
+  if (st != MOE_SUCCESS) return st;
+  if (T == 0) return MOE_SUCCESS;
+  if (layout(T, H, I, E, k, num_local).total > MOE_NO_ALLOC_SCRATCH_BYTES)
+    return MOE_ERROR_WORKSPACE;
+  hipError_t err = hipSuccess;
+  void* ws = scratch_address(&err);
+  if (!ws) {
+    t_last_launch_error = err;
+    return MOE_ERROR_LAUNCH;
+  }
+  return moe_forward(x, w_gate, router_bias, w1, w2, T, H, I, E, k, first_expert, num_local, y,
+                     logits_out, topk_ids_out, topk_weights_out, ws, MOE_NO_ALLOC_SCRATCH_BYTES,
+                     stream);
 }
 
 }  // extern "C"
