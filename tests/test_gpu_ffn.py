@@ -250,3 +250,48 @@ def test_ffn_bitwise_repeatable(T, H, I, E, k):
     runs = [run_ffn(x, perm, offsets, k, w1, w2)[:n] for _ in range(3)]
     for r in runs[1:]:
         assert np.array_equal(r.view(np.uint32), runs[0].view(np.uint32))
+
+
+def sampled_entries(offsets, n_tiles):
+    """Entries at the edges of passes and 16-token tiles: for the first,
+    middle and last experts with entries, positions 0, 15, 16, 31, 32, the
+    last entry of each pass of NT tiles and the expert's last entry."""
+    L = len(offsets) - 1
+    cnt = np.diff(offsets)
+    with_rows = np.flatnonzero(cnt)
+    picks = set()
+    for e in {with_rows[0], with_rows[len(with_rows) // 2], with_rows[-1],
+              int(np.argmax(cnt))}:
+        b, c = int(offsets[e]), int(cnt[e])
+        for q in (0, 15, 16, 31, 32, 16 * n_tiles - 1, 16 * n_tiles, c - 1):
+            if q < c:
+                picks.add(b + q)
+    return sorted(picks)
+
+
+@pytest.mark.parametrize("name,skew", [("fine", False), ("share0", True)])
+def test_ffn_full_size_sampled(name, skew):
+    """The grouped FFN alone at the fine-grained and share-0 sizes (staged
+    kernels with 4 and 8 token tiles per pass), bench.py's launch
+    configuration: every output row of entries at pass and tile edges against
+    the oracle's single-entry FFN. share0 adds an expert chosen by 300 tokens
+    (three passes)."""
+    from synth import configs
+    d = configs.layer_inputs(configs.WORKLOADS[name])
+    T, H, I, E, k, first, L = (d[n] for n in ("T", "H", "I", "E", "k", "first", "L"))
+    note(f"ffn full size {name} T={T} H={H} I={I} E={E} k={k} share=({first},{L})")
+    ids = synth.topk_ids(d["seed"], synth.IDS, T, E, k)
+    if skew:
+        for t in range(300):
+            if first not in ids[t]:
+                ids[t, k - 1] = first
+    _, offsets, perm, _ = oracle.permute(ids, E, first, L)
+    got = run_ffn(d["x"], perm, offsets, k, d["w1"], d["w2"])
+    n = int(offsets[-1])
+    assert np.isnan(got[n:]).all()
+    nt = 4 if name == "fine" else 8
+    for p in sampled_entries(offsets, nt):
+        e = int(np.searchsorted(offsets, p, side="right") - 1)
+        ref = oracle.expert_row(d["x"][perm[p] // k], d["w1"][e], d["w2"][e])
+        err = np.abs(got[p].astype(np.float64) - ref)
+        assert err.max() <= 1e-4 * np.abs(ref).max(), (p, err.max() / np.abs(ref).max())

@@ -86,12 +86,75 @@ def test_forward_shares_sum_to_whole_layer():
     assert err.mean() <= 2e-3 * np.abs(y_full).mean() * 3
 
 
-@pytest.mark.parametrize("name", ["decode", "fine", "share0"])
-def test_forward_full_size_sampled(name):
+@pytest.mark.parametrize("name,n_sample", [("decode", 32), ("fine", 128), ("share0", 256)])
+def test_forward_full_size_sampled(name, n_sample):
+    """The full workload in the launch configuration bench.py times: every
+    token's routing, and the outputs of n_sample tokens spread over the batch
+    (every token at decode size)."""
     cfg = configs.WORKLOADS[name]
     assert moe.partition(cfg["E"], cfg["S"], cfg["s"]) == (cfg["first"], cfg["L"])
     d = configs.layer_inputs(cfg)
     T = d["T"]
-    sample = np.unique(np.array([0, 1, T // 3, T // 2, T - 2, T - 1, 7 % T, (5 * T) // 7],
-                                np.int32))
+    sample = np.unique(np.concatenate([np.linspace(0, T - 1, n_sample).astype(np.int32),
+                                       np.array([1, T - 2], np.int32)]))
     check_forward(d, sample=sample, what=name + " full size")
+
+
+def test_forward_mfma_probe_sampled():
+    """The MFMA-bound probe bench.py times: the share-0 expert weights with
+    T = 32768 tokens (~683 entries per local expert). The GPU runs the whole
+    batch; a token's logits, routing and output depend on that token alone, so
+    256 sampled tokens are checked against the oracle run on those tokens."""
+    cfg = configs.WORKLOADS["share0"]
+    T = 32768
+    d = configs.layer_inputs(cfg, T=T)
+    note(f"forward mfma probe T={T} H={d['H']} I={d['I']} E={d['E']} k={d['k']} "
+         f"share=({d['first']},{d['L']})")
+    y, lg, ids, w = gpu_forward(d)
+    sample = np.linspace(0, T - 1, 256).astype(np.int32)
+    rlg, rids, rw, ry = oracle.forward(d["x"][sample], d["wg"], d["w1"], d["w2"], d["k"],
+                                       d["first"], d["L"], d["bias"])
+    assert (np.abs(lg[sample].astype(np.float64) - rlg) <= np.spacing(np.abs(rlg))).all()
+    assert np.array_equal(ids[sample], rids)
+    assert np.abs(w[sample] - rw).max() <= W_TOL
+    assert_layer_ok(y[sample], ry, "mfma probe")
+
+
+def structured_inputs(kind, T=256, H=512, I=256, E=16, k=4, seed=41):
+    """Inputs whose routing is fixed by construction. shared: every token
+    picks experts 0..k-1 (a router bias of 10 - e on them over tiny logits);
+    disjoint: token t picks experts (t k + j) mod E, by a one-hot column per
+    token in the last T columns of x and W_g rows that read it."""
+    import synth
+    cfg = dict(configs.WORKLOADS["share0"], E=E, k=k, first=0, L=E, S=1, s=0, bias=False)
+    d = configs.layer_inputs(cfg, T=T, H=H, I=I, seed=seed)
+    if kind == "shared":
+        d["wg"] = (d["wg"] * 1e-3).astype(np.float32)
+        b = np.zeros(E, np.float32)
+        b[:k] = 10.0 - np.arange(k, dtype=np.float32)
+        d["bias"] = b
+    else:
+        assert H > T
+        x = d["x"].copy()
+        x[:, H - T:] = 0
+        x[np.arange(T), H - T + np.arange(T)] = synth.f32_to_bf16(np.array([8.0], np.float32))[0]
+        wg = np.zeros((E, H), np.float32)
+        for t in range(T):
+            for j in range(k):
+                wg[(t * k + j) % E, H - T + t] = 1.0 - 0.125 * j  # slot order j
+        d["x"], d["wg"] = x, wg
+    return d
+
+
+@pytest.mark.parametrize("kind", ["shared", "disjoint"])
+def test_forward_structured_routing(kind):
+    """The two routing regimes the pages measure: all tokens on the same
+    experts (4 experts of 256 entries: two staged passes each), and tokens
+    spread evenly over all experts."""
+    d = structured_inputs(kind)
+    T, k, E = d["T"], d["k"], d["E"]
+    want = (np.tile(np.arange(k), (T, 1)) if kind == "shared"
+            else (np.arange(T)[:, None] * k + np.arange(k)[None, :]) % E)
+    check_forward(d, what=kind + " routing")
+    _, _, gids, _ = gpu_forward(d)
+    assert np.array_equal(gids, want.astype(np.int32))
