@@ -60,6 +60,8 @@ def parse_args():
                     help="instead of the layer step: route + permute microseconds over "
                          "T in {1, 64, 4096} x E in {8 .. 4096}, k = 8 (k = E below 8), warm and "
                          "with the caches flushed before each call; one JSON line")
+    ap.add_argument("--routing-only", action="store_true",
+                    help="only the routing timings at 1024 experts (one JSON line)")
     ap.add_argument("--probe-only", action="store_true",
                     help="only the MFMA probe (share-0 weights, T=32768), for counter runs")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -340,14 +342,16 @@ def hbm_probe(torch, stream):
 
 
 def routing_timings(torch):
-    """Route + permute at E = 1024, k = 8, T = 1 / 64 / 4096, microseconds per
-    call pair: `graph` replays 200 captured pairs (each replay checked against
-    the eager outputs), `eager` issues 200 pairs from Python back to back."""
+    """Routing (selection, weights, histogram, scan, permutation) at E = 1024,
+    k = 8, T = 1 / 64 / 4096 through moe_route_permute, microseconds per call:
+    `graph` replays 200 captured calls (each replay checked against the eager
+    outputs), `eager` issues 200 calls from Python back to back, `separate`
+    replays 200 captured moe_route + moe_permute pairs."""
     import routing_grouped_expert_amd as moe
     from synth import configs
 
     Er, kr = configs.ROUTING["E"], configs.ROUTING["k"]
-    out = {"graph": {}, "eager": {}}
+    out = {"graph": {}, "eager": {}, "separate": {}}
     n_it = 200
     for Tr in configs.ROUTING["T"]:
         lg = torch.from_numpy(configs.routing_logits(Tr)).to("cuda:0")
@@ -360,6 +364,10 @@ def routing_timings(torch):
         rws = moe.alloc_workspace(Tr, 128, 128, Er, kr, Er)
 
         def pair(s=None, b=bufs):
+            moe.route_permute(lg, kr, 0, Er, b["ri"], b["rw"], b["rc"], b["ro"], b["rp"], b["re"],
+                              rws, s)
+
+        def separate(s=None, b=bufs):
             moe.route(lg, kr, b["ri"], b["rw"], s)
             moe.permute(b["ri"], Er, 0, Er, b["rc"], b["ro"], b["rp"], b["re"], rws, s)
 
@@ -376,29 +384,30 @@ def routing_timings(torch):
         torch.cuda.synchronize()
         out["eager"][f"T{Tr}"] = round(a.elapsed_time(b) / n_it * 1e3, 2)
 
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for _ in range(n_it):
-                pair(None)
-        reps = []
-        for _ in range(3):
-            for t in bufs.values():
-                t.fill_(-7)
-            torch.cuda.synchronize()
-            a.record(stream)
-            g.replay()
-            b.record(stream)
-            torch.cuda.synchronize()
-            reps.append(a.elapsed_time(b) / n_it * 1e3)
-            for n, t in bufs.items():
-                if n == "rp":  # positions past the local entries are not written
-                    nl = int(ref["ro"][-1])
-                    ok = torch.equal(t[:nl], ref[n][:nl])
-                else:
-                    ok = torch.equal(t, ref[n])
-                assert ok, f"graph replay of routing T={Tr}: {n} differs from the eager result"
-        out["graph"][f"T{Tr}"] = round(float(np.median(reps)), 2)
-        del g
+        for key, fn in (("graph", pair), ("separate", separate)):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for _ in range(n_it):
+                    fn(None)
+            reps = []
+            for _ in range(3):
+                for t in bufs.values():
+                    t.fill_(-7)
+                torch.cuda.synchronize()
+                a.record(stream)
+                g.replay()
+                b.record(stream)
+                torch.cuda.synchronize()
+                reps.append(a.elapsed_time(b) / n_it * 1e3)
+                for n, t in bufs.items():
+                    if n == "rp":  # positions past the local entries are not written
+                        nl = int(ref["ro"][-1])
+                        ok = torch.equal(t[:nl], ref[n][:nl])
+                    else:
+                        ok = torch.equal(t, ref[n])
+                    assert ok, f"graph replay of routing T={Tr} ({key}): {n} differs from eager"
+            out[key][f"T{Tr}"] = round(float(np.median(reps)), 2)
+            del g
     return out
 
 
@@ -458,58 +467,69 @@ def mfma_probe(torch, base, steps):
 
 
 def routing_sweep():
-    """Cost table of the routing steps (route + permute) over token counts and
-    expert counts: median microseconds per call, warm (inputs cached) and cold
-    (a 512 MiB buffer written between calls, so logits and ids come from HBM)."""
+    """Cost table of the routing variants (selection + permutation through
+    moe_route_permute_variant) over token counts and expert counts:
+    microseconds per call from a replayed graph of 50 back-to-back calls
+    (median of 3 replays), for every variant that applies to the cell, the
+    outputs of all variants checked equal, and the variant the plan picks."""
     import torch
 
     import routing_grouped_expert_amd as moe
     from synth import configs
 
     dev = torch.device("cuda:0")
-    stream = torch.cuda.current_stream()
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
     table = []
+    n_it = 50
     for E in (8, 16, 32, 64, 128, 256, 512, 1024, 2048, 4096):
         k = min(8, E)
-        for T in (1, 64, 4096):
+        for T in (1, 4, 16, 64, 256, 1024, 4096):
             lg = torch.from_numpy(configs.routing_logits(T, E=E)).to(dev)
-            ids = torch.empty((T, k), dtype=torch.int32, device=dev)
-            wts = torch.empty((T, k), dtype=torch.float32, device=dev)
-            cnt = torch.empty((E,), dtype=torch.int32, device=dev)
-            off = torch.empty((E + 1,), dtype=torch.int32, device=dev)
-            perm = torch.empty((T * k,), dtype=torch.int32, device=dev)
-            e2p = torch.empty((T * k,), dtype=torch.int32, device=dev)
+            bufs = [torch.empty((T, k), dtype=torch.int32, device=dev),
+                    torch.empty((T, k), dtype=torch.float32, device=dev),
+                    torch.empty((E,), dtype=torch.int32, device=dev),
+                    torch.empty((E + 1,), dtype=torch.int32, device=dev),
+                    torch.empty((T * k,), dtype=torch.int32, device=dev),
+                    torch.empty((T * k,), dtype=torch.int32, device=dev)]
             ws = moe.alloc_workspace(T, 128, 128, E, k, E)
-
-            def call():
-                moe.route(lg, k, ids, wts, stream)
-                moe.permute(ids, E, 0, E, cnt, off, perm, e2p, ws, stream)
-
-            res = {}
-            for mode in ("warm", "cold"):
-                for _ in range(5):
-                    call()
-                times = []
-                for _ in range(50):
-                    if mode == "cold":
-                        flush.fill_(1)
+            row = {"E": E, "T": T, "k": k, "plan": moe.routing_plan(T, E, k, E), "us": {}}
+            ref = None
+            for v in ("one_block", "two_kernels", "tiled"):
+                try:
+                    moe.route_permute(lg, k, 0, E, *bufs, ws, variant=v)
+                except moe.MoeError as exc:
+                    if exc.status != 2:
+                        raise
+                    continue
+                torch.cuda.synchronize()
+                out = [b.clone() for b in bufs]
+                nl = int(out[3][-1])
+                out[4] = out[4][:nl]
+                if ref is None:
+                    ref = out
+                else:
+                    assert all(torch.equal(a, b) for a, b in zip(out, ref)), (E, T, v)
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    for _ in range(n_it):
+                        moe.route_permute(lg, k, 0, E, *bufs, ws, variant=v)
+                reps = []
+                for _ in range(3):
                     a = torch.cuda.Event(enable_timing=True)
                     b = torch.cuda.Event(enable_timing=True)
-                    a.record(stream)
-                    call()
-                    b.record(stream)
-                    times.append((a, b))
-                torch.cuda.synchronize()
-                us = sorted(a.elapsed_time(b) * 1e3 for a, b in times)
-                res[mode] = {"median": round(us[25], 2), "p10": round(us[5], 2),
-                             "p90": round(us[45], 2)}
-            table.append({"E": E, "T": T, "k": k, **res})
-            print(f"E {E:5d} T {T:5d} k {k}: warm {res['warm']['median']:7.2f} us  "
-                  f"cold {res['cold']['median']:7.2f} us", file=sys.stderr, flush=True)
-    print(json.dumps({"metric": "route + permute microseconds per call", "unit": "us",
-                      "higher_is_better": False, "data": "synthetic (seeded N(0,1) logits)",
-                      "table": table}))
+                    a.record()
+                    g.replay()
+                    b.record()
+                    torch.cuda.synchronize()
+                    reps.append(a.elapsed_time(b) / n_it * 1e3)
+                del g
+                row["us"][v] = round(float(np.median(reps)), 2)
+            row["best"] = min(row["us"], key=row["us"].get)
+            table.append(row)
+            print(f"E {E:5d} T {T:5d}: " + "  ".join(f"{v} {u:7.2f}" for v, u in row["us"].items())
+                  + f"   plan {row['plan']}", file=sys.stderr, flush=True)
+    print(json.dumps({"metric": "routing (selection + permutation) microseconds per call",
+                      "unit": "us", "higher_is_better": False,
+                      "data": "synthetic (seeded N(0,1) logits)", "table": table}))
 
 
 def main():
@@ -524,6 +544,12 @@ def main():
 
     import torch
     fp8 = args.weights == "fp8"
+    if args.routing_only:
+        r = routing_timings(torch)
+        print(json.dumps({"routing_us_1024_experts": r["graph"],
+                          "routing_us_1024_experts_eager": r["eager"],
+                          "routing_us_1024_experts_separate_calls": r["separate"]}))
+        return
     if args.probe_only:
         base = Layer("share0", fp8=False)
         print(json.dumps({"mfma_probe": mfma_probe(torch, base, args.steps)}))
@@ -595,6 +621,7 @@ def main():
         "call_ms": head["call_ms"],
         "routing_us_1024_experts": None if routing is None else routing["graph"],
         "routing_us_1024_experts_eager": None if routing is None else routing["eager"],
+        "routing_us_1024_experts_separate_calls": None if routing is None else routing["separate"],
     }
     for name, e in extras.items():
         out[name] = e

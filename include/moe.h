@@ -80,11 +80,12 @@ moe_status moe_partition(int32_t num_experts, int32_t num_shares, int32_t share,
 
 /*
  * moe_workspace_size -- bytes of device workspace that moe_forward needs
- * (*bytes, HOST pointer). moe_router_logits, moe_permute and moe_grouped_ffn
- * need no more than this for the same sizes, so one workspace serves every
- * call. The workspace
- * must be 256-byte aligned. Its contents need no initialisation and are
- * scratch after the call.
+ * (*bytes, HOST pointer); the caller allocates it and passes it in ([P-FP4]
+ * section 2: the caller provides the workspace and output buffers).
+ * moe_router_logits, moe_permute, moe_route_permute and moe_grouped_ffn need
+ * no more than this for the same sizes, so one workspace serves every call.
+ * The workspace must be 256-byte aligned. Its contents need no
+ * initialisation and are scratch after the call.
  */
 moe_status moe_workspace_size(int32_t T, int32_t H, int32_t I, int32_t E, int32_t k,
                               int32_t num_local, size_t* bytes);
@@ -141,6 +142,65 @@ moe_status moe_permute(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E,
                        int32_t first_expert, int32_t num_local, int32_t* expert_counts,
                        int32_t* expert_offsets, int32_t* permuted_rows,
                        int32_t* expanded_to_permuted, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * moe_route_permute -- moe_route, then moe_permute on its topk_ids: the
+ * routing steps of the layer in one call (the routing kernel of [P-ROUTE]
+ * emits the routing indices that the permutation consumes), in the variant
+ * moe_routing_plan names for these sizes. Arguments, outputs and errors are
+ * those of moe_route and moe_permute; the workspace is moe_permute's
+ * (moe_workspace_size covers it). Every variant gives identical outputs.
+ */
+moe_status moe_route_permute(const float* logits, int32_t T, int32_t E, int32_t k,
+                             int32_t first_expert, int32_t num_local, int32_t* topk_ids,
+                             float* topk_weights, int32_t* expert_counts, int32_t* expert_offsets,
+                             int32_t* permuted_rows, int32_t* expanded_to_permuted, void* ws,
+                             size_t ws_bytes, void* stream);
+
+/*
+ * Routing variants: how the selection and the permutation are split into
+ * kernels ([P-ROUTE] section 1: the launch shape follows the token count;
+ * section 2: the valid shapes are fixed ahead of time).
+ *   MOE_ROUTING_ONE_BLOCK   T <= 64: one single-block kernel selects and
+ *                           permutes in on-chip memory (one launch; the
+ *                           selection runs on one compute unit).
+ *   MOE_ROUTING_TWO_KERNELS a selection kernel (one wave per token), then a
+ *                           single-block permutation; while every 64-token
+ *                           tile's masks and bases fit in one block's LDS.
+ *   MOE_ROUTING_TILED       the selection kernel also writes per-tile token
+ *                           masks, then a scan kernel and a scatter kernel;
+ *                           any T.
+ */
+typedef enum moe_routing_variant {
+  MOE_ROUTING_AUTO = 0,
+  MOE_ROUTING_ONE_BLOCK = 1,
+  MOE_ROUTING_TWO_KERNELS = 2,
+  MOE_ROUTING_TILED = 3
+} moe_routing_variant;
+
+/*
+ * moe_routing_plan -- the variant moe_route_permute and moe_forward run for
+ * T tokens, E experts, top-k and a share of num_local experts (*variant,
+ * HOST pointer): the applicable variant with the smallest time predicted by
+ * a cost model fitted to the variants' measured times ([P-VSA]'s planner
+ * likewise picks a kernel configuration from a cost estimate). Pure host
+ * function. Errors as moe_route.
+ */
+moe_status moe_routing_plan(int32_t T, int32_t E, int32_t k, int32_t num_local,
+                            int32_t* variant);
+
+/*
+ * moe_route_permute_variant -- moe_route_permute in a given variant (a
+ * moe_routing_variant; MOE_ROUTING_AUTO = the plan), for measurement and
+ * testing. MOE_ERROR_UNSUPPORTED when the variant does not apply to these
+ * sizes; otherwise as moe_route_permute.
+ */
+moe_status moe_route_permute_variant(const float* logits, int32_t T, int32_t E, int32_t k,
+                                     int32_t first_expert, int32_t num_local, int32_t* topk_ids,
+                                     float* topk_weights, int32_t* expert_counts,
+                                     int32_t* expert_offsets, int32_t* permuted_rows,
+                                     int32_t* expanded_to_permuted, void* ws, size_t ws_bytes,
+                                     int32_t variant, void* stream);
 
 /*
  * moe_grouped_ffn -- for every local entry p of local expert i:
@@ -202,10 +262,12 @@ moe_status moe_combine(const float* expert_out, const int32_t* expanded_to_permu
 
 /*
  * moe_forward -- the whole layer on one GPU for one expert share:
- * moe_router_logits -> moe_route -> moe_permute -> moe_grouped_ffn ->
- * moe_combine, stream-ordered, with no host synchronisation in between.
- * Selections of experts outside the share are masked after renormalisation,
- * so the outputs of all shares add up to the whole layer.
+ * moe_router_logits -> moe_route_permute -> moe_grouped_ffn -> moe_combine,
+ * stream-ordered, with no host synchronisation in between. The share is the
+ * contiguous expert range of the ceil/floor partition ([P-A2A] section 1;
+ * moe_partition); selections of experts outside it are masked after
+ * renormalisation (the non-local members of [P-ACT] section 1 carry a
+ * negative index), so the outputs of all shares add up to the whole layer.
  *   x [T, H] bf16; w_gate [E, H] fp32; router_bias [E] fp32 or NULL;
  *   w1 [num_local, 2I, H] bf16; w2 [num_local, H, I] bf16 (local experts)
  *   y [T, H] bf16 (output)

@@ -37,6 +37,11 @@ _SIGS = {
     "moe_route": ([_VP, _I32, _I32, _I32, _VP, _VP, _VP], ctypes.c_int),
     "moe_permute": ([_VP, _I32, _I32, _I32, _I32, _I32, _VP, _VP, _VP, _VP, _VP, _SZ, _VP],
                     ctypes.c_int),
+    "moe_route_permute": ([_VP, _I32, _I32, _I32, _I32, _I32] + [_VP] * 7 + [_SZ, _VP],
+                          ctypes.c_int),
+    "moe_route_permute_variant": ([_VP, _I32, _I32, _I32, _I32, _I32] + [_VP] * 7 +
+                                  [_SZ, _I32, _VP], ctypes.c_int),
+    "moe_routing_plan": ([_I32, _I32, _I32, _I32, ctypes.POINTER(_I32)], ctypes.c_int),
     "moe_grouped_ffn": ([_VP, _VP, _VP, _I32, _I32, _I32, _I32, _I32, _VP, _VP, _VP, _VP, _SZ,
                          _VP], ctypes.c_int),
     "moe_grouped_ffn_fp8": ([_VP, _VP, _VP, _I32, _I32, _I32, _I32, _I32, _VP, _VP, _VP, _VP, _VP,
@@ -177,6 +182,42 @@ def permute(topk_ids, num_experts, first_expert, num_local, expert_counts, exper
         _ptr(topk_ids), T, k, num_experts, first_expert, num_local, _ptr(expert_counts),
         _ptr(expert_offsets), _ptr(permuted_rows), _ptr(expanded_to_permuted), _ptr(ws), nws,
         _stream(stream)))
+
+
+ROUTING_VARIANTS = {"auto": 0, "one_block": 1, "two_kernels": 2, "tiled": 3}
+
+
+def routing_plan(T, E, k, num_local):
+    """Name of the routing variant moe_route_permute runs for these sizes."""
+    v = _I32()
+    _check("moe_routing_plan", lib().moe_routing_plan(T, E, k, num_local, ctypes.byref(v)))
+    return {c: n for n, c in ROUTING_VARIANTS.items()}[v.value]
+
+
+def route_permute(logits, k, first_expert, num_local, topk_ids, topk_weights, expert_counts,
+                  expert_offsets, permuted_rows, expanded_to_permuted, ws, stream=None,
+                  variant="auto"):
+    """moe_route_permute: routing then the permutation, in one call (variant:
+    a key of ROUTING_VARIANTS; "auto" is the plan)."""
+    T, E = _dims(logits, "logits", 2)
+    _need(logits, "logits", (T, E), 4)
+    _need(topk_ids, "topk_ids", (T, k), 4)
+    _need(topk_weights, "topk_weights", (T, k), 4)
+    _need(expert_counts, "expert_counts", (E,), 4)
+    _need(expert_offsets, "expert_offsets", (num_local + 1,), 4)
+    _need(permuted_rows, "permuted_rows", (T * k,), 4)
+    _need(expanded_to_permuted, "expanded_to_permuted", (T * k,), 4)
+    nws = _need_ws(ws)
+    if variant == "auto":
+        _check("moe_route_permute", lib().moe_route_permute(
+            _ptr(logits), T, E, k, first_expert, num_local, _ptr(topk_ids), _ptr(topk_weights),
+            _ptr(expert_counts), _ptr(expert_offsets), _ptr(permuted_rows),
+            _ptr(expanded_to_permuted), _ptr(ws), nws, _stream(stream)))
+        return
+    _check("moe_route_permute_variant", lib().moe_route_permute_variant(
+        _ptr(logits), T, E, k, first_expert, num_local, _ptr(topk_ids), _ptr(topk_weights),
+        _ptr(expert_counts), _ptr(expert_offsets), _ptr(permuted_rows),
+        _ptr(expanded_to_permuted), _ptr(ws), nws, ROUTING_VARIANTS[variant], _stream(stream)))
 
 
 def _ffn_common(x, permuted_rows, expert_offsets, k, w2, expert_out):

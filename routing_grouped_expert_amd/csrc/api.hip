@@ -17,6 +17,11 @@ hipError_t launch_route(const float* logits, int T, int E, int k, int* ids, floa
 size_t permute_workspace_bytes(int T, int E, int L);
 hipError_t launch_permute(const int* ids, int T, int k, int E, int first, int L, int* counts,
                           int* offsets, int* perm, int* e2p, void* ws, hipStream_t stream);
+hipError_t launch_route_permute(int variant, const float* logits, int T, int E, int k, int first,
+                                int L, int* ids, float* w, int* counts, int* offsets, int* perm,
+                                int* e2p, void* ws, hipStream_t stream);
+int routing_plan(int T, int E, int k, int L);
+bool routing_variant_applies(int variant, int T, int E, int L);
 size_t ffn_workspace_bytes(int T, int k, int I, int L);
 hipError_t launch_grouped_ffn(const uint16_t* x, const int* perm, const int* offsets, int L, int T,
                               int k, int H, int I, const uint16_t* w1, const uint16_t* w2,
@@ -139,10 +144,10 @@ moe_status forward_layer(const uint16_t* x, const float* w_gate, const float* ro
   clear_stale_error();
   hipError_t err =
       moe::launch_router_logits(x, w_gate, router_bias, T, H, E, logits, base + lo.router_ws, s);
-  if (err == hipSuccess) err = moe::launch_route(logits, T, E, k, ids, wts, s);
   if (err == hipSuccess)
-    err = moe::launch_permute(ids, T, k, E, first_expert, num_local, counts, offsets, perm, e2p,
-                              base + lo.permute_ws, s);
+    err = moe::launch_route_permute(moe::routing_plan(T, E, k, num_local), logits, T, E, k,
+                                    first_expert, num_local, ids, wts, counts, offsets, perm, e2p,
+                                    base + lo.permute_ws, s);
   if (err == hipSuccess && num_local > 0) err = ffn(perm, offsets, eo, base + lo.ffn_ws, s);
   if (err == hipSuccess) err = moe::launch_combine(eo, e2p, wts, T, k, H, y, s);
   return launched(err);
@@ -267,6 +272,52 @@ moe_status moe_permute(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E,
   return launched(moe::launch_permute(topk_ids, T, k, E, first_expert, num_local, expert_counts,
                                       expert_offsets, permuted_rows, expanded_to_permuted, ws,
                                       as_stream(stream)));
+}
+
+moe_status moe_routing_plan(int32_t T, int32_t E, int32_t k, int32_t num_local,
+                            int32_t* variant) {
+  if (!variant) return MOE_ERROR_INVALID_VALUE;
+  moe_status st = check_common(T, E, k);
+  if (st == MOE_SUCCESS) st = check_share(E, 0, num_local);
+  if (st != MOE_SUCCESS) return st;
+  *variant = moe::routing_plan(T, E, k, num_local);
+  return MOE_SUCCESS;
+}
+
+moe_status moe_route_permute_variant(const float* logits, int32_t T, int32_t E, int32_t k,
+                                     int32_t first_expert, int32_t num_local, int32_t* topk_ids,
+                                     float* topk_weights, int32_t* expert_counts,
+                                     int32_t* expert_offsets, int32_t* permuted_rows,
+                                     int32_t* expanded_to_permuted, void* ws, size_t ws_bytes,
+                                     int32_t variant, void* stream) {
+  moe_status st = check_common(T, E, k);
+  if (st == MOE_SUCCESS) st = check_share(E, first_expert, num_local);
+  if (st != MOE_SUCCESS) return st;
+  if ((int64_t)T * E >= kMaxIndex) return MOE_ERROR_UNSUPPORTED;
+  if (variant < MOE_ROUTING_AUTO || variant > MOE_ROUTING_TILED) return MOE_ERROR_INVALID_VALUE;
+  if (T == 0) return MOE_SUCCESS;
+  if (!logits || !topk_ids || !topk_weights || !expert_counts || !expert_offsets ||
+      !permuted_rows || !expanded_to_permuted)
+    return MOE_ERROR_INVALID_VALUE;
+  if (variant == MOE_ROUTING_AUTO) variant = moe::routing_plan(T, E, k, num_local);
+  if (!moe::routing_variant_applies(variant, T, E, num_local)) return MOE_ERROR_UNSUPPORTED;
+  const size_t need = moe::permute_workspace_bytes(T, E, num_local);
+  if (need > 0 && (!ws || ws_bytes < need || !aligned256(ws))) return MOE_ERROR_WORKSPACE;
+  clear_stale_error();
+  return launched(moe::launch_route_permute(variant, logits, T, E, k, first_expert, num_local,
+                                            topk_ids, topk_weights, expert_counts, expert_offsets,
+                                            permuted_rows, expanded_to_permuted, ws,
+                                            as_stream(stream)));
+}
+
+moe_status moe_route_permute(const float* logits, int32_t T, int32_t E, int32_t k,
+                             int32_t first_expert, int32_t num_local, int32_t* topk_ids,
+                             float* topk_weights, int32_t* expert_counts, int32_t* expert_offsets,
+                             int32_t* permuted_rows, int32_t* expanded_to_permuted, void* ws,
+                             size_t ws_bytes, void* stream) {
+  return moe_route_permute_variant(logits, T, E, k, first_expert, num_local, topk_ids,
+                                   topk_weights, expert_counts, expert_offsets, permuted_rows,
+                                   expanded_to_permuted, ws, ws_bytes, MOE_ROUTING_AUTO, stream);
 }
 
 moe_status moe_grouped_ffn(const uint16_t* x, const int32_t* permuted_rows,

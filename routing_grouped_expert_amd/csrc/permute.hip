@@ -11,40 +11,71 @@
 // entries keep ascending t, hence ascending r. Masks are built with LDS
 // atomic OR (order-free, so the result is deterministic).
 //
-// T <= 64: one block does all of it in LDS. Larger T: three kernels through
-// the workspace: tile masks; a scan over the tiles of each expert (a thread per
-// expert), whose last block to finish scans the local experts' counts into
-// offsets; scatter.
-#include "device.h"
+// While every tile's masks fit in LDS one block does all of it. Otherwise
+// three kernels through the workspace: tile masks; a scan over the tiles of
+// each expert (a thread per expert) giving the counts and each tile's base;
+// scatter, whose blocks each scan the local experts' counts into offsets.
+//
+// Routing and permutation together (launch_route_permute: the layer's path)
+// come in three variants; a cost model fitted to measurements picks one
+// (routing_plan):
+//   ONE_BLOCK   (T <= 64) one block selects every token's experts
+//               (select.h) and permutes them in LDS: one launch;
+//   TWO_KERNELS the routing kernel (a wave per token), then the single-block
+//               permutation above: two launches;
+//   TILED       the routing kernel also writes the tile masks (route.hip),
+//               then the scan and the scatter: three launches, any T.
+#include "select.h"
 
 namespace moe {
+
+// Routing variants (the values of moe_routing_variant in moe.h).
+constexpr int kRoutingOneBlock = 1, kRoutingTwoKernels = 2, kRoutingTiled = 3;
 
 namespace {
 constexpr int TILE = 64;
 
-// One block of up to 1024 threads, T <= 64.
-// Dynamic LDS: E uint64 masks + (L + 1) ints + 16 ints of scan scratch.
-__global__ __launch_bounds__(1024) void permute_small_kernel(const int* __restrict__ ids, int T,
+// One block of 1024 threads for all nb = ceil(T / 64) tiles, when the masks
+// and each tile's base per expert fit in LDS (block_permute_fits): masks in
+// LDS, then a thread per expert walks its tiles in order for the count and the
+// bases, and the block scans the local counts into offsets. Dynamic LDS:
+// nb E uint64 masks, nb E ints of bases, (L + 1) + 16 ints.
+constexpr size_t kBlockLds = 65536;
+bool block_permute_fits(int T, int E, int L) {
+  const size_t nb = (T + TILE - 1) / TILE;
+  return nb * E * 12 + (size_t)(L + 1 + 16) * 4 <= kBlockLds;
+}
+
+__global__ __launch_bounds__(1024) void permute_block_kernel(const int* __restrict__ ids, int T,
                                                              int k, int E, int first, int L,
                                                              int* __restrict__ counts,
                                                              int* __restrict__ offsets,
                                                              int* __restrict__ perm,
                                                              int* __restrict__ e2p) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  unsigned long long* mask = reinterpret_cast<unsigned long long*>(smem);
-  int* off = reinterpret_cast<int*>(mask + E);
+  const int nb = (T + TILE - 1) / TILE;
+  unsigned long long* mask = reinterpret_cast<unsigned long long*>(smem);  // [nb][E]
+  int* base = reinterpret_cast<int*>(mask + (size_t)nb * E);              // [nb][E]
+  int* off = base + (size_t)nb * E;
   int* tmp = off + (L + 1);
   const int tid = threadIdx.x, nt = blockDim.x;
   const int n = T * k;
-  for (int e = tid; e < E; e += nt) mask[e] = 0ull;
+  for (int i = tid; i < nb * E; i += nt) mask[i] = 0ull;
   __syncthreads();
   for (int r = tid; r < n; r += nt) {
-    const int e = ids[r];
-    if (e >= 0 && e < E) atomicOr(&mask[e], 1ull << (r / k));
+    const int e = ids[r], t = r / k;
+    if (e >= 0 && e < E) atomicOr(&mask[(t / TILE) * E + e], 1ull << (t % TILE));
   }
   __syncthreads();
-  for (int e = tid; e < E; e += nt) counts[e] = __popcll(mask[e]);
-  for (int i = tid; i < L; i += nt) off[i] = __popcll(mask[first + i]);
+  for (int e = tid; e < E; e += nt) {
+    int run = 0;
+    for (int b = 0; b < nb; ++b) {
+      base[b * E + e] = run;
+      run += __popcll(mask[b * E + e]);
+    }
+    counts[e] = run;
+    if (e >= first && e < first + L) off[e - first] = run;
+  }
   __syncthreads();
   block_exclusive_scan(off, L, tmp);
   for (int i = tid; i <= L; i += nt) offsets[i] = off[i];
@@ -52,8 +83,8 @@ __global__ __launch_bounds__(1024) void permute_small_kernel(const int* __restri
     const int e = ids[r];
     int p = -1;
     if (e >= first && e < first + L) {
-      const int t = r / k;
-      p = off[e - first] + __popcll(mask[e] & ((1ull << t) - 1ull));
+      const int t = r / k, b = t / TILE, tl = t % TILE;
+      p = off[e - first] + base[b * E + e] + __popcll(mask[b * E + e] & ((1ull << tl) - 1ull));
       perm[p] = r;
     }
     e2p[r] = p;
@@ -63,12 +94,10 @@ __global__ __launch_bounds__(1024) void permute_small_kernel(const int* __restri
 // Grid: one block per 64-token tile. masks[tile * E + e].
 __global__ __launch_bounds__(256) void tile_masks_kernel(const int* __restrict__ ids, int T, int k,
                                                          int E,
-                                                         unsigned long long* __restrict__ masks,
-                                                         int* __restrict__ done) {
+                                                         unsigned long long* __restrict__ masks) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   unsigned long long* mask = reinterpret_cast<unsigned long long*>(smem);
   const int b = blockIdx.x, tid = threadIdx.x;
-  if (b == 0 && tid == 0) *done = 0;  // the scan kernel's arrival counter
   for (int e = tid; e < E; e += blockDim.x) mask[e] = 0ull;
   __syncthreads();
   const int t0 = b * TILE;
@@ -85,25 +114,33 @@ __global__ __launch_bounds__(256) void tile_masks_kernel(const int* __restrict__
 // Grid: ceil(E / 64) blocks of SW waves; lane j of every wave owns expert
 // 64 * block + j and wave w the w-th of SW equal parts of the tiles:
 // counts[e], and base[tile * L + i] = entries of local expert i in earlier
-// tiles. The last block to finish writes offsets, the exclusive scan of the
-// local experts' counts. Dynamic LDS: (L + 1) + 16 ints.
+// tiles. A wave keeps the popcounts of up to SCAN_REG of its tiles in
+// registers between the two passes (more tiles: their masks are read again).
 constexpr int SW = 16;
+constexpr int SCAN_REG = 8;
 __global__ __launch_bounds__(SW * 64) void expert_scan_kernel(const unsigned long long* __restrict__ masks,
                                                               int nb, int E, int first, int L,
-                                                              int* counts, int* __restrict__ offsets,
-                                                              int* __restrict__ base, int* done) {
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+                                                              int* __restrict__ counts,
+                                                              int* __restrict__ base) {
   __shared__ int part[SW][kWave];
-  __shared__ int is_last;
-  int* off = reinterpret_cast<int*>(smem);
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
   const int e = blockIdx.x * kWave + lane;
   const int per = (nb + SW - 1) / SW;
   const int b0 = min(nb, wave * per), b1 = min(nb, b0 + per);
+  const bool inreg = per <= SCAN_REG;
+  int pc[SCAN_REG];
   int c = 0;
   if (e < E) {
+    if (inreg) {
+#pragma unroll
+      for (int j = 0; j < SCAN_REG; ++j) {
+        pc[j] = b0 + j < b1 ? __popcll(masks[(size_t)(b0 + j) * E + e]) : 0;
+        c += pc[j];
+      }
+    } else {
 #pragma unroll 4
-    for (int b = b0; b < b1; ++b) c += __popcll(masks[(size_t)b * E + e]);
+      for (int b = b0; b < b1; ++b) c += __popcll(masks[(size_t)b * E + e]);
+    }
   }
   part[wave][lane] = c;
   __syncthreads();
@@ -111,10 +148,18 @@ __global__ __launch_bounds__(SW * 64) void expert_scan_kernel(const unsigned lon
   for (int w = 0; w < wave; ++w) run += part[w][lane];
   const int i = e - first;
   if (e < E && i >= 0 && i < L) {
+    if (inreg) {
+#pragma unroll
+      for (int j = 0; j < SCAN_REG; ++j) {
+        if (b0 + j < b1) base[(size_t)(b0 + j) * L + i] = run;
+        run += pc[j];
+      }
+    } else {
 #pragma unroll 4
-    for (int b = b0; b < b1; ++b) {
-      base[(size_t)b * L + i] = run;
-      run += __popcll(masks[(size_t)b * E + e]);
+      for (int b = b0; b < b1; ++b) {
+        base[(size_t)b * L + i] = run;
+        run += __popcll(masks[(size_t)b * E + e]);
+      }
     }
   }
   if (wave == 0 && e < E) {
@@ -122,33 +167,25 @@ __global__ __launch_bounds__(SW * 64) void expert_scan_kernel(const unsigned lon
     for (int w = 0; w < SW; ++w) tot += part[w][lane];
     counts[e] = tot;
   }
-  // Counts are published (release, once per block) before the block is
-  // counted; only the last block acquires. Each device-scope fence writes
-  // back or invalidates the XCD's L2, so the other blocks skip the acquire.
-  __builtin_amdgcn_s_waitcnt(0x0f70);  // this wave's stores have reached L2
-  __syncthreads();
-  if (tid == 0) {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    const int last = atomicAdd(done, 1) == (int)gridDim.x - 1;
-    if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    is_last = last;
-  }
-  __syncthreads();
-  if (!is_last) return;
-  for (int j = tid; j < L; j += blockDim.x)
-    off[j] = __hip_atomic_load(&counts[first + j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  __syncthreads();
-  block_exclusive_scan(off, L, off + L + 1);
-  for (int j = tid; j <= L; j += blockDim.x) offsets[j] = off[j];
 }
 
+// Grid: one block per 64-token tile. Every block scans the local experts'
+// counts into offsets in LDS (block 0 also writes them out), then places its
+// tile's entries. Dynamic LDS: (L + 1) + 16 ints.
 __global__ __launch_bounds__(256) void scatter_kernel(const int* __restrict__ ids, int T, int k,
                                                       int E, int first, int L,
                                                       const unsigned long long* __restrict__ masks,
-                                                      const int* __restrict__ offsets,
+                                                      const int* __restrict__ counts,
+                                                      int* __restrict__ offsets,
                                                       const int* __restrict__ base,
                                                       int* __restrict__ perm,
                                                       int* __restrict__ e2p) {
+  extern __shared__ int off[];
+  for (int j = threadIdx.x; j < L; j += blockDim.x) off[j] = counts[first + j];
+  __syncthreads();
+  block_exclusive_scan(off, L, off + L + 1);
+  if (blockIdx.x == 0)
+    for (int j = threadIdx.x; j <= L; j += blockDim.x) offsets[j] = off[j];
   const int b = blockIdx.x;
   const int t0 = b * TILE;
   const int n = min(TILE, T - t0) * k;
@@ -160,7 +197,7 @@ __global__ __launch_bounds__(256) void scatter_kernel(const int* __restrict__ id
     if (e >= first && e < first + L) {
       const int tl = q / k;
       const unsigned long long m = masks[(size_t)b * E + e];
-      p = offsets[e - first] + base[(size_t)b * L + (e - first)] +
+      p = off[e - first] + base[(size_t)b * L + (e - first)] +
           __popcll(m & ((1ull << tl) - 1ull));
       perm[p] = r;
     }
@@ -169,46 +206,240 @@ __global__ __launch_bounds__(256) void scatter_kernel(const int* __restrict__ id
 }
 }  // namespace
 
-// Workspace for T > 64: tile masks [nb, E] u64, bases [nb, L] int, and the
-// scan kernel's arrival counter.
+// Routing and permutation of T <= 64 tokens in one block of NW waves: wave w
+// routes tokens w, w + NW, .. (each token's logits are loaded before the
+// previous token is selected), records its selections in the LDS masks and
+// the LDS copy of the ids, then the block counts, scans and scatters as
+// permute_block_kernel does for one tile. Dynamic LDS: E uint64 masks, (L + 1) + 16 ints,
+// T k ints of ids.
+template <int VPL, bool VEC, int NW>
+__global__ __launch_bounds__(NW * kWave) void route_permute_small_kernel(
+    const float* __restrict__ logits, int T, int E, int k, int first, int L,
+    int* __restrict__ ids, float* __restrict__ weights, int* __restrict__ counts,
+    int* __restrict__ offsets, int* __restrict__ perm, int* __restrict__ e2p) {
+  constexpr bool THRESH = VPL >= 4;
+  constexpr bool AHEAD = VPL <= 16;  // registers for the next token's logits
+  __shared__ unsigned long long cand[THRESH ? NW : 1][THRESH ? kWave : 1];
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  unsigned long long* mask = reinterpret_cast<unsigned long long*>(smem);
+  int* off = reinterpret_cast<int*>(mask + E);
+  int* tmp = off + (L + 1);
+  int* ids_s = tmp + 16;
+  const int tid = threadIdx.x, nt = blockDim.x, lane = tid % kWave, wave = tid / kWave;
+  const int n = T * k;
+  for (int e = tid; e < E; e += nt) mask[e] = 0ull;
+  __syncthreads();
+  float v[VPL], vn[AHEAD ? VPL : 1];
+  if (wave < T) sel::load_logits<VPL, VEC>(logits + (size_t)wave * E, lane, E, v);
+  for (int t = wave; t < T; t += NW) {
+    if constexpr (AHEAD) {
+      if (t + NW < T) sel::load_logits<VPL, VEC>(logits + (size_t)(t + NW) * E, lane, E, vn);
+    } else if (t != wave) {
+      sel::load_logits<VPL, VEC>(logits + (size_t)t * E, lane, E, v);
+    }
+    const uint32_t e = sel::route_token<VPL, VEC, THRESH>(v, lane, E, k, &cand[THRESH ? wave : 0][0],
+                                                         ids, weights, (size_t)t);
+    if (lane < k) {
+      ids_s[t * k + lane] = static_cast<int>(e);
+      atomicOr(&mask[e], 1ull << t);
+    }
+    if constexpr (AHEAD) {
+#pragma unroll
+      for (int i = 0; i < VPL; ++i) v[i] = vn[i];
+    }
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += nt) counts[e] = __popcll(mask[e]);
+  for (int i = tid; i < L; i += nt) off[i] = __popcll(mask[first + i]);
+  __syncthreads();
+  block_exclusive_scan(off, L, tmp);
+  for (int i = tid; i <= L; i += nt) offsets[i] = off[i];
+  for (int r = tid; r < n; r += nt) {
+    const int e = ids_s[r];
+    int p = -1;
+    if (e >= first && e < first + L) {
+      const int t = r / k;
+      p = off[e - first] + __popcll(mask[e] & ((1ull << t) - 1ull));
+      perm[p] = r;
+    }
+    e2p[r] = p;
+  }
+}
+
+// Workspace of the tiled variant (every T, so that any variant can run in
+// the same workspace): tile masks [nb, E] u64 and bases [nb, L] int.
 size_t permute_workspace_bytes(int T, int E, int L) {
-  if (T <= TILE) return 0;
+  if (T <= 0) return 0;
   const size_t nb = (T + TILE - 1) / TILE;
   size_t masks = nb * (size_t)E * 8;
   masks = (masks + 255) & ~(size_t)255;
   size_t base = nb * (size_t)(L > 0 ? L : 1) * 4;
-  return masks + ((base + 255) & ~(size_t)255) + 256;
+  return masks + ((base + 255) & ~(size_t)255);
+}
+
+namespace {
+struct PermWs {
+  unsigned long long* masks;
+  int* base;
+};
+PermWs perm_ws(void* ws, int T, int E) {
+  const int nb = (T + TILE - 1) / TILE;
+  const size_t mbytes = ((size_t)nb * E * 8 + 255) & ~(size_t)255;
+  char* w = static_cast<char*>(ws);
+  return PermWs{reinterpret_cast<unsigned long long*>(w), reinterpret_cast<int*>(w + mbytes)};
+}
+
+hipError_t launch_scan_scatter(const int* ids, int T, int k, int E, int first, int L, int* counts,
+                               int* offsets, int* perm, int* e2p, const PermWs& w,
+                               hipStream_t stream) {
+  const int nb = (T + TILE - 1) / TILE;
+  hipLaunchKernelGGL(expert_scan_kernel, dim3((E + kWave - 1) / kWave), dim3(SW * kWave), 0,
+                     stream, w.masks, nb, E, first, L, counts, w.base);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(scatter_kernel, dim3(nb), dim3(256), (size_t)(L + 1 + 16) * 4, stream, ids,
+                     T, k, E, first, L, w.masks, counts, offsets, w.base, perm, e2p);
+  return hipGetLastError();
+}
+
+template <int VPL>
+hipError_t launch_small_tier(const float* logits, int T, int E, int k, int first, int L, int* ids,
+                             float* w, int* counts, int* offsets, int* perm, int* e2p,
+                             hipStream_t stream) {
+  constexpr int NW = VPL <= 16 ? 16 : 8;  // 128 VGPRs at 16 waves, 256 at 8
+  const size_t lds = (size_t)E * 8 + (size_t)(L + 1 + 16) * 4 + (size_t)T * k * 4;
+  const bool vec = VPL >= 4 && E % 4 == 0 && (reinterpret_cast<uintptr_t>(logits) & 15u) == 0;
+  if constexpr (VPL >= 4) {
+    if (vec) {
+      hipLaunchKernelGGL((route_permute_small_kernel<VPL, true, NW>), dim3(1), dim3(NW * kWave),
+                         lds, stream, logits, T, E, k, first, L, ids, w, counts, offsets, perm,
+                         e2p);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((route_permute_small_kernel<VPL, false, NW>), dim3(1), dim3(NW * kWave), lds,
+                     stream, logits, T, E, k, first, L, ids, w, counts, offsets, perm, e2p);
+  return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_route(const float* logits, int T, int E, int k, int* ids, float* w,
+                        hipStream_t stream);
+hipError_t launch_route_masks(const float* logits, int T, int E, int k, int* ids, float* w,
+                              unsigned long long* masks, hipStream_t stream);
+
+namespace {
+hipError_t launch_permute_block(const int* ids, int T, int k, int E, int first, int L, int* counts,
+                                int* offsets, int* perm, int* e2p, hipStream_t stream) {
+  const size_t nb = (T + TILE - 1) / TILE;
+  const size_t lds = nb * E * 12 + (size_t)(L + 1 + 16) * 4;
+  hipLaunchKernelGGL(permute_block_kernel, dim3(1), dim3(1024), lds, stream, ids, T, k, E, first,
+                     L, counts, offsets, perm, e2p);
+  return hipGetLastError();
+}
+}  // namespace
+
+// Measured cost of the routing variants (microseconds per call of
+// selection + permutation, back-to-back calls replayed from a captured
+// graph on MI355X; N(0, 1) logits, k = 8, all experts local), by
+// values-per-lane tier (E = 64, 128, .., 4096), token count (1, 4, 16, .., 4096)
+// and variant (ONE_BLOCK, TWO_KERNELS, TILED); 0 where the variant does not
+// apply to that cell.
+constexpr int kCostTiers = 7, kCostPoints = 7;
+constexpr float kCost[kCostTiers][kCostPoints][3] = {
+    {{4.30f, 5.53f, 7.75f}, {4.61f, 5.97f, 8.00f}, {5.35f, 6.51f, 8.98f}, {12.56f, 6.70f, 9.52f}, {0.f, 7.95f, 10.47f}, {0.f, 13.21f, 10.80f}, {0.f, 36.02f, 12.31f}},  // VPL 1 (E = 64)
+    {{4.51f, 5.89f, 8.59f}, {4.80f, 6.27f, 8.46f}, {5.52f, 6.56f, 9.37f}, {13.22f, 6.99f, 10.02f}, {0.f, 8.36f, 10.89f}, {0.f, 14.29f, 10.97f}, {0.f, 0.f, 12.45f}},  // VPL 2 (E = 128)
+    {{4.37f, 5.60f, 8.58f}, {4.47f, 5.64f, 8.41f}, {5.11f, 6.37f, 8.84f}, {10.81f, 6.74f, 9.55f}, {0.f, 8.02f, 9.89f}, {0.f, 14.28f, 10.67f}, {0.f, 0.f, 11.94f}},  // VPL 4 (E = 256)
+    {{4.39f, 5.75f, 8.82f}, {4.77f, 6.06f, 9.49f}, {5.70f, 6.80f, 10.01f}, {12.15f, 6.98f, 10.67f}, {0.f, 8.46f, 11.11f}, {0.f, 0.f, 11.46f}, {0.f, 0.f, 12.85f}},  // VPL 8 (E = 512)
+    {{5.13f, 6.24f, 10.22f}, {5.78f, 6.98f, 10.50f}, {6.64f, 7.44f, 12.15f}, {14.61f, 7.50f, 12.47f}, {0.f, 9.48f, 12.88f}, {0.f, 0.f, 13.39f}, {0.f, 0.f, 15.50f}},  // VPL 16 (E = 1024)
+    {{6.51f, 7.01f, 12.95f}, {7.00f, 7.55f, 13.67f}, {10.00f, 8.40f, 14.38f}, {26.33f, 8.46f, 15.17f}, {0.f, 0.f, 15.78f}, {0.f, 0.f, 16.39f}, {0.f, 0.f, 20.31f}},  // VPL 32 (E = 2048)
+    {{10.88f, 0.f, 19.01f}, {13.79f, 0.f, 19.00f}, {24.65f, 0.f, 21.67f}, {56.61f, 0.f, 22.04f}, {0.f, 0.f, 22.27f}, {0.f, 0.f, 22.81f}, {0.f, 0.f, 32.93f}},  // VPL 64 (E = 4096)
+};
+
+// Predicted microseconds of a variant for T tokens and E experts: the
+// measured costs of E's tier, linear in log2 T between the measured token
+// counts; past the last measured point of the variant (it stops applying
+// there, or T > 4096) the last segment's slope continues.
+double routing_cost(int variant, int T, int E) {
+  int tier = 0;
+  for (int vpl = 1; vpl * 64 < E && tier < kCostTiers - 1; vpl *= 2) ++tier;
+  const int v = variant - kRoutingOneBlock;
+  double lt = 0.0;
+  for (int t = 1; t < T; t *= 2) lt += 1.0;  // ceil(log2 T)
+  const double x = lt / 2.0;                 // the measured points are 2 doublings apart
+  int last = -1;
+  for (int p = 0; p < kCostPoints; ++p)
+    if (kCost[tier][p][v] > 0.f) last = p;
+  if (last < 0) return 1e9;
+  int lo = x >= last ? last - 1 : (int)x;
+  if (lo < 0) return kCost[tier][0][v];
+  const double c0 = kCost[tier][lo][v], c1 = kCost[tier][lo + 1][v];
+  return c0 + (c1 - c0) * (x - lo);
+}
+
+bool routing_variant_applies(int variant, int T, int E, int L) {
+  switch (variant) {
+    case kRoutingOneBlock: return T <= TILE;
+    case kRoutingTwoKernels: return block_permute_fits(T, E, L);
+    case kRoutingTiled: return true;
+  }
+  return false;
+}
+
+// Routing (selection, weights) followed by the permutation, for moe_forward
+// and moe_route_permute, in the given variant (routing_variant_applies must
+// hold). ws: permute_workspace_bytes(T, E, L).
+hipError_t launch_route_permute(int variant, const float* logits, int T, int E, int k, int first,
+                                int L, int* ids, float* w, int* counts, int* offsets, int* perm,
+                                int* e2p, void* ws, hipStream_t stream) {
+  if (variant == kRoutingOneBlock) {
+    if (E <= 64) return launch_small_tier<1>(logits, T, E, k, first, L, ids, w, counts, offsets, perm, e2p, stream);
+    if (E <= 128) return launch_small_tier<2>(logits, T, E, k, first, L, ids, w, counts, offsets, perm, e2p, stream);
+    if (E <= 256) return launch_small_tier<4>(logits, T, E, k, first, L, ids, w, counts, offsets, perm, e2p, stream);
+    if (E <= 512) return launch_small_tier<8>(logits, T, E, k, first, L, ids, w, counts, offsets, perm, e2p, stream);
+    if (E <= 1024) return launch_small_tier<16>(logits, T, E, k, first, L, ids, w, counts, offsets, perm, e2p, stream);
+    if (E <= 2048) return launch_small_tier<32>(logits, T, E, k, first, L, ids, w, counts, offsets, perm, e2p, stream);
+    return launch_small_tier<64>(logits, T, E, k, first, L, ids, w, counts, offsets, perm, e2p, stream);
+  }
+  if (variant == kRoutingTwoKernels) {
+    hipError_t err = launch_route(logits, T, E, k, ids, w, stream);
+    if (err != hipSuccess) return err;
+    return launch_permute_block(ids, T, k, E, first, L, counts, offsets, perm, e2p, stream);
+  }
+  const PermWs pw = perm_ws(ws, T, E);
+  hipError_t err = launch_route_masks(logits, T, E, k, ids, w, pw.masks, stream);
+  if (err != hipSuccess) return err;
+  return launch_scan_scatter(ids, T, k, E, first, L, counts, offsets, perm, e2p, pw, stream);
+}
+
+// The variant moe_route_permute runs: the one with the smallest predicted
+// time among those that apply (routing_cost).
+int routing_plan(int T, int E, int k, int L) {
+  (void)k;
+  int best = kRoutingTiled;
+  double best_us = routing_cost(kRoutingTiled, T, E);
+  for (int v : {kRoutingOneBlock, kRoutingTwoKernels}) {
+    if (!routing_variant_applies(v, T, E, L)) continue;
+    const double us = routing_cost(v, T, E);
+    if (us < best_us) {
+      best_us = us;
+      best = v;
+    }
+  }
+  return best;
 }
 
 hipError_t launch_permute(const int* ids, int T, int k, int E, int first, int L, int* counts,
                           int* offsets, int* perm, int* e2p, void* ws, hipStream_t stream) {
-  if (T <= TILE) {
-    const int n = T * k;
-    int threads = n < 1024 ? ((n + 63) / 64) * 64 : 1024;
-    threads = threads < 256 ? 256 : threads;
-    const size_t lds = (size_t)E * 8 + (size_t)(L + 1) * 4 + 16 * 4;
-    hipLaunchKernelGGL(permute_small_kernel, dim3(1), dim3(threads), lds, stream, ids, T, k, E,
-                       first, L, counts, offsets, perm, e2p);
-    return hipGetLastError();
-  }
+  if (block_permute_fits(T, E, L))
+    return launch_permute_block(ids, T, k, E, first, L, counts, offsets, perm, e2p, stream);
   const int nb = (T + TILE - 1) / TILE;
-  unsigned long long* masks = static_cast<unsigned long long*>(ws);
-  const size_t mbytes = ((size_t)nb * E * 8 + 255) & ~(size_t)255;
-  const size_t bbytes = ((size_t)nb * (L > 0 ? L : 1) * 4 + 255) & ~(size_t)255;
-  int* base = reinterpret_cast<int*>(static_cast<char*>(ws) + mbytes);
-  int* done = reinterpret_cast<int*>(static_cast<char*>(ws) + mbytes + bbytes);
+  const PermWs pw = perm_ws(ws, T, E);
   hipLaunchKernelGGL(tile_masks_kernel, dim3(nb), dim3(256), (size_t)E * 8, stream, ids, T, k, E,
-                     masks, done);
+                     pw.masks);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(expert_scan_kernel, dim3((E + kWave - 1) / kWave), dim3(SW * kWave),
-                     (size_t)(L + 1 + 16) * 4, stream, masks, nb, E, first, L, counts, offsets,
-                     base, done);
-  err = hipGetLastError();
-  if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(scatter_kernel, dim3(nb), dim3(256), 0, stream, ids, T, k, E, first, L, masks,
-                     offsets, base, perm, e2p);
-  return hipGetLastError();
+  return launch_scan_scatter(ids, T, k, E, first, L, counts, offsets, perm, e2p, pw, stream);
 }
 
 }  // namespace moe

@@ -1,5 +1,5 @@
 // Routing: top-k of each token's fp32 logits, then the softmax renormalised
-// over the k selected experts.
+// over the k selected experts (selection and weights: select.h).
 //
 // Page "TRTLLM-Gen MoE routing optimisation in FlashInfer: relieving register
 // pressure" (flashinfer PR #3751), section 1 "Dynamic thread block size":
@@ -10,156 +10,103 @@
 // whatever E is, and the tier table plays the role of that page's section 2
 // (valid expert-count / block-size combinations fixed at compile time).
 //
-// Selection: k rounds of a wave-wide maximum of the order-preserving 32-bit
-// image of the logits; on equal logits the lower id wins; -0 is folded onto
-// +0 first so the two compare equal. Weights: w_j = exp(l_j - l_0) /
-// sum_i exp(l_i - l_0) over the k selected logits (the full-softmax
-// normaliser cancels in the renormalisation).
-#include "device.h"
+// Two forms of the kernel:
+//  - route_kernel<..., false>: 4 waves (tokens) per block; moe_route.
+//  - route_kernel<..., true>: 16 waves per block, one 16-token slice of a
+//    64-token tile; besides ids and weights it writes that slice of the
+//    tile's 64-bit token masks per expert (masks[tile][e], 16 bits of it),
+//    the input of the permutation's scan, so the layer needs no separate
+//    mask kernel.
+#include "select.h"
 
 namespace moe {
 
 namespace {
 
-// Order-preserving unsigned image of a logit (-0 folded onto +0): larger
-// logit, larger value. Lanes past E hold 0, below every logit's image.
-__device__ __forceinline__ uint32_t mono(float v) {
-  const uint32_t u = __float_as_uint(v + 0.0f);
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-__device__ __forceinline__ float from_mono(uint32_t m) {
-  return __uint_as_float((m & 0x80000000u) ? (m & 0x7FFFFFFFu) : ~m);
-}
+constexpr int kMaskWaves = 16;  // tokens per block of the masked form
 
-// Selection: every lane keeps the two best of its entries not yet taken
-// (h1 before h2 in the order: larger value first, then lower expert). A round
-// takes the wave-wide maximum of the h1 values; when several lanes hold it,
-// the lowest of their experts (a second reduction, skipped when one lane
-// holds it). The winning lane moves h2 up, and when it wins a second time
-// (its h2 already moved up) it rescans its entries after the one just taken.
-// Lane j keeps the entry taken in round j. A lane's entries are visited in
-// increasing expert order, so "greater than" keeps the lower expert on ties.
-// VEC (E a multiple of 4, 16-byte aligned logits, VPL >= 4): a lane loads its
-// values as groups of 4 consecutive experts, expert 4 (lane + 64 g) + c;
-// otherwise entry i of a lane is expert lane + 64 i.
-template <int VPL, bool VEC>
-__global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ logits, int T, int E,
-                                                   int k, int* __restrict__ ids,
-                                                   float* __restrict__ weights) {
-  const int lane = threadIdx.x % kWave;
-  const int t = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
-  if (t >= T) return;  // whole waves leave: every selection round runs on a full wave
-  const float* l = logits + (size_t)t * E;
-  auto expert = [&](int i) -> uint32_t {
-    return VEC ? 4 * (lane + kWave * (i / 4)) + (i % 4) : lane + kWave * i;
-  };
-  uint32_t val[VPL];
-  if constexpr (VEC) {
-    f32x4 v[VPL / 4];
-#pragma unroll
-    for (int g = 0; g < VPL / 4; ++g) {
-      const int e = 4 * (lane + kWave * g);
-      v[g] = e < E ? *reinterpret_cast<const f32x4*>(l + e) : f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-#pragma unroll
-    for (int i = 0; i < VPL; ++i) val[i] = (int)expert(i) < E ? mono(v[i / 4][i % 4]) : 0u;
-  } else {
-#pragma unroll
-    for (int i = 0; i < VPL; ++i) {
-      const int e = expert(i);
-      val[i] = e < E ? mono(l[e]) : 0u;
+template <int VPL, bool VEC, bool MASKS>
+__global__ __launch_bounds__(MASKS ? kMaskWaves * kWave : 4 * kWave) void route_kernel(
+    const float* __restrict__ logits, int T, int E, int k, int* __restrict__ ids,
+    float* __restrict__ weights, uint16_t* __restrict__ masks16) {
+  constexpr int NW = MASKS ? kMaskWaves : 4;
+  constexpr bool THRESH = VPL >= 4;
+  __shared__ unsigned long long cand[THRESH ? NW : 1][THRESH ? kWave : 1];
+  extern __shared__ uint32_t msk[];  // MASKS: E token masks of this slice
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  const int t = blockIdx.x * NW + wave;
+  float v[VPL];
+  if (t < T) sel::load_logits<VPL, VEC>(logits + (size_t)t * E, lane, E, v);
+  if constexpr (MASKS) {  // (the logits are in flight meanwhile)
+    for (int e = threadIdx.x; e < E; e += blockDim.x) msk[e] = 0u;
+    __syncthreads();
+  }
+  if (t < T) {
+    const uint32_t e =
+        sel::route_token<VPL, VEC, THRESH>(v, lane, E, k, &cand[THRESH ? wave : 0][0], ids, weights,
+                                           (size_t)t);
+    if constexpr (MASKS) {
+      if (lane < k) atomicOr(&msk[e], 1u << wave);
     }
   }
-  uint32_t h1v = 0, h1e = 0, h2v = 0, h2e = 0;
-  // the lane's best two entries after (bv, be) in the selection order
-  auto top2 = [&](bool bounded, uint32_t bv, uint32_t be) {
-    h1v = 0;
-    h2v = 0;
-#pragma unroll
-    for (int i = 0; i < VPL; ++i) {
-      const uint32_t e = expert(i);
-      uint32_t v = val[i];
-      if (bounded) v = (v < bv || (v == bv && e > be)) ? v : 0u;
-      const bool c1 = v > h1v, c2 = v > h2v;
-      h2v = c1 ? h1v : (c2 ? v : h2v);
-      h2e = c1 ? h1e : (c2 ? e : h2e);
-      h1v = c1 ? v : h1v;
-      h1e = c1 ? e : h1e;
+  if constexpr (MASKS) {
+    __syncthreads();
+    // slice s = blockIdx % 4 of tile blockIdx / 4: bits 16 s .. 16 s + 15 of
+    // each 64-bit mask (little-endian: the s-th 16-bit half-word)
+    const int tile = blockIdx.x / 4, s = blockIdx.x % 4;
+    const bool last = blockIdx.x == (int)gridDim.x - 1;
+    for (int e = threadIdx.x; e < E; e += blockDim.x) {
+      uint16_t* w = masks16 + ((size_t)tile * E + e) * 4;
+      w[s] = static_cast<uint16_t>(msk[e]);
+      if (last)  // slices of the last tile past T: no tokens
+        for (int q = s + 1; q < 4; ++q) w[q] = 0;
     }
-  };
-  top2(false, 0u, 0u);
-  bool h2_fresh = true;  // h2 is this lane's second best below h1
-  uint32_t mine_v = 0, mine_e = 0, top_v = 0;
-  for (int j = 0; j < k; ++j) {
-    const uint32_t m = wave_max_u32(h1v);
-    const bool cand = h1v == m;
-    const uint64_t cm = __builtin_amdgcn_ballot_w64(cand);
-    uint32_t be;
-    bool win;
-    if (__builtin_popcountll(cm) == 1) {
-      be = __builtin_amdgcn_readlane(static_cast<int>(h1e), __builtin_ctzll(cm));
-      win = cand;
-    } else {
-      be = wave_min_u32(cand ? h1e : 0xFFFFFFFFu);
-      win = cand && h1e == be;
-    }
-    if (j == 0) top_v = m;
-    if (lane == j) {
-      mine_v = m;
-      mine_e = be;
-    }
-    const bool rescan = win && !h2_fresh;
-    if (win) {
-      h1v = h2v;
-      h1e = h2e;
-      h2_fresh = false;
-    }
-    if (__builtin_amdgcn_ballot_w64(rescan)) {
-      if (rescan) {
-        top2(true, m, be);
-        h2_fresh = true;
-      }
-    }
-  }
-  const float topf = from_mono(top_v);
-  const float ex = lane < k ? expf(from_mono(mine_v) - topf) : 0.0f;
-  float s = 0.0f;  // sum in slot order
-  for (int j = 0; j < k; ++j) s += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ex), j));
-  if (lane < k) {
-    ids[(size_t)t * k + lane] = static_cast<int>(mine_e);
-    weights[(size_t)t * k + lane] = ex / s;
   }
 }
 
-template <int VPL>
+template <int VPL, bool MASKS>
 hipError_t launch_tier(const float* logits, int T, int E, int k, int* ids, float* w,
-                       hipStream_t stream) {
-  const int waves_per_block = 4;
-  dim3 grid((T + waves_per_block - 1) / waves_per_block);
+                       uint16_t* masks16, hipStream_t stream) {
+  constexpr int NW = MASKS ? kMaskWaves : 4;
+  dim3 grid((T + NW - 1) / NW);
+  const size_t lds = MASKS ? (size_t)E * 4 : 0;
   const bool vec = VPL >= 4 && E % 4 == 0 && (reinterpret_cast<uintptr_t>(logits) & 15u) == 0;
   if constexpr (VPL >= 4) {
     if (vec) {
-      hipLaunchKernelGGL((route_kernel<VPL, true>), grid, dim3(waves_per_block * kWave), 0, stream,
-                         logits, T, E, k, ids, w);
+      hipLaunchKernelGGL((route_kernel<VPL, true, MASKS>), grid, dim3(NW * kWave), lds, stream,
+                         logits, T, E, k, ids, w, masks16);
       return hipGetLastError();
     }
   }
-  hipLaunchKernelGGL((route_kernel<VPL, false>), grid, dim3(waves_per_block * kWave), 0, stream,
-                     logits, T, E, k, ids, w);
+  hipLaunchKernelGGL((route_kernel<VPL, false, MASKS>), grid, dim3(NW * kWave), lds, stream,
+                     logits, T, E, k, ids, w, masks16);
   return hipGetLastError();
+}
+
+template <bool MASKS>
+hipError_t launch_any(const float* logits, int T, int E, int k, int* ids, float* w,
+                      uint16_t* masks16, hipStream_t stream) {
+  if (E <= 64) return launch_tier<1, MASKS>(logits, T, E, k, ids, w, masks16, stream);
+  if (E <= 128) return launch_tier<2, MASKS>(logits, T, E, k, ids, w, masks16, stream);
+  if (E <= 256) return launch_tier<4, MASKS>(logits, T, E, k, ids, w, masks16, stream);
+  if (E <= 512) return launch_tier<8, MASKS>(logits, T, E, k, ids, w, masks16, stream);
+  if (E <= 1024) return launch_tier<16, MASKS>(logits, T, E, k, ids, w, masks16, stream);
+  if (E <= 2048) return launch_tier<32, MASKS>(logits, T, E, k, ids, w, masks16, stream);
+  return launch_tier<64, MASKS>(logits, T, E, k, ids, w, masks16, stream);
 }
 
 }  // namespace
 
 hipError_t launch_route(const float* logits, int T, int E, int k, int* ids, float* w,
                         hipStream_t stream) {
-  if (E <= 64) return launch_tier<1>(logits, T, E, k, ids, w, stream);
-  if (E <= 128) return launch_tier<2>(logits, T, E, k, ids, w, stream);
-  if (E <= 256) return launch_tier<4>(logits, T, E, k, ids, w, stream);
-  if (E <= 512) return launch_tier<8>(logits, T, E, k, ids, w, stream);
-  if (E <= 1024) return launch_tier<16>(logits, T, E, k, ids, w, stream);
-  if (E <= 2048) return launch_tier<32>(logits, T, E, k, ids, w, stream);
-  return launch_tier<64>(logits, T, E, k, ids, w, stream);
+  return launch_any<false>(logits, T, E, k, ids, w, nullptr, stream);
+}
+
+// Routing of T tokens that also writes the 64-token tile masks
+// (masks [ceil(T / 64), E] u64).
+hipError_t launch_route_masks(const float* logits, int T, int E, int k, int* ids, float* w,
+                              unsigned long long* masks, hipStream_t stream) {
+  return launch_any<true>(logits, T, E, k, ids, w, reinterpret_cast<uint16_t*>(masks), stream);
 }
 
 }  // namespace moe
