@@ -5,6 +5,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include "plan.h"
+
 #include <cstdint>
 #include <mutex>
 
@@ -19,17 +21,19 @@ hipError_t launch_permute(const int* ids, int T, int k, int E, int first, int L,
                           int* offsets, int* perm, int* e2p, void* ws, hipStream_t stream);
 hipError_t launch_route_permute(int variant, const float* logits, int T, int E, int k, int first,
                                 int L, int* ids, float* w, int* counts, int* offsets, int* perm,
-                                int* e2p, void* ws, hipStream_t stream);
+                                int* e2p, void* ws, const PlanOut& po, hipStream_t stream);
 int routing_plan(int T, int E, int k, int L);
 bool routing_variant_applies(int variant, int T, int E, int L);
 size_t ffn_workspace_bytes(int T, int k, int I, int L);
 hipError_t launch_grouped_ffn(const uint16_t* x, const int* perm, const int* offsets, int L, int T,
                               int k, int H, int I, const uint16_t* w1, const uint16_t* w2,
-                              float* out, void* ws, hipStream_t stream);
+                              float* out, void* ws, bool plan_ready, hipStream_t stream);
 hipError_t launch_grouped_ffn_fp8(const uint16_t* x, const int* perm, const int* offsets, int L,
                                   int T, int k, int H, int I, const uint8_t* w1q,
                                   const float* w1s, const uint8_t* w2q, const float* w2s,
-                                  float* out, void* ws, hipStream_t stream);
+                                  float* out, void* ws, bool plan_ready, hipStream_t stream);
+bool ffn_plan_target(const void* x, const void* w1, const void* w2, const void* out, int T, int k,
+                     int L, int H, int I, bool f8, void* ws, PlanOut* po);
 hipError_t launch_combine(const float* eo, const int* e2p, const float* w, int T, int k, int H,
                           uint16_t* y, hipStream_t stream);
 }  // namespace moe
@@ -112,15 +116,18 @@ Layout layout(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k, int64_t L) 
 bool aligned256(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 255u) == 0; }
 
 // The layer for one expert share: router logits, route, permute, the grouped
-// FFN that `ffn` launches (bf16 or FP8 weights), combine. Arguments are
-// checked before any launch; weights_given says whether the FFN's weight
-// pointers are all non-NULL.
+// FFN that `ffn` launches (bf16 or FP8 weights, w1 / w2 the code or value
+// arrays), combine. Arguments are checked before any launch; weights_given
+// says whether the FFN's weight pointers are all non-NULL. When the
+// persistent FFN kernels run, the routing's permutation kernel writes their
+// pass plan (one launch fewer: the FFN is told plan_ready).
 template <class Ffn>
 moe_status forward_layer(const uint16_t* x, const float* w_gate, const float* router_bias,
                          int32_t T, int32_t H, int32_t I, int32_t E, int32_t k,
                          int32_t first_expert, int32_t num_local, uint16_t* y, float* logits_out,
                          int32_t* topk_ids_out, float* topk_weights_out, void* ws,
-                         size_t ws_bytes, void* stream, bool weights_given, Ffn ffn) {
+                         size_t ws_bytes, void* stream, bool weights_given, const void* w1,
+                         const void* w2, bool f8, Ffn ffn) {
   moe_status st = check_common(T, E, k);
   if (st == MOE_SUCCESS) st = check_share(E, first_expert, num_local);
   if (st == MOE_SUCCESS) st = check_dims(T, k, H, I);
@@ -141,14 +148,19 @@ moe_status forward_layer(const uint16_t* x, const float* w_gate, const float* ro
   float* eo = reinterpret_cast<float*>(base + lo.expert_out);
   hipStream_t s = as_stream(stream);
 
+  moe::PlanOut po{};
+  const bool plan_ready = num_local > 0 && moe::ffn_plan_target(x, w1, w2, eo, T, k, num_local, H,
+                                                                I, f8, base + lo.ffn_ws, &po);
+
   clear_stale_error();
   hipError_t err =
       moe::launch_router_logits(x, w_gate, router_bias, T, H, E, logits, base + lo.router_ws, s);
   if (err == hipSuccess)
     err = moe::launch_route_permute(moe::routing_plan(T, E, k, num_local), logits, T, E, k,
                                     first_expert, num_local, ids, wts, counts, offsets, perm, e2p,
-                                    base + lo.permute_ws, s);
-  if (err == hipSuccess && num_local > 0) err = ffn(perm, offsets, eo, base + lo.ffn_ws, s);
+                                    base + lo.permute_ws, po, s);
+  if (err == hipSuccess && num_local > 0)
+    err = ffn(perm, offsets, eo, base + lo.ffn_ws, plan_ready, s);
   if (err == hipSuccess) err = moe::launch_combine(eo, e2p, wts, T, k, H, y, s);
   return launched(err);
 }
@@ -306,7 +318,7 @@ moe_status moe_route_permute_variant(const float* logits, int32_t T, int32_t E, 
   clear_stale_error();
   return launched(moe::launch_route_permute(variant, logits, T, E, k, first_expert, num_local,
                                             topk_ids, topk_weights, expert_counts, expert_offsets,
-                                            permuted_rows, expanded_to_permuted, ws,
+                                            permuted_rows, expanded_to_permuted, ws, moe::PlanOut{},
                                             as_stream(stream)));
 }
 
@@ -336,7 +348,7 @@ moe_status moe_grouped_ffn(const uint16_t* x, const int32_t* permuted_rows,
   if (!ws || ws_bytes < need || !aligned256(ws)) return MOE_ERROR_WORKSPACE;
   clear_stale_error();
   return launched(moe::launch_grouped_ffn(x, permuted_rows, expert_offsets, num_local, T, k, H, I,
-                                          w1, w2, expert_out, ws, as_stream(stream)));
+                                          w1, w2, expert_out, ws, false, as_stream(stream)));
 }
 
 moe_status moe_grouped_ffn_fp8(const uint16_t* x, const int32_t* permuted_rows,
@@ -356,7 +368,7 @@ moe_status moe_grouped_ffn_fp8(const uint16_t* x, const int32_t* permuted_rows,
   if (!ws || ws_bytes < need || !aligned256(ws)) return MOE_ERROR_WORKSPACE;
   clear_stale_error();
   return launched(moe::launch_grouped_ffn_fp8(x, permuted_rows, expert_offsets, num_local, T, k, H,
-                                              I, w1q, w1s, w2q, w2s, expert_out, ws,
+                                              I, w1q, w1s, w2q, w2s, expert_out, ws, false,
                                               as_stream(stream)));
 }
 
@@ -379,10 +391,11 @@ moe_status moe_forward(const uint16_t* x, const float* w_gate, const float* rout
                        void* ws, size_t ws_bytes, void* stream) {
   return forward_layer(
       x, w_gate, router_bias, T, H, I, E, k, first_expert, num_local, y, logits_out,
-      topk_ids_out, topk_weights_out, ws, ws_bytes, stream, w1 && w2,
-      [&](const int32_t* perm, const int32_t* offsets, float* eo, void* fws, hipStream_t s) {
+      topk_ids_out, topk_weights_out, ws, ws_bytes, stream, w1 && w2, w1, w2, false,
+      [&](const int32_t* perm, const int32_t* offsets, float* eo, void* fws, bool ready,
+          hipStream_t s) {
         return moe::launch_grouped_ffn(x, perm, offsets, num_local, T, k, H, I, w1, w2, eo, fws,
-                                       s);
+                                       ready, s);
       });
 }
 
@@ -394,10 +407,12 @@ moe_status moe_forward_fp8(const uint16_t* x, const float* w_gate, const float* 
                            void* ws, size_t ws_bytes, void* stream) {
   return forward_layer(
       x, w_gate, router_bias, T, H, I, E, k, first_expert, num_local, y, logits_out,
-      topk_ids_out, topk_weights_out, ws, ws_bytes, stream, w1q && w1s && w2q && w2s,
-      [&](const int32_t* perm, const int32_t* offsets, float* eo, void* fws, hipStream_t s) {
+      topk_ids_out, topk_weights_out, ws, ws_bytes, stream, w1q && w1s && w2q && w2s, w1q, w2q,
+      true,
+      [&](const int32_t* perm, const int32_t* offsets, float* eo, void* fws, bool ready,
+          hipStream_t s) {
         return moe::launch_grouped_ffn_fp8(x, perm, offsets, num_local, T, k, H, I, w1q, w1s, w2q,
-                                           w2s, eo, fws, s);
+                                           w2s, eo, fws, ready, s);
       });
 }
 

@@ -23,7 +23,7 @@
 //              as two bf16 arrays hi = bf16(a), lo = bf16(a - hi) whose sum
 //              is a to about 2^-17 relative (a is never rounded to bf16 alone).
 // down kernel: out = W2[e] (hi + lo) as two MFMAs into one fp32 accumulator.
-#include "device.h"
+#include "plan.h"
 
 namespace moe {
 
@@ -399,11 +399,12 @@ hipError_t launch_grouped_ffn_sk_fp8(const uint16_t* x, const int* perm, const i
                                      int L, int T, int k, int H, int I, const uint8_t* w1q,
                                      const float* w1s, const uint8_t* w2q, const float* w2s,
                                      uint16_t* h_hi, uint16_t* h_lo, float* out, void* ws,
-                                     hipStream_t stream);
+                                     bool plan_ready, hipStream_t stream);
 hipError_t launch_grouped_ffn_sk(const uint16_t* x, const int* perm, const int* offsets, int L,
                                  int T, int k, int H, int I, const uint16_t* w1,
                                  const uint16_t* w2, uint16_t* h_hi, uint16_t* h_lo, float* out,
-                                 void* ws, hipStream_t stream);
+                                 void* ws, bool plan_ready, hipStream_t stream);
+PlanOut ffn_sk_plan_out(int T, int k, int L, bool f8, void* ws);
 
 namespace {
 size_t h_array_bytes(int T, int k, int I) {
@@ -424,15 +425,27 @@ bool ffn_vector_path(const void* x, const void* w1, const void* w2, const void* 
          H % BLOCK_ROWS == 0 && I % BLOCK_ROWS == 0;
 }
 
+// Whether the persistent kernels run for these arguments and, if so, where
+// their pass plan goes (*po) in the FFN workspace ws: a caller that computes
+// the expert offsets can write the plan itself and pass plan_ready.
+bool ffn_plan_target(const void* x, const void* w1, const void* w2, const void* out, int T, int k,
+                     int L, int H, int I, bool f8, void* ws, PlanOut* po) {
+  const bool sk = f8 ? ffn_sk_fp8_applies(x, w1, w2, out, T, k, L, H, I)
+                     : ffn_sk_applies(x, w1, w2, out, T, k, L, H, I);
+  if (!sk || L < 1) return false;
+  *po = ffn_sk_plan_out(T, k, L, f8, static_cast<char*>(ws) + 2 * h_array_bytes(T, k, I));
+  return true;
+}
+
 hipError_t launch_grouped_ffn(const uint16_t* x, const int* perm, const int* offsets, int L, int T,
                               int k, int H, int I, const uint16_t* w1, const uint16_t* w2,
-                              float* out, void* ws, hipStream_t stream) {
+                              float* out, void* ws, bool plan_ready, hipStream_t stream) {
   const size_t half = h_array_bytes(T, k, I);
   uint16_t* h_hi = static_cast<uint16_t*>(ws);
   uint16_t* h_lo = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + half);
   if (ffn_sk_applies(x, w1, w2, out, T, k, L, H, I))
     return launch_grouped_ffn_sk(x, perm, offsets, L, T, k, H, I, w1, w2, h_hi, h_lo, out,
-                                 static_cast<char*>(ws) + 2 * half, stream);
+                                 static_cast<char*>(ws) + 2 * half, plan_ready, stream);
   return launch_generic<false>(x, perm, offsets, L, T, k, H, I, w1, nullptr, w2, nullptr, h_hi,
                                h_lo, out, ffn_vector_path(x, w1, w2, ws, out, H, I), stream);
 }
@@ -441,13 +454,14 @@ hipError_t launch_grouped_ffn(const uint16_t* x, const int* perm, const int* off
 hipError_t launch_grouped_ffn_fp8(const uint16_t* x, const int* perm, const int* offsets, int L,
                                   int T, int k, int H, int I, const uint8_t* w1q,
                                   const float* w1s, const uint8_t* w2q, const float* w2s,
-                                  float* out, void* ws, hipStream_t stream) {
+                                  float* out, void* ws, bool plan_ready, hipStream_t stream) {
   const size_t half = h_array_bytes(T, k, I);
   uint16_t* h_hi = static_cast<uint16_t*>(ws);
   uint16_t* h_lo = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + half);
   if (ffn_sk_fp8_applies(x, w1q, w2q, out, T, k, L, H, I))
     return launch_grouped_ffn_sk_fp8(x, perm, offsets, L, T, k, H, I, w1q, w1s, w2q, w2s, h_hi,
-                                     h_lo, out, static_cast<char*>(ws) + 2 * half, stream);
+                                     h_lo, out, static_cast<char*>(ws) + 2 * half, plan_ready,
+                                     stream);
   return launch_generic<true>(x, perm, offsets, L, T, k, H, I, w1q, w1s, w2q, w2s, h_hi, h_lo,
                               out, ffn_vector_path(x, w1q, w2q, ws, out, H, I), stream);
 }

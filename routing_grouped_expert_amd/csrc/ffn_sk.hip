@@ -39,7 +39,7 @@
 // down: K-split tile rows = 128 rows of W2 (8 groups of 16 sharing each B
 //       fragment); B = hi and lo, two MFMAs into one fp32 accumulator; the
 //       finished tile writes fp32 expert_out.
-#include "device.h"
+#include "plan.h"
 
 #include <algorithm>
 #include <type_traits>
@@ -88,18 +88,8 @@ constexpr int UP_ROWS = 16 * UP_RG;
 constexpr int DOWN_GROUPS = 8;    // 16-row groups per down tile
 constexpr int DOWN_ROWS = 16 * DOWN_GROUPS;
 
-// Plan layout (ints): [0] passes P, then pass_expert[Pmax], pass_beg[Pmax],
-// pass_cnt[Pmax]; counters follow at a 256-byte boundary.
-struct PlanView {
-  int* hdr;
-  int* expert;
-  int* beg;
-  int* cnt;
-};
-
-__device__ __forceinline__ PlanView plan_view(int* plan, int pmax) {
-  return PlanView{plan, plan + 4, plan + 4 + pmax, plan + 4 + 2 * pmax};
-}
+// The plan (plan.h) lies at the start of the workspace; the fixup counters
+// follow at a 256-byte boundary.
 
 // Read-only view for the FFN kernels (the plan is written by an earlier
 // kernel), so its wave-uniform entries are fetched with scalar loads.
@@ -117,29 +107,13 @@ __device__ __forceinline__ PlanRO plan_ro(const int* __restrict__ plan, int pmax
 // One block of 1024 threads: list the passes (expert, first entry, entries)
 // of every local expert with entries, and zero the fixup counters.
 __global__ __launch_bounds__(1024) void ffn_plan_kernel(const int* __restrict__ offsets, int L,
-                                                        int nmax, int nr, int* plan, int pmax,
-                                                        int* counters, int ncounters) {
-  extern __shared__ __attribute__((aligned(16))) int s_pass[];  // L + 1, then 16 scratch
-  const int tid = threadIdx.x;
-  for (int i = tid; i < ncounters; i += blockDim.x) counters[i] = 0;
-  for (int i = tid; i < L; i += blockDim.x) {
-    int b = max(0, min(offsets[i], nmax));
-    int e = max(b, min(offsets[i + 1], nmax));
-    s_pass[i] = (e - b + nr - 1) / nr;
-  }
+                                                        PlanOut po) {
+  extern __shared__ __attribute__((aligned(16))) int s_lds[];  // 2 (L + 1) + 16
+  int* off = s_lds;
+  for (int i = threadIdx.x; i < po.ncounters; i += blockDim.x) po.counters[i] = 0;
+  for (int i = threadIdx.x; i <= L; i += blockDim.x) off[i] = offsets[i];
   __syncthreads();
-  block_exclusive_scan(s_pass, L, s_pass + L + 1);
-  PlanView pv = plan_view(plan, pmax);
-  for (int i = tid; i < L; i += blockDim.x) {
-    int b = max(0, min(offsets[i], nmax));
-    int e = max(b, min(offsets[i + 1], nmax));
-    for (int q = s_pass[i], t = b; t < e; ++q, t += nr) {
-      pv.expert[q] = i;
-      pv.beg[q] = t;
-      pv.cnt[q] = min(nr, e - t);
-    }
-  }
-  if (tid == 0) pv.hdr[0] = s_pass[L];
+  write_ffn_plan(off, L, po, off + L + 1);
 }
 
 __device__ __forceinline__ bf16x8 ld8(const uint16_t* p) {
@@ -1386,23 +1360,35 @@ SkLayout sk_layout(int T, int k, int L, int NT, bool f8) {
   return o;
 }
 
+PlanOut plan_out(const SkLayout& lo, char* ws, int T, int k, int NT) {
+  const int nbm = lo.nb_up > lo.nb_down ? lo.nb_up : lo.nb_down;
+  return PlanOut{reinterpret_cast<int*>(ws + lo.plan), lo.pmax, NT * 16, T * k,
+                 reinterpret_cast<int*>(ws + lo.counters), 2 * lo.subs * nbm};
+}
+
+// plan_ready: the plan and zeroed counters are already in the workspace
+// (written by the routing's permutation kernel), so no plan kernel runs.
 template <int NT>
 hipError_t launch_sk_nt(const uint16_t* x, const int* perm, const int* offsets, int L, int T,
                         int k, int H, int I, const void* w1, const void* w2, const float* s1,
                         const float* s2, uint16_t* h_hi, uint16_t* h_lo, float* out, char* ws,
-                        hipStream_t stream) {
+                        bool plan_ready, hipStream_t stream) {
   // s1 / s2 non-null: FP8 weight codes with row scales
   const bool f8 = s1 != nullptr;
   const SkLayout lo = sk_layout(T, k, L, NT, f8);
-  int* plan = reinterpret_cast<int*>(ws + lo.plan);
-  int* counters = reinterpret_cast<int*>(ws + lo.counters);
+  const PlanOut po = plan_out(lo, ws, T, k, NT);
+  int* plan = po.plan;
+  int* counters = po.counters;
   f32x4* slots = reinterpret_cast<f32x4*>(ws + lo.slots);
   const int nmax = T * k;
   const int nbm = lo.nb_up > lo.nb_down ? lo.nb_up : lo.nb_down;
-  hipLaunchKernelGGL(ffn_plan_kernel, dim3(1), dim3(1024), (size_t)(L + 1 + 16) * 4, stream,
-                     offsets, L, nmax, NT * 16, plan, lo.pmax, counters, 2 * lo.subs * nbm);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
+  hipError_t err = hipSuccess;
+  if (!plan_ready) {
+    hipLaunchKernelGGL(ffn_plan_kernel, dim3(1), dim3(1024), (size_t)(2 * (L + 1) + 16) * 4,
+                       stream, offsets, L, po);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
   if constexpr (NT == 1) {
     if (f8)
       hipLaunchKernelGGL((ffn_up_sk_kernel<UP_RG, UP8_STEPS, true>), dim3(lo.nb_up), dim3(256), 0,
@@ -1464,6 +1450,14 @@ bool ffn_sk_applies(const void* x, const void* w1, const void* w2, const void* o
          (size_t)T * H * 2 < lim && (size_t)T * k * I * 2 < lim;
 }
 
+// The plan the persistent kernels will read for these sizes, in the FFN's own
+// workspace `ws` (the part after h_hi / h_lo), for a caller that writes it
+// itself.
+PlanOut ffn_sk_plan_out(int T, int k, int L, bool f8, void* ws) {
+  const int nt = pick_nt(T, k, L);
+  return plan_out(sk_layout(T, k, L, nt, f8), static_cast<char*>(ws), T, k, nt);
+}
+
 size_t ffn_sk_workspace_bytes(int T, int k, int L) {
   const int nt = pick_nt(T, k, L);
   const size_t a = sk_layout(T, k, L, nt, false).total;
@@ -1474,12 +1468,12 @@ size_t ffn_sk_workspace_bytes(int T, int k, int L) {
 hipError_t launch_grouped_ffn_sk(const uint16_t* x, const int* perm, const int* offsets, int L,
                                  int T, int k, int H, int I, const uint16_t* w1,
                                  const uint16_t* w2, uint16_t* h_hi, uint16_t* h_lo, float* out,
-                                 void* ws, hipStream_t stream) {
+                                 void* ws, bool plan_ready, hipStream_t stream) {
   char* w = static_cast<char*>(ws);
   switch (pick_nt(T, k, L)) {
-    case 1: return launch_sk_nt<1>(x, perm, offsets, L, T, k, H, I, w1, w2, nullptr, nullptr, h_hi, h_lo, out, w, stream);
-    case 4: return launch_sk_nt<4>(x, perm, offsets, L, T, k, H, I, w1, w2, nullptr, nullptr, h_hi, h_lo, out, w, stream);
-    default: return launch_sk_nt<8>(x, perm, offsets, L, T, k, H, I, w1, w2, nullptr, nullptr, h_hi, h_lo, out, w, stream);
+    case 1: return launch_sk_nt<1>(x, perm, offsets, L, T, k, H, I, w1, w2, nullptr, nullptr, h_hi, h_lo, out, w, plan_ready, stream);
+    case 4: return launch_sk_nt<4>(x, perm, offsets, L, T, k, H, I, w1, w2, nullptr, nullptr, h_hi, h_lo, out, w, plan_ready, stream);
+    default: return launch_sk_nt<8>(x, perm, offsets, L, T, k, H, I, w1, w2, nullptr, nullptr, h_hi, h_lo, out, w, plan_ready, stream);
   }
 }
 
@@ -1502,12 +1496,12 @@ hipError_t launch_grouped_ffn_sk_fp8(const uint16_t* x, const int* perm, const i
                                      int L, int T, int k, int H, int I, const uint8_t* w1q,
                                      const float* w1s, const uint8_t* w2q, const float* w2s,
                                      uint16_t* h_hi, uint16_t* h_lo, float* out, void* ws,
-                                     hipStream_t stream) {
+                                     bool plan_ready, hipStream_t stream) {
   char* w = static_cast<char*>(ws);
   switch (pick_nt(T, k, L)) {
-    case 1: return launch_sk_nt<1>(x, perm, offsets, L, T, k, H, I, w1q, w2q, w1s, w2s, h_hi, h_lo, out, w, stream);
-    case 4: return launch_sk_nt<4>(x, perm, offsets, L, T, k, H, I, w1q, w2q, w1s, w2s, h_hi, h_lo, out, w, stream);
-    default: return launch_sk_nt<8>(x, perm, offsets, L, T, k, H, I, w1q, w2q, w1s, w2s, h_hi, h_lo, out, w, stream);
+    case 1: return launch_sk_nt<1>(x, perm, offsets, L, T, k, H, I, w1q, w2q, w1s, w2s, h_hi, h_lo, out, w, plan_ready, stream);
+    case 4: return launch_sk_nt<4>(x, perm, offsets, L, T, k, H, I, w1q, w2q, w1s, w2s, h_hi, h_lo, out, w, plan_ready, stream);
+    default: return launch_sk_nt<8>(x, perm, offsets, L, T, k, H, I, w1q, w2q, w1s, w2s, h_hi, h_lo, out, w, plan_ready, stream);
   }
 }
 

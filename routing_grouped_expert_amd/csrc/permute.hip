@@ -25,6 +25,7 @@
 //               permutation above: two launches;
 //   TILED       the routing kernel also writes the tile masks (route.hip),
 //               then the scan and the scatter: three launches, any T.
+#include "plan.h"
 #include "select.h"
 
 namespace moe {
@@ -38,12 +39,23 @@ constexpr int TILE = 64;
 // One block of 1024 threads for all nb = ceil(T / 64) tiles, when the masks
 // and each tile's base per expert fit in LDS (block_permute_fits): masks in
 // LDS, then a thread per expert walks its tiles in order for the count and the
-// bases, and the block scans the local counts into offsets. Dynamic LDS:
-// nb E uint64 masks, nb E ints of bases, (L + 1) + 16 ints.
+// bases, and the block scans the local counts into offsets (then, given a
+// PlanOut, writes the grouped FFN's pass plan). Dynamic LDS: nb E uint64
+// masks, nb E ints of bases, 2 ((L + 1) + 16) ints.
 constexpr size_t kBlockLds = 65536;
 bool block_permute_fits(int T, int E, int L) {
   const size_t nb = (T + TILE - 1) / TILE;
-  return nb * E * 12 + (size_t)(L + 1 + 16) * 4 <= kBlockLds;
+  return nb * E * 12 + 2 * (size_t)(L + 1 + 16) * 4 <= kBlockLds;
+}
+
+// After the block's offsets scan: zero this block's share of the FFN fixup
+// counters and (block 0) write the FFN pass plan. s_pass: L + 1 + 16 ints.
+__device__ inline void maybe_write_plan(const int* off, int L, const PlanOut& po, int* s_pass) {
+  if (!po.plan) return;
+  const int nt = blockDim.x;
+  for (int i = blockIdx.x * nt + threadIdx.x; i < po.ncounters; i += gridDim.x * nt)
+    po.counters[i] = 0;
+  if (blockIdx.x == 0) write_ffn_plan(off, L, po, s_pass);
 }
 
 __global__ __launch_bounds__(1024) void permute_block_kernel(const int* __restrict__ ids, int T,
@@ -51,13 +63,14 @@ __global__ __launch_bounds__(1024) void permute_block_kernel(const int* __restri
                                                              int* __restrict__ counts,
                                                              int* __restrict__ offsets,
                                                              int* __restrict__ perm,
-                                                             int* __restrict__ e2p) {
+                                                             int* __restrict__ e2p, PlanOut po) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int nb = (T + TILE - 1) / TILE;
   unsigned long long* mask = reinterpret_cast<unsigned long long*>(smem);  // [nb][E]
   int* base = reinterpret_cast<int*>(mask + (size_t)nb * E);              // [nb][E]
   int* off = base + (size_t)nb * E;
   int* tmp = off + (L + 1);
+  int* s_pass = tmp + 16;
   const int tid = threadIdx.x, nt = blockDim.x;
   const int n = T * k;
   for (int i = tid; i < nb * E; i += nt) mask[i] = 0ull;
@@ -79,6 +92,7 @@ __global__ __launch_bounds__(1024) void permute_block_kernel(const int* __restri
   __syncthreads();
   block_exclusive_scan(off, L, tmp);
   for (int i = tid; i <= L; i += nt) offsets[i] = off[i];
+  maybe_write_plan(off, L, po, s_pass);
   for (int r = tid; r < n; r += nt) {
     const int e = ids[r];
     int p = -1;
@@ -170,8 +184,9 @@ __global__ __launch_bounds__(SW * 64) void expert_scan_kernel(const unsigned lon
 }
 
 // Grid: one block per 64-token tile. Every block scans the local experts'
-// counts into offsets in LDS (block 0 also writes them out), then places its
-// tile's entries. Dynamic LDS: (L + 1) + 16 ints.
+// counts into offsets in LDS (block 0 also writes them out, and the FFN pass
+// plan given a PlanOut), then places its tile's entries. Dynamic LDS:
+// 2 ((L + 1) + 16) ints.
 __global__ __launch_bounds__(256) void scatter_kernel(const int* __restrict__ ids, int T, int k,
                                                       int E, int first, int L,
                                                       const unsigned long long* __restrict__ masks,
@@ -179,13 +194,14 @@ __global__ __launch_bounds__(256) void scatter_kernel(const int* __restrict__ id
                                                       int* __restrict__ offsets,
                                                       const int* __restrict__ base,
                                                       int* __restrict__ perm,
-                                                      int* __restrict__ e2p) {
+                                                      int* __restrict__ e2p, PlanOut po) {
   extern __shared__ int off[];
   for (int j = threadIdx.x; j < L; j += blockDim.x) off[j] = counts[first + j];
   __syncthreads();
   block_exclusive_scan(off, L, off + L + 1);
   if (blockIdx.x == 0)
     for (int j = threadIdx.x; j <= L; j += blockDim.x) offsets[j] = off[j];
+  maybe_write_plan(off, L, po, off + L + 1 + 16);
   const int b = blockIdx.x;
   const int t0 = b * TILE;
   const int n = min(TILE, T - t0) * k;
@@ -210,13 +226,13 @@ __global__ __launch_bounds__(256) void scatter_kernel(const int* __restrict__ id
 // routes tokens w, w + NW, .. (each token's logits are loaded before the
 // previous token is selected), records its selections in the LDS masks and
 // the LDS copy of the ids, then the block counts, scans and scatters as
-// permute_block_kernel does for one tile. Dynamic LDS: E uint64 masks, (L + 1) + 16 ints,
-// T k ints of ids.
+// permute_block_kernel does for one tile. Dynamic LDS: E uint64 masks,
+// (L + 1) + 16 ints, T k ints of ids, (L + 1) + 16 ints of plan scratch.
 template <int VPL, bool VEC, int NW>
 __global__ __launch_bounds__(NW * kWave) void route_permute_small_kernel(
     const float* __restrict__ logits, int T, int E, int k, int first, int L,
     int* __restrict__ ids, float* __restrict__ weights, int* __restrict__ counts,
-    int* __restrict__ offsets, int* __restrict__ perm, int* __restrict__ e2p) {
+    int* __restrict__ offsets, int* __restrict__ perm, int* __restrict__ e2p, PlanOut po) {
   constexpr bool THRESH = VPL >= 4;
   constexpr bool AHEAD = VPL <= 16;  // registers for the next token's logits
   __shared__ unsigned long long cand[THRESH ? NW : 1][THRESH ? kWave : 1];
@@ -225,6 +241,7 @@ __global__ __launch_bounds__(NW * kWave) void route_permute_small_kernel(
   int* off = reinterpret_cast<int*>(mask + E);
   int* tmp = off + (L + 1);
   int* ids_s = tmp + 16;
+  int* s_pass = ids_s + T * k;
   const int tid = threadIdx.x, nt = blockDim.x, lane = tid % kWave, wave = tid / kWave;
   const int n = T * k;
   for (int e = tid; e < E; e += nt) mask[e] = 0ull;
@@ -254,6 +271,7 @@ __global__ __launch_bounds__(NW * kWave) void route_permute_small_kernel(
   __syncthreads();
   block_exclusive_scan(off, L, tmp);
   for (int i = tid; i <= L; i += nt) offsets[i] = off[i];
+  maybe_write_plan(off, L, po, s_pass);
   for (int r = tid; r < n; r += nt) {
     const int e = ids_s[r];
     int p = -1;
@@ -291,34 +309,34 @@ PermWs perm_ws(void* ws, int T, int E) {
 
 hipError_t launch_scan_scatter(const int* ids, int T, int k, int E, int first, int L, int* counts,
                                int* offsets, int* perm, int* e2p, const PermWs& w,
-                               hipStream_t stream) {
+                               const PlanOut& po, hipStream_t stream) {
   const int nb = (T + TILE - 1) / TILE;
   hipLaunchKernelGGL(expert_scan_kernel, dim3((E + kWave - 1) / kWave), dim3(SW * kWave), 0,
                      stream, w.masks, nb, E, first, L, counts, w.base);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(scatter_kernel, dim3(nb), dim3(256), (size_t)(L + 1 + 16) * 4, stream, ids,
-                     T, k, E, first, L, w.masks, counts, offsets, w.base, perm, e2p);
+  hipLaunchKernelGGL(scatter_kernel, dim3(nb), dim3(256), 2 * (size_t)(L + 1 + 16) * 4, stream,
+                     ids, T, k, E, first, L, w.masks, counts, offsets, w.base, perm, e2p, po);
   return hipGetLastError();
 }
 
 template <int VPL>
 hipError_t launch_small_tier(const float* logits, int T, int E, int k, int first, int L, int* ids,
                              float* w, int* counts, int* offsets, int* perm, int* e2p,
-                             hipStream_t stream) {
+                             const PlanOut& po, hipStream_t stream) {
   constexpr int NW = VPL <= 16 ? 16 : 8;  // 128 VGPRs at 16 waves, 256 at 8
-  const size_t lds = (size_t)E * 8 + (size_t)(L + 1 + 16) * 4 + (size_t)T * k * 4;
+  const size_t lds = (size_t)E * 8 + 2 * (size_t)(L + 1 + 16) * 4 + (size_t)T * k * 4;
   const bool vec = VPL >= 4 && E % 4 == 0 && (reinterpret_cast<uintptr_t>(logits) & 15u) == 0;
   if constexpr (VPL >= 4) {
     if (vec) {
       hipLaunchKernelGGL((route_permute_small_kernel<VPL, true, NW>), dim3(1), dim3(NW * kWave),
                          lds, stream, logits, T, E, k, first, L, ids, w, counts, offsets, perm,
-                         e2p);
+                         e2p, po);
       return hipGetLastError();
     }
   }
   hipLaunchKernelGGL((route_permute_small_kernel<VPL, false, NW>), dim3(1), dim3(NW * kWave), lds,
-                     stream, logits, T, E, k, first, L, ids, w, counts, offsets, perm, e2p);
+                     stream, logits, T, E, k, first, L, ids, w, counts, offsets, perm, e2p, po);
   return hipGetLastError();
 }
 }  // namespace
@@ -330,11 +348,12 @@ hipError_t launch_route_masks(const float* logits, int T, int E, int k, int* ids
 
 namespace {
 hipError_t launch_permute_block(const int* ids, int T, int k, int E, int first, int L, int* counts,
-                                int* offsets, int* perm, int* e2p, hipStream_t stream) {
+                                int* offsets, int* perm, int* e2p, const PlanOut& po,
+                                hipStream_t stream) {
   const size_t nb = (T + TILE - 1) / TILE;
-  const size_t lds = nb * E * 12 + (size_t)(L + 1 + 16) * 4;
+  const size_t lds = nb * E * 12 + 2 * (size_t)(L + 1 + 16) * 4;
   hipLaunchKernelGGL(permute_block_kernel, dim3(1), dim3(1024), lds, stream, ids, T, k, E, first,
-                     L, counts, offsets, perm, e2p);
+                     L, counts, offsets, perm, e2p, po);
   return hipGetLastError();
 }
 }  // namespace
@@ -388,28 +407,29 @@ bool routing_variant_applies(int variant, int T, int E, int L) {
 
 // Routing (selection, weights) followed by the permutation, for moe_forward
 // and moe_route_permute, in the given variant (routing_variant_applies must
-// hold). ws: permute_workspace_bytes(T, E, L).
+// hold). ws: permute_workspace_bytes(T, E, L). po.plan non-NULL: the
+// permutation kernel also writes the grouped FFN's pass plan (moe_forward).
 hipError_t launch_route_permute(int variant, const float* logits, int T, int E, int k, int first,
                                 int L, int* ids, float* w, int* counts, int* offsets, int* perm,
-                                int* e2p, void* ws, hipStream_t stream) {
+                                int* e2p, void* ws, const PlanOut& po, hipStream_t stream) {
   if (variant == kRoutingOneBlock) {
-    if (E <= 64) return launch_small_tier<1>(logits, T, E, k, first, L, ids, w, counts, offsets, perm, e2p, stream);
-    if (E <= 128) return launch_small_tier<2>(logits, T, E, k, first, L, ids, w, counts, offsets, perm, e2p, stream);
-    if (E <= 256) return launch_small_tier<4>(logits, T, E, k, first, L, ids, w, counts, offsets, perm, e2p, stream);
-    if (E <= 512) return launch_small_tier<8>(logits, T, E, k, first, L, ids, w, counts, offsets, perm, e2p, stream);
-    if (E <= 1024) return launch_small_tier<16>(logits, T, E, k, first, L, ids, w, counts, offsets, perm, e2p, stream);
-    if (E <= 2048) return launch_small_tier<32>(logits, T, E, k, first, L, ids, w, counts, offsets, perm, e2p, stream);
-    return launch_small_tier<64>(logits, T, E, k, first, L, ids, w, counts, offsets, perm, e2p, stream);
+    if (E <= 64) return launch_small_tier<1>(logits, T, E, k, first, L, ids, w, counts, offsets, perm, e2p, po, stream);
+    if (E <= 128) return launch_small_tier<2>(logits, T, E, k, first, L, ids, w, counts, offsets, perm, e2p, po, stream);
+    if (E <= 256) return launch_small_tier<4>(logits, T, E, k, first, L, ids, w, counts, offsets, perm, e2p, po, stream);
+    if (E <= 512) return launch_small_tier<8>(logits, T, E, k, first, L, ids, w, counts, offsets, perm, e2p, po, stream);
+    if (E <= 1024) return launch_small_tier<16>(logits, T, E, k, first, L, ids, w, counts, offsets, perm, e2p, po, stream);
+    if (E <= 2048) return launch_small_tier<32>(logits, T, E, k, first, L, ids, w, counts, offsets, perm, e2p, po, stream);
+    return launch_small_tier<64>(logits, T, E, k, first, L, ids, w, counts, offsets, perm, e2p, po, stream);
   }
   if (variant == kRoutingTwoKernels) {
     hipError_t err = launch_route(logits, T, E, k, ids, w, stream);
     if (err != hipSuccess) return err;
-    return launch_permute_block(ids, T, k, E, first, L, counts, offsets, perm, e2p, stream);
+    return launch_permute_block(ids, T, k, E, first, L, counts, offsets, perm, e2p, po, stream);
   }
   const PermWs pw = perm_ws(ws, T, E);
   hipError_t err = launch_route_masks(logits, T, E, k, ids, w, pw.masks, stream);
   if (err != hipSuccess) return err;
-  return launch_scan_scatter(ids, T, k, E, first, L, counts, offsets, perm, e2p, pw, stream);
+  return launch_scan_scatter(ids, T, k, E, first, L, counts, offsets, perm, e2p, pw, po, stream);
 }
 
 // The variant moe_route_permute runs: the one with the smallest predicted
@@ -431,15 +451,16 @@ int routing_plan(int T, int E, int k, int L) {
 
 hipError_t launch_permute(const int* ids, int T, int k, int E, int first, int L, int* counts,
                           int* offsets, int* perm, int* e2p, void* ws, hipStream_t stream) {
+  const PlanOut none{};
   if (block_permute_fits(T, E, L))
-    return launch_permute_block(ids, T, k, E, first, L, counts, offsets, perm, e2p, stream);
+    return launch_permute_block(ids, T, k, E, first, L, counts, offsets, perm, e2p, none, stream);
   const int nb = (T + TILE - 1) / TILE;
   const PermWs pw = perm_ws(ws, T, E);
   hipLaunchKernelGGL(tile_masks_kernel, dim3(nb), dim3(256), (size_t)E * 8, stream, ids, T, k, E,
                      pw.masks);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  return launch_scan_scatter(ids, T, k, E, first, L, counts, offsets, perm, e2p, pw, stream);
+  return launch_scan_scatter(ids, T, k, E, first, L, counts, offsets, perm, e2p, pw, none, stream);
 }
 
 }  // namespace moe

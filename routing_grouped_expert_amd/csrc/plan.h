@@ -1,0 +1,60 @@
+// The pass plan of the persistent grouped-FFN kernels (ffn_sk.hip): the list
+// of passes (local expert, first entry, entries) that the kernels deal out as
+// tiles, and the zeroed arrival counters of their cross-block fixup. Written
+// either by ffn_plan_kernel or, in the layer (moe_forward), by the routing's
+// permutation kernel right after it has the offsets, which saves a launch.
+#pragma once
+
+#include "device.h"
+
+namespace moe {
+
+// Plan layout (ints): [0] passes P, then pass_expert[pmax], pass_beg[pmax],
+// pass_cnt[pmax].
+struct PlanView {
+  int* hdr;
+  int* expert;
+  int* beg;
+  int* cnt;
+};
+
+__device__ __forceinline__ PlanView plan_view(int* plan, int pmax) {
+  return PlanView{plan, plan + 4, plan + 4 + pmax, plan + 4 + 2 * pmax};
+}
+
+// Where a plan goes: `plan` (NULL: no plan to write), passes of at most nr
+// entries over entries [0, nmax), and `ncounters` counters to zero.
+struct PlanOut {
+  int* plan;
+  int pmax, nr, nmax;
+  int* counters;
+  int ncounters;
+};
+
+// The plan from the exclusive scan `off` of the local experts' entry counts
+// (LDS, off[L] = entries in all). One block, every thread calls it; `s_pass`
+// is LDS scratch of L + 1 + 16 ints. The counters are zeroed by this block
+// (counter_stride = 1) or shared out over many (see callers).
+__device__ inline void write_ffn_plan(const int* off, int L, const PlanOut& po, int* s_pass) {
+  const int tid = threadIdx.x, nt = blockDim.x;
+  for (int i = tid; i < L; i += nt) {
+    const int b = max(0, min(off[i], po.nmax));
+    const int e = max(b, min(off[i + 1], po.nmax));
+    s_pass[i] = (e - b + po.nr - 1) / po.nr;
+  }
+  __syncthreads();
+  block_exclusive_scan(s_pass, L, s_pass + L + 1);
+  const PlanView pv = plan_view(po.plan, po.pmax);
+  for (int i = tid; i < L; i += nt) {
+    const int b = max(0, min(off[i], po.nmax));
+    const int e = max(b, min(off[i + 1], po.nmax));
+    for (int q = s_pass[i], t = b; t < e; ++q, t += po.nr) {
+      pv.expert[q] = i;
+      pv.beg[q] = t;
+      pv.cnt[q] = min(po.nr, e - t);
+    }
+  }
+  if (tid == 0) pv.hdr[0] = s_pass[L];
+}
+
+}  // namespace moe

@@ -203,7 +203,7 @@ def variants_for(T, E, L):
     if T <= 64:
         out.append("one_block")
     nb = (T + 63) // 64
-    if nb * E * 12 + (L + 17) * 4 <= 65536:
+    if nb * E * 12 + 2 * (L + 17) * 4 <= 65536:
         out.append("two_kernels")
     return out
 
