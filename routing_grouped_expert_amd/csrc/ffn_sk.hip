@@ -178,6 +178,15 @@ struct Pos {
   int t, kc;
 };
 
+// Chunk kc of a tile whose chunk order starts at `rot` (wrapping at C): a
+// tile dealt whole to one block starts at chunk tile % C, so the blocks
+// streaming at the same moment read different offsets within their weight
+// rows (see pf_issue); a tile cut between blocks keeps rot = 0.
+__device__ __forceinline__ int rot_chunk(int kc, int rot, int C) {
+  const int c = kc + rot;
+  return c >= C ? c - C : c;
+}
+
 // The units of a block. Tiles are dealt in whole rounds (in round r block b
 // takes tile r NB + b, so the blocks running together on one XCD hold
 // neighbouring tiles of the same pass and read its token rows from the same
@@ -497,18 +506,19 @@ __device__ __forceinline__ void up_mma(UpOps8<RG, S>& r, f32x4 (&acc)[2 * RG], u
 // turns them into addresses when the tile is reached, so those loads never
 // stall the weight stream.
 struct UpRaw {
-  int g, ex, tb, tc, r;
+  int g, ex, tb, tc, r, rot;
 };
 struct UpTile {
-  int g, ex, tb, tc;
+  int g, ex, tb, tc, rot;
   size_t wrow;  // lane's gate row (+ its K offset) in W1
   size_t xoff;  // lane's token row (+ its K offset) in x
   bool xz;      // the lane's entry is outside [0, T k): a zero row
 };
 
 __device__ __forceinline__ void up_issue(UpRaw& raw, int tile, int G, const PlanRO& pv,
-                                         const int* perm, int lane) {
+                                         const int* perm, int lane, int C, int TD) {
   const int pass = tile / G;
+  raw.rot = tile < TD ? tile % C : 0;
   raw.g = tile - pass * G;
   raw.ex = pv.expert[pass];
   raw.tb = pv.beg[pass];
@@ -529,6 +539,7 @@ __device__ __forceinline__ void up_finish(UpTile& st, const UpRaw& raw, int k, i
   st.ex = raw.ex;
   st.tb = raw.tb;
   st.tc = raw.tc;
+  st.rot = raw.rot;
   st.wrow = ((size_t)raw.ex * 2 * I + raw.g * (16 * RG)) * H + wlane;
   st.xz = !(raw.r >= 0 && raw.r < nmax);
   const int r = st.xz ? 0 : raw.r;
@@ -567,10 +578,10 @@ __global__ __launch_bounds__(256) void ffn_up_sk_kernel(
   UpRaw rn;
   {
     UpRaw r0;
-    up_issue(r0, rg.p0.t, G, pv, perm, lane);
+    up_issue(r0, rg.p0.t, G, pv, perm, lane, C, rg.TD);
     up_finish<RG>(ts, r0, k, H, I, nmax, wlane, kq);
   }
-  up_issue(rn, rg.next_tile(rg.p0.t), G, pv, perm, lane);
+  up_issue(rn, rg.next_tile(rg.p0.t), G, pv, perm, lane, C, rg.TD);
   __builtin_amdgcn_sched_barrier(0);  // ahead of the weight loads
 
   f32x4 acc[N];
@@ -620,20 +631,23 @@ __global__ __launch_bounds__(256) void ffn_up_sk_kernel(
   // this is its last unit in the block. Every unit starts with its first
   // half in flight in `h0`, so no register changes role between units.
   Ops h0, h1;
-  up_load(h0, w1 + ts.wrow, w1 + ts.wrow + I_H, x + ts.xoff, H, (size_t)rg.p0.kc * KUNIT, ts.xz);
+  up_load(h0, w1 + ts.wrow, w1 + ts.wrow + I_H, x + ts.xoff, H,
+          (size_t)rot_chunk(rg.p0.kc, ts.rot, C) * KUNIT, ts.xz);
   __builtin_amdgcn_sched_barrier(0);
   for (Pos p = rg.p0;;) {
-    up_load(h1, w1 + ts.wrow, w1 + ts.wrow + I_H, x + ts.xoff, H, (size_t)p.kc * KUNIT + KHALF, ts.xz);
+    up_load(h1, w1 + ts.wrow, w1 + ts.wrow + I_H, x + ts.xoff, H,
+            (size_t)rot_chunk(p.kc, ts.rot, C) * KUNIT + KHALF, ts.xz);
     __builtin_amdgcn_sched_barrier(0);
     up_mma(h0, acc, tw, lane);
     const Pos pn = rg.next(p);  // past the end: p again (loaded, unused)
     if (pn.t != p.t) {
       up_finish<RG>(tn, rn, k, H, I, nmax, wlane, kq);
-      up_issue(rn, rg.next_tile(pn.t), G, pv, perm, lane);  // the tile after
+      up_issue(rn, rg.next_tile(pn.t), G, pv, perm, lane, C, rg.TD);  // the tile after
     } else {
       tn = ts;
     }
-    up_load(h0, w1 + tn.wrow, w1 + tn.wrow + I_H, x + tn.xoff, H, (size_t)pn.kc * KUNIT, tn.xz);
+    up_load(h0, w1 + tn.wrow, w1 + tn.wrow + I_H, x + tn.xoff, H,
+            (size_t)rot_chunk(pn.kc, tn.rot, C) * KUNIT, tn.xz);
     __builtin_amdgcn_sched_barrier(0);
     up_mma(h1, acc, tw, lane);
     if (rg.ends_tile(p)) tile_end(p.t);
@@ -745,16 +759,18 @@ __device__ __forceinline__ void down_mma(DownOps8<DG, S>& r, f32x4 (&acc)[DG], u
 
 // Per-tile state of the down projection (plan entries loaded a tile ahead).
 struct DownRaw {
-  int g, ex, tb, tc;
+  int g, ex, tb, tc, rot;
 };
 struct DownTile {
-  int g, ex, tb, tc;
+  int g, ex, tb, tc, rot;
   size_t wrow;  // lane's first W2 row (+ its K offset)
   size_t hrow;  // lane's row of h (+ its K offset)
 };
 
-__device__ __forceinline__ void down_issue(DownRaw& raw, int tile, int G, const PlanRO& pv) {
+__device__ __forceinline__ void down_issue(DownRaw& raw, int tile, int G, const PlanRO& pv, int C,
+                                           int TD) {
   const int pass = tile / G;
+  raw.rot = tile < TD ? tile % C : 0;
   raw.g = tile - pass * G;
   raw.ex = pv.expert[pass];
   raw.tb = pv.beg[pass];
@@ -768,6 +784,7 @@ __device__ __forceinline__ void down_finish(DownTile& st, const DownRaw& raw, in
   st.ex = raw.ex;
   st.tb = raw.tb;
   st.tc = raw.tc;
+  st.rot = raw.rot;
   st.wrow = ((size_t)raw.ex * H + raw.g * (16 * DG)) * I + wlane;
   const int n = lane & 15;  // slots past the entries read the first entry's row
   st.hrow = (size_t)(raw.tb + (n < raw.tc ? n : 0)) * I + kq;
@@ -803,10 +820,10 @@ __global__ __launch_bounds__(256) void ffn_down_sk_kernel(
   DownRaw rn;
   {
     DownRaw r0;
-    down_issue(r0, rg.p0.t, G, pv);
+    down_issue(r0, rg.p0.t, G, pv, C, rg.TD);
     down_finish<DG>(ts, r0, H, I, lane, wlane, kq);
   }
-  down_issue(rn, rg.next_tile(rg.p0.t), G, pv);
+  down_issue(rn, rg.next_tile(rg.p0.t), G, pv, C, rg.TD);
 
   f32x4 acc[DG];
 #pragma unroll
@@ -838,20 +855,23 @@ __global__ __launch_bounds__(256) void ffn_down_sk_kernel(
 
   // Units in two halves, as in the up projection.
   Ops h0, h1;
-  down_load(h0, w2 + ts.wrow, I, h_hi + ts.hrow, h_lo + ts.hrow, (size_t)rg.p0.kc * KUNIT);
+  down_load(h0, w2 + ts.wrow, I, h_hi + ts.hrow, h_lo + ts.hrow,
+            (size_t)rot_chunk(rg.p0.kc, ts.rot, C) * KUNIT);
   __builtin_amdgcn_sched_barrier(0);
   for (Pos p = rg.p0;;) {
-    down_load(h1, w2 + ts.wrow, I, h_hi + ts.hrow, h_lo + ts.hrow, (size_t)p.kc * KUNIT + KHALF);
+    down_load(h1, w2 + ts.wrow, I, h_hi + ts.hrow, h_lo + ts.hrow,
+              (size_t)rot_chunk(p.kc, ts.rot, C) * KUNIT + KHALF);
     __builtin_amdgcn_sched_barrier(0);
     down_mma(h0, acc, tw, lane);
     const Pos pn = rg.next(p);
     if (pn.t != p.t) {
       down_finish<DG>(tn, rn, H, I, lane, wlane, kq);
-      down_issue(rn, rg.next_tile(pn.t), G, pv);  // the tile after
+      down_issue(rn, rg.next_tile(pn.t), G, pv, C, rg.TD);  // the tile after
     } else {
       tn = ts;
     }
-    down_load(h0, w2 + tn.wrow, I, h_hi + tn.hrow, h_lo + tn.hrow, (size_t)pn.kc * KUNIT);
+    down_load(h0, w2 + tn.wrow, I, h_hi + tn.hrow, h_lo + tn.hrow,
+              (size_t)rot_chunk(pn.kc, tn.rot, C) * KUNIT);
     __builtin_amdgcn_sched_barrier(0);
     down_mma(h1, acc, tw, lane);
     if (rg.ends_tile(p)) tile_end(p.t);
@@ -981,14 +1001,23 @@ __device__ __forceinline__ void pf_mma(const PfA<F8>& a, const pf_row_t* b0, con
 // Tile state (plan entries and the B rows' offsets), loaded a tile ahead.
 template <int NT>
 struct PfRaw {
-  int g, ex, tb, tc;
+  int g, ex, tb, tc, rot;
   int r[PfStage<NT * 16>::PER];
 };
 
+// A tile dealt whole to one block walks its K chunks starting at chunk
+// tile % C (wrapping round; rot_chunk), so the blocks streaming at the same
+// moment read different offsets within their weight rows. Rows whose length
+// is a multiple of 4 KB otherwise put every block's current 128 bytes at the
+// same low address bits: the down projection at I = 2048 (4 KB rows) read
+// 5.1 TB/s against 5.7 TB/s at I = 1920 and 2176, and rotating took the
+// fine-grained FFN from 3.65 to 3.51 ms and share 0 from 1.41 to 1.36 ms. A
+// tile cut between blocks (stream-K) is not rotated.
 template <int NT, bool UP>
 __device__ __forceinline__ void pf_issue(PfRaw<NT>& raw, int tile, int G, const PlanRO& pv,
-                                         const int* perm, int tid) {
+                                         const int* perm, int tid, int C, int TD) {
   const int pass = tile / G;
+  raw.rot = tile < TD ? tile % C : 0;
   raw.g = tile - pass * G;
   raw.ex = pv.expert[pass];
   raw.tb = pv.beg[pass];
@@ -1003,7 +1032,7 @@ __device__ __forceinline__ void pf_issue(PfRaw<NT>& raw, int tile, int G, const 
 
 template <int NT>
 struct PfTile {
-  int g, ex, tb, tc, ntiles;
+  int g, ex, tb, tc, ntiles, rot;
   size_t wrow;                               // this lane's first weight row (+ K offset)
   uint32_t voff[PfStage<NT * 16>::PER];      // staged B rows (+ this thread's column), bytes
 };
@@ -1025,6 +1054,7 @@ __device__ __forceinline__ void pf_finish(PfTile<NT>& st, const PfRaw<NT>& raw, 
   st.tb = raw.tb;
   st.tc = raw.tc;
   st.ntiles = (raw.tc + 15) >> 4;
+  st.rot = raw.rot;
   const int kq = (lane >> 4) * 8;
   const int K = UP ? H : I;
   const int row = UP ? raw.g * PF_UP_COLS + wave * 8 * PF_GROUPS
@@ -1045,13 +1075,15 @@ __device__ __forceinline__ void pf_finish(PfTile<NT>& st, const PfRaw<NT>& raw, 
   }
 }
 
-// With 4 token tiles, at most 128 VGPRs, so that two blocks share a CU: the
-// down projection then took 1477 us against 1617 us with one block per CU
-// (fine-grained shape); the up projection fits 128 anyway.
+// The up projection with 4 token tiles is held to 128 VGPRs, so that two
+// blocks share a CU. The down projection with 4 token tiles runs one block
+// per CU with its weights two chunks ahead (146 VGPRs): fine-grained FFN
+// 3.635 against 3.682 ms for two blocks per CU one chunk ahead (two blocks
+// and two chunks ahead spill at 128 VGPRs: 4.10 ms).
 // F8: FP8 E4M3 weight codes with one fp32 scale per row (wscale), applied to
 // the finished sums.
 template <int NT, bool UP, bool F8>
-__global__ __launch_bounds__(PF_THREADS, NT <= 4 ? 4 : 1) void ffn_pf_kernel(
+__global__ __launch_bounds__(PF_THREADS, (NT <= 4 && UP) ? 4 : 1) void ffn_pf_kernel(
     const uint16_t* __restrict__ b0src, const uint16_t* __restrict__ b1src,
     const int* __restrict__ perm, int k, int H, int I, int nmax, const void* __restrict__ wv,
     const float* __restrict__ wscale, const int* __restrict__ plan, int pmax, f32x4* slots,
@@ -1088,23 +1120,26 @@ __global__ __launch_bounds__(PF_THREADS, NT <= 4 ? 4 : 1) void ffn_pf_kernel(
   Pos p1 = sc.next(p0);
   {
     PfRaw<NT> r0;
-    pf_issue<NT, UP>(r0, p0.t, G, pv, perm, tid);
+    pf_issue<NT, UP>(r0, p0.t, G, pv, perm, tid, C, sc.TD);
     pf_finish<NT, UP, F8>(t0, r0, k, H, I, nmax, wave, lane, tid);
     if (p1.t != p0.t) {
-      pf_issue<NT, UP>(r0, p1.t, G, pv, perm, tid);
+      pf_issue<NT, UP>(r0, p1.t, G, pv, perm, tid, C, sc.TD);
       pf_finish<NT, UP, F8>(t1, r0, k, H, I, nmax, wave, lane, tid);
     } else {
       t1 = t0;
     }
   }
-  pf_issue<NT, UP>(rn, sc.next_tile(p1.t), G, pv, perm, tid);
+  pf_issue<NT, UP>(rn, sc.next_tile(p1.t), G, pv, perm, tid, C, sc.TD);
 
   f32x4 acc[NACC];
 #pragma unroll
   for (int i = 0; i < NACC; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  auto chunk = [&](const PfTile<NT>& t, int kc) {  // the tile's kc-th chunk (rotated)
+    return (size_t)rot_chunk(kc, t.rot, C) * PF_K;
+  };
   auto load_a = [&](PfA<F8>& a, const PfTile<NT>& t, int kc) {
-    const size_t kb = (size_t)kc * PF_K;
+    const size_t kb = chunk(t, kc);
     if constexpr (F8) {
 #pragma unroll
       for (int q = 0; q < PF_GROUPS; ++q)
@@ -1123,7 +1158,7 @@ __global__ __launch_bounds__(PF_THREADS, NT <= 4 ? 4 : 1) void ffn_pf_kernel(
     }
   };
   auto load_b = [&](PfStage<NR> (&st)[NB_ARR], const PfTile<NT>& t, int kc) {
-    const size_t kb = (size_t)kc * PF_K;
+    const size_t kb = chunk(t, kc);
     pf_stage_load(st[0], rs0, t.voff, (uint32_t)(kb * 2));
     if (!UP) pf_stage_load(st[NB_ARR - 1], rs1, t.voff, (uint32_t)(kb * 2));
   };
@@ -1191,9 +1226,10 @@ __global__ __launch_bounds__(PF_THREADS, NT <= 4 ? 4 : 1) void ffn_pf_kernel(
   // two units ahead, through three register sets (share 0: 882 us against
   // 911 us one unit ahead), and so do the FP8 kernels, whose register sets
   // are small (fine-grained FP8 call: 2.26 ms against 2.31 ms; share 0
-  // unchanged); the others stay at one unit ahead (the bf16 down projection
-  // at 8 tiles measured the same either way).
-  constexpr bool A3 = (UP && NT >= 8) || F8;
+  // unchanged), and the down projection with 4 token tiles (one block per
+  // CU, see the launch bounds); the bf16 down projection at 8 tiles measured
+  // the same either way and stays at one unit ahead.
+  constexpr bool A3 = (UP && NT >= 8) || F8 || (!UP && NT == 4);
   PfA<F8> a0, a1, a2;  // a2: A3 only
   PfStage<NR> sb0[NB_ARR], sb1[NB_ARR];
   load_b(sb1, t0, p0.kc);
@@ -1213,7 +1249,7 @@ __global__ __launch_bounds__(PF_THREADS, NT <= 4 ? 4 : 1) void ffn_pf_kernel(
     const Pos p2 = sc.next(p1);
     if (p2.t != p1.t) {
       pf_finish<NT, UP, F8>(t2, rn, k, H, I, nmax, wave, lane, tid);
-      pf_issue<NT, UP>(rn, sc.next_tile(p2.t), G, pv, perm, tid);
+      pf_issue<NT, UP>(rn, sc.next_tile(p2.t), G, pv, perm, tid, C, sc.TD);
     } else {
       t2 = t1;
     }
