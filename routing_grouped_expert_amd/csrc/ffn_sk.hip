@@ -181,7 +181,9 @@ struct Pos {
 // Chunk kc of a tile whose chunk order starts at `rot` (wrapping at C): a
 // tile dealt whole to one block starts at chunk tile % C, so the blocks
 // streaming at the same moment read different offsets within their weight
-// rows (see pf_issue); a tile cut between blocks keeps rot = 0.
+// rows (see pf_issue); a tile cut between blocks keeps rot = 0, and so do the
+// FP8 kernels (their code rows measured 1-2% slower rotated: fine-grained
+// 2.289 against 2.248 ms, share 0 1.144 against 1.131 ms).
 __device__ __forceinline__ int rot_chunk(int kc, int rot, int C) {
   const int c = kc + rot;
   return c >= C ? c - C : c;
@@ -578,10 +580,10 @@ __global__ __launch_bounds__(256) void ffn_up_sk_kernel(
   UpRaw rn;
   {
     UpRaw r0;
-    up_issue(r0, rg.p0.t, G, pv, perm, lane, C, rg.TD);
+    up_issue(r0, rg.p0.t, G, pv, perm, lane, C, F8 ? 0 : rg.TD);
     up_finish<RG>(ts, r0, k, H, I, nmax, wlane, kq);
   }
-  up_issue(rn, rg.next_tile(rg.p0.t), G, pv, perm, lane, C, rg.TD);
+  up_issue(rn, rg.next_tile(rg.p0.t), G, pv, perm, lane, C, F8 ? 0 : rg.TD);
   __builtin_amdgcn_sched_barrier(0);  // ahead of the weight loads
 
   f32x4 acc[N];
@@ -642,7 +644,7 @@ __global__ __launch_bounds__(256) void ffn_up_sk_kernel(
     const Pos pn = rg.next(p);  // past the end: p again (loaded, unused)
     if (pn.t != p.t) {
       up_finish<RG>(tn, rn, k, H, I, nmax, wlane, kq);
-      up_issue(rn, rg.next_tile(pn.t), G, pv, perm, lane, C, rg.TD);  // the tile after
+      up_issue(rn, rg.next_tile(pn.t), G, pv, perm, lane, C, F8 ? 0 : rg.TD);  // the tile after
     } else {
       tn = ts;
     }
@@ -820,10 +822,10 @@ __global__ __launch_bounds__(256) void ffn_down_sk_kernel(
   DownRaw rn;
   {
     DownRaw r0;
-    down_issue(r0, rg.p0.t, G, pv, C, rg.TD);
+    down_issue(r0, rg.p0.t, G, pv, C, F8 ? 0 : rg.TD);
     down_finish<DG>(ts, r0, H, I, lane, wlane, kq);
   }
-  down_issue(rn, rg.next_tile(rg.p0.t), G, pv, C, rg.TD);
+  down_issue(rn, rg.next_tile(rg.p0.t), G, pv, C, F8 ? 0 : rg.TD);
 
   f32x4 acc[DG];
 #pragma unroll
@@ -866,7 +868,7 @@ __global__ __launch_bounds__(256) void ffn_down_sk_kernel(
     const Pos pn = rg.next(p);
     if (pn.t != p.t) {
       down_finish<DG>(tn, rn, H, I, lane, wlane, kq);
-      down_issue(rn, rg.next_tile(pn.t), G, pv, C, rg.TD);  // the tile after
+      down_issue(rn, rg.next_tile(pn.t), G, pv, C, F8 ? 0 : rg.TD);  // the tile after
     } else {
       tn = ts;
     }
@@ -1120,16 +1122,16 @@ __global__ __launch_bounds__(PF_THREADS, (NT <= 4 && UP) ? 4 : 1) void ffn_pf_ke
   Pos p1 = sc.next(p0);
   {
     PfRaw<NT> r0;
-    pf_issue<NT, UP>(r0, p0.t, G, pv, perm, tid, C, sc.TD);
+    pf_issue<NT, UP>(r0, p0.t, G, pv, perm, tid, C, F8 ? 0 : sc.TD);
     pf_finish<NT, UP, F8>(t0, r0, k, H, I, nmax, wave, lane, tid);
     if (p1.t != p0.t) {
-      pf_issue<NT, UP>(r0, p1.t, G, pv, perm, tid, C, sc.TD);
+      pf_issue<NT, UP>(r0, p1.t, G, pv, perm, tid, C, F8 ? 0 : sc.TD);
       pf_finish<NT, UP, F8>(t1, r0, k, H, I, nmax, wave, lane, tid);
     } else {
       t1 = t0;
     }
   }
-  pf_issue<NT, UP>(rn, sc.next_tile(p1.t), G, pv, perm, tid, C, sc.TD);
+  pf_issue<NT, UP>(rn, sc.next_tile(p1.t), G, pv, perm, tid, C, F8 ? 0 : sc.TD);
 
   f32x4 acc[NACC];
 #pragma unroll
@@ -1249,7 +1251,7 @@ __global__ __launch_bounds__(PF_THREADS, (NT <= 4 && UP) ? 4 : 1) void ffn_pf_ke
     const Pos p2 = sc.next(p1);
     if (p2.t != p1.t) {
       pf_finish<NT, UP, F8>(t2, rn, k, H, I, nmax, wave, lane, tid);
-      pf_issue<NT, UP>(rn, sc.next_tile(p2.t), G, pv, perm, tid, C, sc.TD);
+      pf_issue<NT, UP>(rn, sc.next_tile(p2.t), G, pv, perm, tid, C, F8 ? 0 : sc.TD);
     } else {
       t2 = t1;
     }
