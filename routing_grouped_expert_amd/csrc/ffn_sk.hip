@@ -179,7 +179,7 @@ struct Pos {
 };
 
 // Chunk kc of a tile whose chunk order starts at `rot` (wrapping at C): a
-// tile dealt whole to one block starts at chunk tile % C, so the blocks
+// tile dealt whole to one block starts at chunk 7 tile % C, so the blocks
 // streaming at the same moment read different offsets within their weight
 // rows (see pf_issue); a tile cut between blocks keeps rot = 0, and so do the
 // FP8 kernels (their code rows measured 1-2% slower rotated: fine-grained
@@ -520,7 +520,7 @@ struct UpTile {
 __device__ __forceinline__ void up_issue(UpRaw& raw, int tile, int G, const PlanRO& pv,
                                          const int* perm, int lane, int C, int TD) {
   const int pass = tile / G;
-  raw.rot = tile < TD ? tile % C : 0;
+  raw.rot = tile < TD ? (tile * 7) % C : 0;
   raw.g = tile - pass * G;
   raw.ex = pv.expert[pass];
   raw.tb = pv.beg[pass];
@@ -772,7 +772,7 @@ struct DownTile {
 __device__ __forceinline__ void down_issue(DownRaw& raw, int tile, int G, const PlanRO& pv, int C,
                                            int TD) {
   const int pass = tile / G;
-  raw.rot = tile < TD ? tile % C : 0;
+  raw.rot = tile < TD ? (tile * 7) % C : 0;
   raw.g = tile - pass * G;
   raw.ex = pv.expert[pass];
   raw.tb = pv.beg[pass];
@@ -1008,18 +1008,19 @@ struct PfRaw {
 };
 
 // A tile dealt whole to one block walks its K chunks starting at chunk
-// tile % C (wrapping round; rot_chunk), so the blocks streaming at the same
+// 7 tile % C (wrapping round; rot_chunk), so the blocks streaming at the same
 // moment read different offsets within their weight rows. Rows whose length
 // is a multiple of 4 KB otherwise put every block's current 128 bytes at the
 // same low address bits: the down projection at I = 2048 (4 KB rows) read
 // 5.1 TB/s against 5.7 TB/s at I = 1920 and 2176, and rotating took the
-// fine-grained FFN from 3.65 to 3.51 ms and share 0 from 1.41 to 1.36 ms. A
-// tile cut between blocks (stream-K) is not rotated.
+// fine-grained FFN from 3.65 to 3.51 ms and share 0 from 1.41 to 1.36 ms
+// (starting at 7 tile % C rather than tile % C: 1.34 ms at share 0). A tile
+// cut between blocks (stream-K) is not rotated.
 template <int NT, bool UP>
 __device__ __forceinline__ void pf_issue(PfRaw<NT>& raw, int tile, int G, const PlanRO& pv,
                                          const int* perm, int tid, int C, int TD) {
   const int pass = tile / G;
-  raw.rot = tile < TD ? tile % C : 0;
+  raw.rot = tile < TD ? (tile * 7) % C : 0;
   raw.g = tile - pass * G;
   raw.ex = pv.expert[pass];
   raw.tb = pv.beg[pass];
