@@ -85,6 +85,12 @@ constexpr int UP8_CAP = 2;
 constexpr int DOWN8_CAP = 1;
 constexpr int UP_RG = 1;          // 16-row gate groups (and as many up groups) per up tile
 constexpr int UP_ROWS = 16 * UP_RG;
+// The FP8 up tile holds two gate groups (and two up groups): at one group the
+// token fragments (bf16, 16 tokens) cost as many bytes per K step as the FP8
+// weight codes, and the up kernel streamed slower (decode shape: 194 us
+// against 167 us at two groups).
+constexpr int UP8_RG = 2;
+constexpr int UP8_ROWS = 16 * UP8_RG;
 constexpr int DOWN_GROUPS = 8;    // 16-row groups per down tile
 constexpr int DOWN_ROWS = 16 * DOWN_GROUPS;
 
@@ -1347,7 +1353,7 @@ size_t a256(size_t n) { return (n + 255) & ~(size_t)255; }
 template <int NT>
 int up_blocks(bool f8) {
   if constexpr (NT == 1)
-    return f8 ? resident_blocks<ffn_up_sk_kernel<UP_RG, UP8_STEPS, true>>(256, UP8_CAP)
+    return f8 ? resident_blocks<ffn_up_sk_kernel<UP8_RG, UP8_STEPS, true>>(256, UP8_CAP)
               : std::min(resident_blocks<ffn_up_sk_kernel<UP_RG, UP_STEPS, false>>(256, UP_CAP),
                          resident_blocks<ffn_up_sk_kernel<UP_RG, UP_STEPS_SHORT, false>>(256, UP_CAP));
   else
@@ -1376,7 +1382,7 @@ int blocks_for(int NT, bool up, bool f8) {
 // counters per block, and 2 x `subs` slots per block shared by both kernels
 // (a block's first and last tile; `subs` = 1 for the K-split kernels, one per
 // wave for the prefill kernels). A slot holds one wave's partial tile: for the
-// K-split kernels the larger of the two tiles' accumulators (2 UP_RG or
+// K-split kernels the largest of the tiles' accumulators (2 UP_RG, 2 UP8_RG or
 // DOWN_GROUPS f32x4 per lane), for the prefill kernels at most 4 NT.
 struct SkLayout {
   size_t plan, counters, slots, total;
@@ -1394,7 +1400,7 @@ SkLayout sk_layout(int T, int k, int L, int NT, bool f8) {
   o.subs = NT == 1 ? 1 : PF_WAVES;
   o.counters = a256((size_t)(4 + 3 * o.pmax) * 4);
   o.slots = o.counters + a256((size_t)2 * o.subs * nbm * 4);
-  const int slot_n = NT == 1 ? (2 * UP_RG > DOWN_GROUPS ? 2 * UP_RG : DOWN_GROUPS) : 4 * NT;
+  const int slot_n = NT == 1 ? std::max({2 * UP_RG, 2 * UP8_RG, DOWN_GROUPS}) : 4 * NT;
   o.total = o.slots + a256((size_t)2 * o.subs * nbm * slot_n * kWave * 16);
   return o;
 }
@@ -1430,7 +1436,7 @@ hipError_t launch_sk_nt(const uint16_t* x, const int* perm, const int* offsets, 
   }
   if constexpr (NT == 1) {
     if (f8)
-      hipLaunchKernelGGL((ffn_up_sk_kernel<UP_RG, UP8_STEPS, true>), dim3(lo.nb_up), dim3(256), 0,
+      hipLaunchKernelGGL((ffn_up_sk_kernel<UP8_RG, UP8_STEPS, true>), dim3(lo.nb_up), dim3(256), 0,
                          stream, x, perm, k, H, I, nmax, w1, s1, plan, lo.pmax, slots, counters,
                          h_hi, h_lo, lo.nb_up);
     else if (H % UP_KUNIT == 0)
@@ -1524,7 +1530,7 @@ bool ffn_sk_fp8_applies(const void* x, const void* w1q, const void* w2q, const v
   auto al = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
   if (!(al(x) && al(w1q) && al(w2q) && al(out))) return false;
   if (pick_nt(T, k, L) == 1)
-    return H % UP8_KUNIT == 0 && I % DOWN8_KUNIT == 0 && I % UP_ROWS == 0 && H % DOWN_ROWS == 0;
+    return H % UP8_KUNIT == 0 && I % DOWN8_KUNIT == 0 && I % UP8_ROWS == 0 && H % DOWN_ROWS == 0;
   // the staged kernels address token rows with 32-bit byte offsets below 2^31
   const size_t lim = (size_t)1 << 31;
   return H % PF_K == 0 && I % PF_K == 0 && H % PF_ROWS == 0 && I % PF_UP_COLS == 0 &&
