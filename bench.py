@@ -16,6 +16,9 @@ The same run also measures:
     plain streaming probe on the same part);
   - the share-0 prefill layer (E=384 over 5 shares, experts 0..76, T=4096)
     and the decode layer (T=32, H=4096, I=14336, E=8, top-2) as extra keys;
+  - the same layers and the headline one with FP8 E4M3 expert weights
+    (moe_forward_fp8: per-row fp32 scales, bf16 activations) as the
+    ``*_fp8`` keys;
   - an MFMA-bound probe: the share-0 expert weights with T=32768 tokens, the
     grouped FFN's useful bf16 TFLOP/s against the 2.5 PFLOP/s dense peak;
   - routing microseconds at 1024 experts (route + permute, T = 1 / 64 / 4096),
@@ -49,7 +52,7 @@ def parse_args():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="fine", choices=["tiny", "decode", "fine", "share0"])
     ap.add_argument("--no-extras", action="store_true",
-                    help="skip the share-0 / decode extra keys and the MFMA probe")
+                    help="skip the share-0 / decode / FP8 extra keys and the MFMA probe")
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the oracle timing (profiling runs)")
     ap.add_argument("--no-routing", action="store_true", help="skip the routing-only timings")
@@ -569,6 +572,16 @@ def main():
                 log(f"mfma probe: {probe['useful_tflops']} TFLOP/s")
             del lay
             torch.cuda.empty_cache()
+        if not fp8:
+            # the FP8 E4M3 weight path (moe_forward_fp8) on the same workloads
+            for name in ("decode", "share0", args.workload):
+                lay = Layer(name, fp8=True)
+                extras[f"{name}_fp8"] = dict(
+                    workload=lay.describe() + ", FP8 E4M3 weights with per-row fp32 scales",
+                    **summarize(lay, args.steps, args.warmup))
+                log(f"{name} fp8: {extras[name + '_fp8']['ms_per_step']} ms/step")
+                del lay
+                torch.cuda.empty_cache()
 
     layer = Layer(args.workload, fp8=fp8)
     head = summarize(layer, args.steps, args.warmup)
