@@ -201,3 +201,31 @@ def test_library_shares_torchs_hip_runtime():
     n = int(out.stdout.split()[0])
     assert n == 1, out.stdout
     assert "torch" in out.stdout, out.stdout
+
+
+def _block_permute_fits(T, E, L):
+    # the single-block permutation keeps every 64-token tile's masks and bases
+    # (12 bytes per tile and expert) and two scan arrays of L + 17 ints in 64 KB
+    nb = (T + 63) // 64
+    return nb * E * 12 + 2 * (L + 17) * 4 <= 65536
+
+
+@pytest.mark.parametrize("E", [8, 64, 256, 1024, 2048, 4096])
+def test_routing_plan_picks_an_applicable_variant(E):
+    """moe_routing_plan (host logic, no launch): the variant it names applies to
+    the sizes (ONE_BLOCK up to one 64-token tile, TWO_KERNELS while the
+    single-block permutation fits its LDS), and its choices at the measured
+    token counts are the cost table's: one fused launch for a single token,
+    the tiled split at 4096 tokens."""
+    k = min(8, E)
+    for T in (1, 2, 4, 16, 63, 64, 65, 256, 1000, 1024, 4096, 65536):
+        v = moe.routing_plan(T, E, k, E)
+        assert v in ("one_block", "two_kernels", "tiled")
+        if v == "one_block":
+            assert T <= 64
+        if v == "two_kernels":
+            assert _block_permute_fits(T, E, E)
+    assert moe.routing_plan(1, E, k, E) == "one_block"
+    assert moe.routing_plan(4096, E, k, E) == "tiled"
+    if E == 1024:
+        assert moe.routing_plan(64, E, k, E) == "two_kernels"
