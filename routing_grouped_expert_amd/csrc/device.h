@@ -62,6 +62,15 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
   return r;
 }
 
+// Workgroups are dispatched to the 8 XCDs round-robin (block b to XCD b % 8),
+// and each XCD has its own L2. Renumber blocks so that consecutive work
+// ranges -- the same experts, hence the same activation rows -- run on the
+// same XCD: physical block b becomes (b % 8) * (NB / 8) + b / 8.
+constexpr int kXcds = 8;
+__device__ __forceinline__ int xcd_block(int b, int NB) {
+  return NB % kXcds == 0 ? (b % kXcds) * (NB / kXcds) + b / kXcds : b;
+}
+
 // Eight FP8 E4M3 (OCP e4m3fn) weight codes, lo = codes 0..3 and hi = codes
 // 4..7 in byte order, as eight bf16 values. Every E4M3 value is a bf16 value,
 // so the conversion is exact; CDNA4's scaled decoder turns two codes into two

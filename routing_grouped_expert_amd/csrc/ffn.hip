@@ -404,7 +404,7 @@ hipError_t launch_grouped_ffn_sk(const uint16_t* x, const int* perm, const int* 
                                  int T, int k, int H, int I, const uint16_t* w1,
                                  const uint16_t* w2, uint16_t* h_hi, uint16_t* h_lo, float* out,
                                  void* ws, bool plan_ready, hipStream_t stream);
-PlanOut ffn_sk_plan_out(int T, int k, int L, bool f8, void* ws);
+PlanOut ffn_sk_plan_out(int T, int k, int L, int H, int I, bool f8, void* ws);
 
 namespace {
 size_t h_array_bytes(int T, int k, int I) {
@@ -433,7 +433,7 @@ bool ffn_plan_target(const void* x, const void* w1, const void* w2, const void* 
   const bool sk = f8 ? ffn_sk_fp8_applies(x, w1, w2, out, T, k, L, H, I)
                      : ffn_sk_applies(x, w1, w2, out, T, k, L, H, I);
   if (!sk || L < 1) return false;
-  *po = ffn_sk_plan_out(T, k, L, f8, static_cast<char*>(ws) + 2 * h_array_bytes(T, k, I));
+  *po = ffn_sk_plan_out(T, k, L, H, I, f8, static_cast<char*>(ws) + 2 * h_array_bytes(T, k, I));
   return true;
 }
 

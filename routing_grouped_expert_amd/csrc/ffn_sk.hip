@@ -46,6 +46,13 @@
 
 namespace moe {
 
+int ffn_dense_blocks();
+bool ffn_dense_shape_ok(int T, int k, int H, int I);
+int ffn_dense_pass_tokens();
+hipError_t launch_ffn_dense(const uint16_t* x, const int* perm, int k, int H, int I, int nmax,
+                            const uint16_t* w1, const uint16_t* w2, const int* plan, int pmax,
+                            uint16_t* h_hi, uint16_t* h_lo, float* out, hipStream_t stream);
+
 namespace {
 // Tile shapes, measured on MI355X at the decode shape (T32 H4096 I14336 E8
 // top-2; up kernel / down kernel, microseconds). With fragment-layout weight
@@ -251,15 +258,6 @@ struct Sched {
     return t >= TD && ((t == ps.t && ps.kc > 0) || (t == pe.t && pe.kc < C - 1));
   }
 };
-
-// Workgroups are dispatched to the 8 XCDs round-robin (block b to XCD b % 8),
-// and each XCD has its own L2. Renumber blocks so that consecutive unit
-// ranges -- the same experts, hence the same activation rows -- run on the
-// same XCD: physical block b becomes (b % 8) * (NB / 8) + b / 8.
-constexpr int kXcds = 8;
-__device__ __forceinline__ int xcd_block(int b, int NB) {
-  return NB % kXcds == 0 ? (b % kXcds) * (NB / kXcds) + b / kXcds : b;
-}
 
 // Sum the four waves' accumulators of one tile through LDS, RCH f32x4 per
 // lane at a time: every wave writes its region, then wave 0 adds them in wave
@@ -1335,17 +1333,25 @@ int resident_blocks(int threads = 256, int cap = 8) {
 // Token tiles (of 16) per pass, from twice the mean entries per local expert
 // (an expert with more entries takes further passes, each reading its weights
 // again), capped by T (a token picks an expert at most once). 1: the K-split
-// kernels; 4 or 8: the kernels with token rows staged in LDS. Between 16 and
-// 32 the staged kernels with 4 tiles win over 2-tile passes: on the
-// fine-grained shape (T512 H7168 I2048 E256 top-8) 4.05 ms against 5.46 ms,
-// mostly by not repeating passes for the experts above 32 entries. Staged
-// kernels at 2 tiles (weights two chunks ahead, at most 120 VGPRs) took the
-// same shape's grouped FFN to 3.79 ms against 3.69 ms at 4 tiles.
-int pick_nt(int T, int k, int L) {
+// kernels; 4 or 8: the kernels with token rows staged in LDS; 16: the dense
+// kernels (ffn_dense.hip: passes of 256 tokens, both operands staged in LDS)
+// once the mean reaches kDenseMean entries per expert and the shape suits
+// them (bf16 weights only). Between 16 and 32 the staged kernels with 4 tiles
+// win over 2-tile passes: on the fine-grained shape (T512 H7168 I2048 E256
+// top-8) 4.05 ms against 5.46 ms, mostly by not repeating passes for the
+// experts above 32 entries. Staged kernels at 2 tiles (weights two chunks
+// ahead, at most 120 VGPRs) took the same shape's grouped FFN to 3.79 ms
+// against 3.69 ms at 4 tiles.
+constexpr long kDenseMean = 256;
+int pick_staged_nt(int T, int k, int L) {
   const long bound = T;
   const long twice_mean = L > 0 ? (2L * T * k + L - 1) / L : bound;
   const long want = twice_mean < bound ? twice_mean : bound;
   return want <= 16 ? 1 : want <= 64 ? 4 : 8;
+}
+int pick_nt(int T, int k, int L, int H, int I, bool f8) {
+  if (!f8 && L > 0 && (long)T * k >= kDenseMean * L && ffn_dense_shape_ok(T, k, H, I)) return 16;
+  return pick_staged_nt(T, k, L);
 }
 
 size_t a256(size_t n) { return (n + 255) & ~(size_t)255; }
@@ -1372,6 +1378,7 @@ int down_blocks(bool f8) {
 
 int blocks_for(int NT, bool up, bool f8) {
   switch (NT) {
+    case 16: return ffn_dense_blocks();
     case 1: return up ? up_blocks<1>(f8) : down_blocks<1>(f8);
     case 4: return up ? up_blocks<4>(f8) : down_blocks<4>(f8);
     default: return up ? up_blocks<8>(f8) : down_blocks<8>(f8);
@@ -1399,6 +1406,10 @@ SkLayout sk_layout(int T, int k, int L, int NT, bool f8) {
   o.plan = 0;
   o.subs = NT == 1 ? 1 : PF_WAVES;
   o.counters = a256((size_t)(4 + 3 * o.pmax) * 4);
+  if (NT == 16) {  // the dense kernels: whole tiles only, no counters or slots
+    o.slots = o.total = o.counters;
+    return o;
+  }
   o.slots = o.counters + a256((size_t)2 * o.subs * nbm * 4);
   const int slot_n = NT == 1 ? std::max({2 * UP_RG, 2 * UP8_RG, DOWN_GROUPS}) : 4 * NT;
   o.total = o.slots + a256((size_t)2 * o.subs * nbm * slot_n * kWave * 16);
@@ -1408,7 +1419,7 @@ SkLayout sk_layout(int T, int k, int L, int NT, bool f8) {
 PlanOut plan_out(const SkLayout& lo, char* ws, int T, int k, int NT) {
   const int nbm = lo.nb_up > lo.nb_down ? lo.nb_up : lo.nb_down;
   return PlanOut{reinterpret_cast<int*>(ws + lo.plan), lo.pmax, NT * 16, T * k,
-                 reinterpret_cast<int*>(ws + lo.counters), 2 * lo.subs * nbm};
+                 reinterpret_cast<int*>(ws + lo.counters), NT == 16 ? 0 : 2 * lo.subs * nbm};
 }
 
 // plan_ready: the plan and zeroed counters are already in the workspace
@@ -1480,13 +1491,31 @@ hipError_t launch_sk_nt(const uint16_t* x, const int* perm, const int* offsets, 
   }
   return hipGetLastError();
 }
+// The dense kernels (ffn_dense.hip) on the plan of passes of 256 entries.
+hipError_t launch_dense_path(const uint16_t* x, const int* perm, const int* offsets, int L, int T,
+                             int k, int H, int I, const uint16_t* w1, const uint16_t* w2,
+                             uint16_t* h_hi, uint16_t* h_lo, float* out, char* ws,
+                             bool plan_ready, hipStream_t stream) {
+  const SkLayout lo = sk_layout(T, k, L, 16, false);
+  const PlanOut po = plan_out(lo, ws, T, k, 16);
+  if (!plan_ready) {
+    hipLaunchKernelGGL(ffn_plan_kernel, dim3(1), dim3(1024), (size_t)(2 * (L + 1) + 16) * 4,
+                       stream, offsets, L, po);
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  return launch_ffn_dense(x, perm, k, H, I, T * k, w1, w2, po.plan, lo.pmax, h_hi, h_lo, out,
+                          stream);
+}
 }  // namespace
 
 bool ffn_sk_applies(const void* x, const void* w1, const void* w2, const void* out, int T, int k,
                     int L, int H, int I) {
   auto al = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
   if (!(al(x) && al(w1) && al(w2) && al(out))) return false;
-  if (pick_nt(T, k, L) == 1)
+  const int nt = pick_nt(T, k, L, H, I, false);
+  if (nt == 16) return true;  // the dense kernels' shape conditions hold
+  if (nt == 1)
     return H % UP_KUNIT_SHORT == 0 && I % DOWN_KUNIT == 0 && I % UP_ROWS == 0 &&
            H % DOWN_ROWS == 0;
   // the staged kernels address token rows with 32-bit byte offsets below 2^31
@@ -1498,13 +1527,15 @@ bool ffn_sk_applies(const void* x, const void* w1, const void* w2, const void* o
 // The plan the persistent kernels will read for these sizes, in the FFN's own
 // workspace `ws` (the part after h_hi / h_lo), for a caller that writes it
 // itself.
-PlanOut ffn_sk_plan_out(int T, int k, int L, bool f8, void* ws) {
-  const int nt = pick_nt(T, k, L);
+PlanOut ffn_sk_plan_out(int T, int k, int L, int H, int I, bool f8, void* ws) {
+  const int nt = pick_nt(T, k, L, H, I, f8);
   return plan_out(sk_layout(T, k, L, nt, f8), static_cast<char*>(ws), T, k, nt);
 }
 
+// The staged layout bounds the dense one (fewer passes, no counters or
+// slots), so the size does not depend on which of them runs.
 size_t ffn_sk_workspace_bytes(int T, int k, int L) {
-  const int nt = pick_nt(T, k, L);
+  const int nt = pick_staged_nt(T, k, L);
   const size_t a = sk_layout(T, k, L, nt, false).total;
   const size_t b = sk_layout(T, k, L, nt, true).total;  // the FP8 kernels' share of it
   return a > b ? a : b;
@@ -1515,7 +1546,8 @@ hipError_t launch_grouped_ffn_sk(const uint16_t* x, const int* perm, const int* 
                                  const uint16_t* w2, uint16_t* h_hi, uint16_t* h_lo, float* out,
                                  void* ws, bool plan_ready, hipStream_t stream) {
   char* w = static_cast<char*>(ws);
-  switch (pick_nt(T, k, L)) {
+  switch (pick_nt(T, k, L, H, I, false)) {
+    case 16: return launch_dense_path(x, perm, offsets, L, T, k, H, I, w1, w2, h_hi, h_lo, out, w, plan_ready, stream);
     case 1: return launch_sk_nt<1>(x, perm, offsets, L, T, k, H, I, w1, w2, nullptr, nullptr, h_hi, h_lo, out, w, plan_ready, stream);
     case 4: return launch_sk_nt<4>(x, perm, offsets, L, T, k, H, I, w1, w2, nullptr, nullptr, h_hi, h_lo, out, w, plan_ready, stream);
     default: return launch_sk_nt<8>(x, perm, offsets, L, T, k, H, I, w1, w2, nullptr, nullptr, h_hi, h_lo, out, w, plan_ready, stream);
@@ -1529,7 +1561,7 @@ bool ffn_sk_fp8_applies(const void* x, const void* w1q, const void* w2q, const v
                         int k, int L, int H, int I) {
   auto al = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
   if (!(al(x) && al(w1q) && al(w2q) && al(out))) return false;
-  if (pick_nt(T, k, L) == 1)
+  if (pick_nt(T, k, L, H, I, true) == 1)
     return H % UP8_KUNIT == 0 && I % DOWN8_KUNIT == 0 && I % UP8_ROWS == 0 && H % DOWN_ROWS == 0;
   // the staged kernels address token rows with 32-bit byte offsets below 2^31
   const size_t lim = (size_t)1 << 31;
@@ -1543,7 +1575,7 @@ hipError_t launch_grouped_ffn_sk_fp8(const uint16_t* x, const int* perm, const i
                                      uint16_t* h_hi, uint16_t* h_lo, float* out, void* ws,
                                      bool plan_ready, hipStream_t stream) {
   char* w = static_cast<char*>(ws);
-  switch (pick_nt(T, k, L)) {
+  switch (pick_nt(T, k, L, H, I, true)) {
     case 1: return launch_sk_nt<1>(x, perm, offsets, L, T, k, H, I, w1q, w2q, w1s, w2s, h_hi, h_lo, out, w, plan_ready, stream);
     case 4: return launch_sk_nt<4>(x, perm, offsets, L, T, k, H, I, w1q, w2q, w1s, w2s, h_hi, h_lo, out, w, plan_ready, stream);
     default: return launch_sk_nt<8>(x, perm, offsets, L, T, k, H, I, w1q, w2q, w1s, w2s, h_hi, h_lo, out, w, plan_ready, stream);

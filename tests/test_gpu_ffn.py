@@ -153,6 +153,31 @@ def test_ffn_prefill_share():
     check_ffn(384, 512, 256, 20, 4, 5, 6)
 
 
+# Dense path (at least 256 entries per local expert on average, H a multiple
+# of 256, I of 128): passes of 256 tokens, 256 x 256 tiles of weight rows and
+# tokens with both operands staged in LDS. Two passes per expert, a share,
+# passes filling every number of 16-token groups of the four token quarters,
+# one expert taking every token (four passes), an empty expert.
+@pytest.mark.parametrize("T,H,I,E,k,first,L", [(1024, 256, 256, 4, 2, 0, 4),
+                                               (2048, 512, 384, 8, 2, 2, 3),
+                                               (600, 768, 256, 2, 1, 0, 2)])
+def test_ffn_dense(T, H, I, E, k, first, L):
+    check_ffn(T, H, I, E, k, first, L)
+
+
+@pytest.mark.parametrize("counts", [[1, 17, 65, 129, 200, 255, 256, 257, 300, 511, 513, 600, 700],
+                                    [600, 0, 400]])
+def test_ffn_dense_partial_passes(counts):
+    ids = partial_pass_ids(counts)
+    check_ffn(len(ids), 256, 256, len(counts), 1, 0, len(counts), ids=ids)
+
+
+def test_ffn_dense_skewed():
+    T, E, k = 1024, 4, 2
+    ids = np.stack([np.zeros(T, np.int32), 1 + np.arange(T, dtype=np.int32) % 3], 1)
+    check_ffn(T, 256, 256, E, k, 0, E, ids=ids)
+
+
 def test_ffn_share_and_empty_experts():
     check_ffn(40, 128, 256, 16, 2, 3, 9)   # several local experts get no rows
 
@@ -216,9 +241,10 @@ def test_ffn_checked_path_misaligned_out():
 
 # An entry whose expanded index lies outside [0, T k) gathers a zero row on
 # every path: the element-wise kernels (ragged H), the K-split kernels (one
-# 16-token tile per pass) and the staged kernels (token rows in LDS).
+# 16-token tile per pass), the staged kernels (token rows in LDS) and the
+# dense kernels.
 @pytest.mark.parametrize("T,H,I,E,k", [(37, 200, 72, 5, 2), (32, 4096, 1024, 8, 2),
-                                       (256, 512, 512, 8, 2)])
+                                       (256, 512, 512, 8, 2), (1024, 256, 256, 4, 2)])
 def test_ffn_out_of_range_rows_are_zero(T, H, I, E, k):
     note(f"ffn out-of-range rows T={T} H={H} I={I} E={E} k={k}")
     x, w1, w2, ids = layer(5, T, H, I, E, k, 0, E)
@@ -239,9 +265,9 @@ def test_ffn_out_of_range_rows_are_zero(T, H, I, E, k):
 # The fixed order of every sum (in-block wave order, cross-block fixup in
 # block order) makes the output bitwise repeatable, with tiles cut between
 # blocks: the K-split up kernel cut by stream-K, and the staged kernels with a
-# whole round followed by cut tiles.
+# whole round followed by cut tiles; and on the dense kernels.
 @pytest.mark.parametrize("T,H,I,E,k", [(32, 4096, 1024, 8, 2), (40, 4096, 2048, 20, 2),
-                                       (3200, 512, 256, 300, 8)])
+                                       (3200, 512, 256, 300, 8), (1024, 256, 256, 4, 2)])
 def test_ffn_bitwise_repeatable(T, H, I, E, k):
     note(f"ffn repeatability T={T} H={H} I={I} E={E} k={k}")
     x, w1, w2, ids = layer(6, T, H, I, E, k, 0, E)
