@@ -26,8 +26,12 @@
 // operand is the hi and lo halves of the intermediate). Rows past a pass's
 // entries carry a buffer offset beyond the resource, which reads zeros with
 // no memory request. Within a block, 16-byte piece q of row r sits at slot
-// q ^ s(r), s(r) = ((r >> 1) ^ (r >> 3)) & 3, so the MFMA fragment reads
-// (16 rows, one piece each, per 16 lanes) touch every LDS bank once.
+// q ^ ((r >> 1) & 3): the MFMA fragment reads (16 rows, one piece each, per
+// 16 lanes) then run without bank conflicts. Measured on MI355X with a probe
+// of such reads (16 waves per CU): 490 B/ns per CU conflict-free, against
+// 280 B/ns and 4 conflict cycles per read for rows without the XOR, for
+// rows padded to 144 bytes, for q ^ (r & 3) and for q ^ (((r >> 1) ^
+// (r >> 3)) & 3).
 //
 // Pipeline: one block barrier per stage. At stage i a wave waits for its own
 // loads of stage i (vmcnt), meets the block (so every wave's loads of stage i
@@ -66,7 +70,7 @@ constexpr uint32_t kDnPad = 0x80000000u;  // a buffer offset past every resource
 typedef u16x8 dn_buf_t[DN_ROWS * 4];
 typedef __attribute__((address_space(3))) void lds_void_t;
 
-__device__ __forceinline__ int dn_swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+__device__ __forceinline__ int dn_swz(int r) { return (r >> 1) & 3; }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t dn_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
@@ -233,6 +237,7 @@ __device__ __forceinline__ void dn_body(const uint16_t* __restrict__ b0src,
   const int K = UP ? H : I;
   const int C = K / DN_K;
   const int G = UP ? I / DN_UP_COLS : H / DN_ROWS;
+  if (plan[1] != 1) return;  // the staged kernels take this plan
   const int P = plan[0];
   const int TT = P * G;
   const int b = xcd_block(blockIdx.x, NB);
@@ -435,15 +440,21 @@ bool ffn_dense_shape_ok(int T, int k, int H, int I) {
 int ffn_dense_pass_tokens() { return DN_TOK; }
 
 // The up and down kernels over the pass plan `plan` (passes of at most 256
-// entries; written beforehand).
-hipError_t launch_ffn_dense(const uint16_t* x, const int* perm, int k, int H, int I, int nmax,
-                            const uint16_t* w1, const uint16_t* w2, const int* plan, int pmax,
-                            uint16_t* h_hi, uint16_t* h_lo, float* out, hipStream_t stream) {
+// entries, written beforehand); they return at once unless the plan names
+// the dense kernels.
+hipError_t launch_ffn_dense_up(const uint16_t* x, const int* perm, int k, int H, int I, int nmax,
+                               const uint16_t* w1, const int* plan, int pmax, uint16_t* h_hi,
+                               uint16_t* h_lo, hipStream_t stream) {
   const int nb = ffn_dense_blocks();
   hipLaunchKernelGGL(ffn_dense_up_kernel, dim3(nb), dim3(DN_THREADS), 0, stream, x, perm, k, H, I,
                      nmax, w1, plan, pmax, h_hi, h_lo, nb);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
+  return hipGetLastError();
+}
+
+hipError_t launch_ffn_dense_down(const uint16_t* h_hi, const uint16_t* h_lo, int k, int H, int I,
+                                 int nmax, const uint16_t* w2, const int* plan, int pmax,
+                                 float* out, hipStream_t stream) {
+  const int nb = ffn_dense_blocks();
   hipLaunchKernelGGL(ffn_dense_down_kernel, dim3(nb), dim3(DN_THREADS), 0, stream, h_hi, h_lo, k,
                      H, I, nmax, w2, plan, pmax, out, nb);
   return hipGetLastError();

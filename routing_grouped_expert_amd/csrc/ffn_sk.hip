@@ -49,9 +49,12 @@ namespace moe {
 int ffn_dense_blocks();
 bool ffn_dense_shape_ok(int T, int k, int H, int I);
 int ffn_dense_pass_tokens();
-hipError_t launch_ffn_dense(const uint16_t* x, const int* perm, int k, int H, int I, int nmax,
-                            const uint16_t* w1, const uint16_t* w2, const int* plan, int pmax,
-                            uint16_t* h_hi, uint16_t* h_lo, float* out, hipStream_t stream);
+hipError_t launch_ffn_dense_up(const uint16_t* x, const int* perm, int k, int H, int I, int nmax,
+                               const uint16_t* w1, const int* plan, int pmax, uint16_t* h_hi,
+                               uint16_t* h_lo, hipStream_t stream);
+hipError_t launch_ffn_dense_down(const uint16_t* h_hi, const uint16_t* h_lo, int k, int H, int I,
+                                 int nmax, const uint16_t* w2, const int* plan, int pmax,
+                                 float* out, hipStream_t stream);
 
 namespace {
 // Tile shapes, measured on MI355X at the decode shape (T32 H4096 I14336 E8
@@ -914,9 +917,15 @@ constexpr int PF_STEPS = PF_K / 32;
 constexpr int PF_GROUPS = 2;                        // 16-row MFMA groups per wave
 constexpr int PF_ROWS = PF_WAVES * 16 * PF_GROUPS;  // weight rows per tile
 constexpr int PF_UP_COLS = PF_ROWS / 2;             // h columns per up tile
-constexpr int PF_PAD = 8;                           // bf16 padding per LDS row
 
-typedef uint16_t pf_row_t[PF_K + PF_PAD];
+// A staged token row holds one 64-wide chunk (128 bytes, eight 16-byte
+// pieces); piece q of row n sits at slot q ^ (n % 8), so both the stores of
+// whole rows and the MFMA fragment reads (16 rows, one piece each, per 16
+// lanes) run without LDS bank conflicts. Rows padded to 144 bytes instead
+// took 4 conflict cycles per fragment read (a probe of such reads on MI355X:
+// 270 against 495 B/ns per CU).
+typedef uint16_t pf_row_t[PF_K];
+__device__ __forceinline__ int pf_slot(int n, int q) { return ((q ^ n) & 7) * 8; }
 
 // One 64-wide chunk of NR B rows: thread t holds pieces t, t + 512, ...
 // (piece = row n, 16-byte column q).
@@ -952,7 +961,7 @@ __device__ __forceinline__ void pf_stage_store(const PfStage<NR>& st, pf_row_t* 
   for (int i = 0; i < PfStage<NR>::PER; ++i) {
     const int piece = tid + PF_THREADS * i;
     if (PfStage<NR>::PIECES % PF_THREADS == 0 || piece < PfStage<NR>::PIECES)
-      *reinterpret_cast<u16x8*>(&dst[piece / (PF_K / 8)][(piece % (PF_K / 8)) * 8]) = st.v[i];
+      *reinterpret_cast<u16x8*>(&dst[piece / (PF_K / 8)][pf_slot(piece / (PF_K / 8), piece % (PF_K / 8))]) = st.v[i];
   }
 }
 
@@ -990,12 +999,12 @@ __device__ __forceinline__ void pf_mma(const PfA<F8>& a, const pf_row_t* b0, con
       if (nt >= nv) break;
       const int n = nt * 16 + (lane & 15);
       const int c = F8 ? (lane >> 4) * 16 + st * 8 : st * 32 + (lane >> 4) * 8;
-      const bf16x8 h = *reinterpret_cast<const bf16x8*>(&b0[n][c]);
+      const bf16x8 h = *reinterpret_cast<const bf16x8*>(&b0[n][pf_slot(n, c / 8)]);
 #pragma unroll
       for (int q = 0; q < PF_GROUPS; ++q)
         acc[q * NT + nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w[q], h, acc[q * NT + nt], 0, 0, 0);
       if (!UP) {
-        const bf16x8 l = *reinterpret_cast<const bf16x8*>(&b1[n][c]);
+        const bf16x8 l = *reinterpret_cast<const bf16x8*>(&b1[n][pf_slot(n, c / 8)]);
 #pragma unroll
         for (int q = 0; q < PF_GROUPS; ++q)
           acc[q * NT + nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w[q], l, acc[q * NT + nt], 0, 0, 0);
@@ -1106,6 +1115,7 @@ __global__ __launch_bounds__(PF_THREADS, (NT <= 4 && UP) ? 4 : 1) void ffn_pf_ke
   __shared__ u16x8 slab_t[FL ? PF_WAVES : 1][FL ? PF_GROUPS * 128 : 1];
   __shared__ int fix_flag;
   const PlanRO pv = plan_ro(plan, pmax);
+  if (pv.hdr[1] != 0) return;  // the dense kernels take this plan
   const int P = pv.hdr[0];
   const int K = UP ? H : I;
   const int G = UP ? I / PF_UP_COLS : H / PF_ROWS, C = K / PF_K;
@@ -1333,25 +1343,28 @@ int resident_blocks(int threads = 256, int cap = 8) {
 // Token tiles (of 16) per pass, from twice the mean entries per local expert
 // (an expert with more entries takes further passes, each reading its weights
 // again), capped by T (a token picks an expert at most once). 1: the K-split
-// kernels; 4 or 8: the kernels with token rows staged in LDS; 16: the dense
-// kernels (ffn_dense.hip: passes of 256 tokens, both operands staged in LDS)
-// once the mean reaches kDenseMean entries per expert and the shape suits
-// them (bf16 weights only). Between 16 and 32 the staged kernels with 4 tiles
+// kernels; 4 or 8: the kernels with token rows staged in LDS. With 8, the
+// dense kernels (ffn_dense.hip: passes of 256 tokens, both operands staged in
+// LDS) may take the call instead, which the plan writer decides from the
+// local entry counts (at least kDenseMean per local expert). Between 16 and 32 the staged kernels with 4 tiles
 // win over 2-tile passes: on the fine-grained shape (T512 H7168 I2048 E256
 // top-8) 4.05 ms against 5.46 ms, mostly by not repeating passes for the
 // experts above 32 entries. Staged kernels at 2 tiles (weights two chunks
 // ahead, at most 120 VGPRs) took the same shape's grouped FFN to 3.79 ms
 // against 3.69 ms at 4 tiles.
-constexpr long kDenseMean = 256;
-int pick_staged_nt(int T, int k, int L) {
+constexpr int kDenseMean = 112;
+int pick_nt(int T, int k, int L) {
   const long bound = T;
   const long twice_mean = L > 0 ? (2L * T * k + L - 1) / L : bound;
   const long want = twice_mean < bound ? twice_mean : bound;
   return want <= 16 ? 1 : want <= 64 ? 4 : 8;
 }
-int pick_nt(int T, int k, int L, int H, int I, bool f8) {
-  if (!f8 && L > 0 && (long)T * k >= kDenseMean * L && ffn_dense_shape_ok(T, k, H, I)) return 16;
-  return pick_staged_nt(T, k, L);
+// Whether the dense kernels may take the call: the local entries can reach
+// kDenseMean per local expert (T k of them at most), the shape suits them,
+// bf16 weights. The plan writer then decides from the actual counts.
+bool dense_possible(int T, int k, int L, int H, int I, bool f8) {
+  return !f8 && L > 0 && (long)T * k >= (long)kDenseMean * L && pick_nt(T, k, L) == 8 &&
+         ffn_dense_shape_ok(T, k, H, I);
 }
 
 size_t a256(size_t n) { return (n + 255) & ~(size_t)255; }
@@ -1378,7 +1391,6 @@ int down_blocks(bool f8) {
 
 int blocks_for(int NT, bool up, bool f8) {
   switch (NT) {
-    case 16: return ffn_dense_blocks();
     case 1: return up ? up_blocks<1>(f8) : down_blocks<1>(f8);
     case 4: return up ? up_blocks<4>(f8) : down_blocks<4>(f8);
     default: return up ? up_blocks<8>(f8) : down_blocks<8>(f8);
@@ -1406,20 +1418,18 @@ SkLayout sk_layout(int T, int k, int L, int NT, bool f8) {
   o.plan = 0;
   o.subs = NT == 1 ? 1 : PF_WAVES;
   o.counters = a256((size_t)(4 + 3 * o.pmax) * 4);
-  if (NT == 16) {  // the dense kernels: whole tiles only, no counters or slots
-    o.slots = o.total = o.counters;
-    return o;
-  }
   o.slots = o.counters + a256((size_t)2 * o.subs * nbm * 4);
   const int slot_n = NT == 1 ? std::max({2 * UP_RG, 2 * UP8_RG, DOWN_GROUPS}) : 4 * NT;
   o.total = o.slots + a256((size_t)2 * o.subs * nbm * slot_n * kWave * 16);
   return o;
 }
 
-PlanOut plan_out(const SkLayout& lo, char* ws, int T, int k, int NT) {
+// dense: the dense kernels may take the call (the plan writer decides).
+PlanOut plan_out(const SkLayout& lo, char* ws, int T, int k, int NT, bool dense) {
   const int nbm = lo.nb_up > lo.nb_down ? lo.nb_up : lo.nb_down;
   return PlanOut{reinterpret_cast<int*>(ws + lo.plan), lo.pmax, NT * 16, T * k,
-                 reinterpret_cast<int*>(ws + lo.counters), NT == 16 ? 0 : 2 * lo.subs * nbm};
+                 reinterpret_cast<int*>(ws + lo.counters), 2 * lo.subs * nbm,
+                 dense ? ffn_dense_pass_tokens() : 0, kDenseMean};
 }
 
 // plan_ready: the plan and zeroed counters are already in the workspace
@@ -1432,7 +1442,8 @@ hipError_t launch_sk_nt(const uint16_t* x, const int* perm, const int* offsets, 
   // s1 / s2 non-null: FP8 weight codes with row scales
   const bool f8 = s1 != nullptr;
   const SkLayout lo = sk_layout(T, k, L, NT, f8);
-  const PlanOut po = plan_out(lo, ws, T, k, NT);
+  const bool dense = NT == 8 && dense_possible(T, k, L, H, I, f8);
+  const PlanOut po = plan_out(lo, ws, T, k, NT, dense);
   int* plan = po.plan;
   int* counters = po.counters;
   f32x4* slots = reinterpret_cast<f32x4*>(ws + lo.slots);
@@ -1470,6 +1481,13 @@ hipError_t launch_sk_nt(const uint16_t* x, const int* perm, const int* offsets, 
   }
   err = hipGetLastError();
   if (err != hipSuccess) return err;
+  // The dense kernels' turn when the plan writer chose them (the staged
+  // kernels then return at once, and the other way round).
+  if (dense) {
+    err = launch_ffn_dense_up(x, perm, k, H, I, nmax, static_cast<const uint16_t*>(w1), plan,
+                              lo.pmax, h_hi, h_lo, stream);
+    if (err != hipSuccess) return err;
+  }
   if constexpr (NT == 1) {
     if (f8)
       hipLaunchKernelGGL((ffn_down_sk_kernel<DOWN_GROUPS, DOWN8_STEPS, true>), dim3(lo.nb_down),
@@ -1489,23 +1507,10 @@ hipError_t launch_sk_nt(const uint16_t* x, const int* perm, const int* offsets, 
                          stream, h_hi, h_lo, perm, k, H, I, nmax, w2, s2, plan, lo.pmax, slots,
                          counters + lo.subs * nbm, h_hi, h_lo, out, lo.nb_down);
   }
-  return hipGetLastError();
-}
-// The dense kernels (ffn_dense.hip) on the plan of passes of 256 entries.
-hipError_t launch_dense_path(const uint16_t* x, const int* perm, const int* offsets, int L, int T,
-                             int k, int H, int I, const uint16_t* w1, const uint16_t* w2,
-                             uint16_t* h_hi, uint16_t* h_lo, float* out, char* ws,
-                             bool plan_ready, hipStream_t stream) {
-  const SkLayout lo = sk_layout(T, k, L, 16, false);
-  const PlanOut po = plan_out(lo, ws, T, k, 16);
-  if (!plan_ready) {
-    hipLaunchKernelGGL(ffn_plan_kernel, dim3(1), dim3(1024), (size_t)(2 * (L + 1) + 16) * 4,
-                       stream, offsets, L, po);
-    const hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
-  }
-  return launch_ffn_dense(x, perm, k, H, I, T * k, w1, w2, po.plan, lo.pmax, h_hi, h_lo, out,
-                          stream);
+  err = hipGetLastError();
+  if (err != hipSuccess || !dense) return err;
+  return launch_ffn_dense_down(h_hi, h_lo, k, H, I, nmax, static_cast<const uint16_t*>(w2), plan,
+                               lo.pmax, out, stream);
 }
 }  // namespace
 
@@ -1513,9 +1518,7 @@ bool ffn_sk_applies(const void* x, const void* w1, const void* w2, const void* o
                     int L, int H, int I) {
   auto al = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
   if (!(al(x) && al(w1) && al(w2) && al(out))) return false;
-  const int nt = pick_nt(T, k, L, H, I, false);
-  if (nt == 16) return true;  // the dense kernels' shape conditions hold
-  if (nt == 1)
+  if (pick_nt(T, k, L) == 1)
     return H % UP_KUNIT_SHORT == 0 && I % DOWN_KUNIT == 0 && I % UP_ROWS == 0 &&
            H % DOWN_ROWS == 0;
   // the staged kernels address token rows with 32-bit byte offsets below 2^31
@@ -1528,14 +1531,15 @@ bool ffn_sk_applies(const void* x, const void* w1, const void* w2, const void* o
 // workspace `ws` (the part after h_hi / h_lo), for a caller that writes it
 // itself.
 PlanOut ffn_sk_plan_out(int T, int k, int L, int H, int I, bool f8, void* ws) {
-  const int nt = pick_nt(T, k, L, H, I, f8);
-  return plan_out(sk_layout(T, k, L, nt, f8), static_cast<char*>(ws), T, k, nt);
+  const int nt = pick_nt(T, k, L);
+  return plan_out(sk_layout(T, k, L, nt, f8), static_cast<char*>(ws), T, k, nt,
+                  nt == 8 && dense_possible(T, k, L, H, I, f8));
 }
 
-// The staged layout bounds the dense one (fewer passes, no counters or
-// slots), so the size does not depend on which of them runs.
+// The dense kernels read only the plan, which the staged layout holds (its
+// passes of 128 entries outnumber passes of 256).
 size_t ffn_sk_workspace_bytes(int T, int k, int L) {
-  const int nt = pick_staged_nt(T, k, L);
+  const int nt = pick_nt(T, k, L);
   const size_t a = sk_layout(T, k, L, nt, false).total;
   const size_t b = sk_layout(T, k, L, nt, true).total;  // the FP8 kernels' share of it
   return a > b ? a : b;
@@ -1546,8 +1550,7 @@ hipError_t launch_grouped_ffn_sk(const uint16_t* x, const int* perm, const int* 
                                  const uint16_t* w2, uint16_t* h_hi, uint16_t* h_lo, float* out,
                                  void* ws, bool plan_ready, hipStream_t stream) {
   char* w = static_cast<char*>(ws);
-  switch (pick_nt(T, k, L, H, I, false)) {
-    case 16: return launch_dense_path(x, perm, offsets, L, T, k, H, I, w1, w2, h_hi, h_lo, out, w, plan_ready, stream);
+  switch (pick_nt(T, k, L)) {
     case 1: return launch_sk_nt<1>(x, perm, offsets, L, T, k, H, I, w1, w2, nullptr, nullptr, h_hi, h_lo, out, w, plan_ready, stream);
     case 4: return launch_sk_nt<4>(x, perm, offsets, L, T, k, H, I, w1, w2, nullptr, nullptr, h_hi, h_lo, out, w, plan_ready, stream);
     default: return launch_sk_nt<8>(x, perm, offsets, L, T, k, H, I, w1, w2, nullptr, nullptr, h_hi, h_lo, out, w, plan_ready, stream);
@@ -1561,7 +1564,7 @@ bool ffn_sk_fp8_applies(const void* x, const void* w1q, const void* w2q, const v
                         int k, int L, int H, int I) {
   auto al = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
   if (!(al(x) && al(w1q) && al(w2q) && al(out))) return false;
-  if (pick_nt(T, k, L, H, I, true) == 1)
+  if (pick_nt(T, k, L) == 1)
     return H % UP8_KUNIT == 0 && I % DOWN8_KUNIT == 0 && I % UP8_ROWS == 0 && H % DOWN_ROWS == 0;
   // the staged kernels address token rows with 32-bit byte offsets below 2^31
   const size_t lim = (size_t)1 << 31;
@@ -1575,7 +1578,7 @@ hipError_t launch_grouped_ffn_sk_fp8(const uint16_t* x, const int* perm, const i
                                      uint16_t* h_hi, uint16_t* h_lo, float* out, void* ws,
                                      bool plan_ready, hipStream_t stream) {
   char* w = static_cast<char*>(ws);
-  switch (pick_nt(T, k, L, H, I, true)) {
+  switch (pick_nt(T, k, L)) {
     case 1: return launch_sk_nt<1>(x, perm, offsets, L, T, k, H, I, w1q, w2q, w1s, w2s, h_hi, h_lo, out, w, plan_ready, stream);
     case 4: return launch_sk_nt<4>(x, perm, offsets, L, T, k, H, I, w1q, w2q, w1s, w2s, h_hi, h_lo, out, w, plan_ready, stream);
     default: return launch_sk_nt<8>(x, perm, offsets, L, T, k, H, I, w1q, w2q, w1s, w2s, h_hi, h_lo, out, w, plan_ready, stream);

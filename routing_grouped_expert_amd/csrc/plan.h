@@ -9,8 +9,9 @@
 
 namespace moe {
 
-// Plan layout (ints): [0] passes P, then pass_expert[pmax], pass_beg[pmax],
-// pass_cnt[pmax].
+// Plan layout (ints): [0] passes P, [1] kernel family (0: the staged or
+// K-split kernels, 1: the dense kernels), then pass_expert[pmax],
+// pass_beg[pmax], pass_cnt[pmax].
 struct PlanView {
   int* hdr;
   int* expert;
@@ -23,12 +24,17 @@ __device__ __forceinline__ PlanView plan_view(int* plan, int pmax) {
 }
 
 // Where a plan goes: `plan` (NULL: no plan to write), passes of at most nr
-// entries over entries [0, nmax), and `ncounters` counters to zero.
+// entries over entries [0, nmax), and `ncounters` counters to zero. With
+// nr_dense > 0 the writer picks the dense kernels, with passes of nr_dense
+// entries, when the local entries reach dense_min per local expert: only the
+// device knows the entry counts, and on an expert share they can be a small
+// fraction of the T k selections.
 struct PlanOut {
   int* plan;
   int pmax, nr, nmax;
   int* counters;
   int ncounters;
+  int nr_dense, dense_min;
 };
 
 // The plan from the exclusive scan `off` of the local experts' entry counts
@@ -37,10 +43,13 @@ struct PlanOut {
 // (counter_stride = 1) or shared out over many (see callers).
 __device__ inline void write_ffn_plan(const int* off, int L, const PlanOut& po, int* s_pass) {
   const int tid = threadIdx.x, nt = blockDim.x;
+  const int n_local = max(0, min(off[L], po.nmax)) - max(0, min(off[0], po.nmax));
+  const bool dense = po.nr_dense > 0 && (long)n_local >= (long)po.dense_min * L;
+  const int nr = dense ? po.nr_dense : po.nr;
   for (int i = tid; i < L; i += nt) {
     const int b = max(0, min(off[i], po.nmax));
     const int e = max(b, min(off[i + 1], po.nmax));
-    s_pass[i] = (e - b + po.nr - 1) / po.nr;
+    s_pass[i] = (e - b + nr - 1) / nr;
   }
   __syncthreads();
   block_exclusive_scan(s_pass, L, s_pass + L + 1);
@@ -48,13 +57,16 @@ __device__ inline void write_ffn_plan(const int* off, int L, const PlanOut& po, 
   for (int i = tid; i < L; i += nt) {
     const int b = max(0, min(off[i], po.nmax));
     const int e = max(b, min(off[i + 1], po.nmax));
-    for (int q = s_pass[i], t = b; t < e; ++q, t += po.nr) {
+    for (int q = s_pass[i], t = b; t < e; ++q, t += nr) {
       pv.expert[q] = i;
       pv.beg[q] = t;
-      pv.cnt[q] = min(po.nr, e - t);
+      pv.cnt[q] = min(nr, e - t);
     }
   }
-  if (tid == 0) pv.hdr[0] = s_pass[L];
+  if (tid == 0) {
+    pv.hdr[0] = s_pass[L];
+    pv.hdr[1] = dense ? 1 : 0;
+  }
 }
 
 }  // namespace moe

@@ -153,8 +153,8 @@ def test_ffn_prefill_share():
     check_ffn(384, 512, 256, 20, 4, 5, 6)
 
 
-# Dense path (at least 256 entries per local expert on average, H a multiple
-# of 256, I of 128): passes of 256 tokens, 256 x 256 tiles of weight rows and
+# Dense path (at least 112 local entries per local expert on average, H a
+# multiple of 256, I of 128): passes of 256 tokens, 256 x 256 tiles of weight rows and
 # tokens with both operands staged in LDS. Two passes per expert, a share,
 # passes filling every number of 16-token groups of the four token quarters,
 # one expert taking every token (four passes), an empty expert.
