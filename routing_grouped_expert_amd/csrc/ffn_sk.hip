@@ -1417,7 +1417,7 @@ SkLayout sk_layout(int T, int k, int L, int NT, bool f8) {
   const int nbm = o.nb_up > o.nb_down ? o.nb_up : o.nb_down;
   o.plan = 0;
   o.subs = NT == 1 ? 1 : PF_WAVES;
-  o.counters = a256((size_t)(4 + 3 * o.pmax) * 4);
+  o.counters = a256((size_t)(4 + kPlanArrays * o.pmax) * 4);
   o.slots = o.counters + a256((size_t)2 * o.subs * nbm * 4);
   const int slot_n = NT == 1 ? std::max({2 * UP_RG, 2 * UP8_RG, DOWN_GROUPS}) : 4 * NT;
   o.total = o.slots + a256((size_t)2 * o.subs * nbm * slot_n * kWave * 16);

@@ -11,16 +11,21 @@ namespace moe {
 
 // Plan layout (ints): [0] passes P, [1] kernel family (0: the staged or
 // K-split kernels, 1: the dense kernels), then pass_expert[pmax],
-// pass_beg[pmax], pass_cnt[pmax].
+// pass_beg[pmax], pass_cnt[pmax], and per pass its expert's first pass
+// pass_first[pmax] and number of passes pass_num[pmax].
+constexpr int kPlanArrays = 5;
 struct PlanView {
   int* hdr;
   int* expert;
   int* beg;
   int* cnt;
+  int* first;
+  int* num;
 };
 
 __device__ __forceinline__ PlanView plan_view(int* plan, int pmax) {
-  return PlanView{plan, plan + 4, plan + 4 + pmax, plan + 4 + 2 * pmax};
+  return PlanView{plan, plan + 4, plan + 4 + pmax, plan + 4 + 2 * pmax, plan + 4 + 3 * pmax,
+                  plan + 4 + 4 * pmax};
 }
 
 // Where a plan goes: `plan` (NULL: no plan to write), passes of at most nr
@@ -57,10 +62,13 @@ __device__ inline void write_ffn_plan(const int* off, int L, const PlanOut& po, 
   for (int i = tid; i < L; i += nt) {
     const int b = max(0, min(off[i], po.nmax));
     const int e = max(b, min(off[i + 1], po.nmax));
-    for (int q = s_pass[i], t = b; t < e; ++q, t += nr) {
+    const int q0 = s_pass[i], np = s_pass[i + 1] - q0;
+    for (int q = q0, t = b; t < e; ++q, t += nr) {
       pv.expert[q] = i;
       pv.beg[q] = t;
       pv.cnt[q] = min(nr, e - t);
+      pv.first[q] = q0;
+      pv.num[q] = np;
     }
   }
   if (tid == 0) {
