@@ -17,7 +17,8 @@
 // 128 tokens. Here a tile is 256 weight rows x 256 tokens (256 flop per
 // weight byte within the block, and passes of one expert that run together
 // on an XCD share its weight lines in L2), computed by 8 waves of 128 rows x
-// 64 tokens each (v_mfma_f32_16x16x32_bf16, fp32 accumulate).
+// 64 tokens each (v_mfma_f32_16x16x32_bf16, fp32 accumulate; a wave quarter
+// takes every fourth 16-token group, see dn_groups).
 //
 // Staging: each 32-wide K stage of both operands goes HBM/L2 -> LDS by
 // buffer loads that write LDS directly (one 1 KB block of 16 rows x 64 bytes
@@ -190,6 +191,16 @@ __device__ __forceinline__ int dn_frag_slot(int lane) {
   return r * 4 + ((lane >> 4) ^ dn_swz(r));
 }
 
+// The 16 token groups of a pass are dealt to the four wave quarters
+// strided (quarter w takes groups w, w + 4, w + 8, w + 12), so that the two
+// waves of each SIMD share the work of a partly filled pass evenly; this is
+// how many of its groups quarter wc multiplies for a pass of cnt entries
+// (wave-uniform; the valid groups are the first ones).
+__device__ __forceinline__ int dn_groups(int cnt, int wc) {
+  const int ng = (cnt + 15) >> 4;
+  return __builtin_amdgcn_readfirstlane(min(4, max(0, (ng - wc + 3) >> 2)));
+}
+
 // The LDS stage slots: S slots of 2 (up) or 3 (down) operand regions of
 // 16 KB: the weight tile, the token rows and, for the down projection, the
 // lo half of the intermediate.
@@ -205,7 +216,7 @@ __device__ __forceinline__ void dn_read(DnFrags& f, const u16x8* wa, const u16x8
 #pragma unroll
   for (int i = 0; i < 8; ++i) f.a[i] = __builtin_bit_cast(bf16x8, wa[i * 64]);
 #pragma unroll
-  for (int t = 0; t < 4; ++t) f.b[t] = __builtin_bit_cast(bf16x8, wb[t * 64]);
+  for (int t = 0; t < 4; ++t) f.b[t] = __builtin_bit_cast(bf16x8, wb[t * 4 * 64]);
 }
 
 // The up projection's body. A stage is one 32-wide K slice of the weight and
@@ -233,13 +244,13 @@ __device__ __forceinline__ void dn_body_up(const uint16_t* __restrict__ x,
   if (b >= TT) return;
   const int tid = threadIdx.x, lane = tid % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-  const int wr = wave & 1, wc = wave >> 1;  // 128-row half, 64-token quarter
+  const int wr = wave & 1, wc = wave >> 1;  // 128-row half, token quarter
   const u32x4 rb0 = dn_rsrc4(x, (uint32_t)((size_t)(nmax / k) * H * 2));
   const uint32_t lds0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)lds;
   // this lane's fragment slots: weight rows of its half, tokens of its quarter
   const int fs = dn_frag_slot(lane);
   const u16x8* const fa = lds + (wr * 8) * 64 + fs;
-  const u16x8* const fb = lds + DN_REGION + (wc * 4) * 64 + fs;
+  const u16x8* const fb = lds + DN_REGION + wc * 64 + fs;
 
   // issue side: stage `issued` is the next to load
   DnIssue is;
@@ -287,7 +298,7 @@ __device__ __forceinline__ void dn_body_up(const uint16_t* __restrict__ x,
   DnTile cur = dn_tile(plan, pmax, b, G);
   int kc = 0;  // stage of the current tile
   int c = 0;   // stage of the block
-  int nv = __builtin_amdgcn_readfirstlane(min(4, max(0, (cur.cnt - wc * 64 + 15) >> 4)));
+  int nv = dn_groups(cur.cnt, wc);
   f32x4 acc[32];
 #pragma unroll
   for (int i = 0; i < 32; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -297,7 +308,7 @@ __device__ __forceinline__ void dn_body_up(const uint16_t* __restrict__ x,
     typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      const int n = wc * 64 + t * 16 + (lane & 15);
+      const int n = (t * 4 + wc) * 16 + (lane & 15);
       if (n < cur.cnt) {
 #pragma unroll
         for (int f = 0; f < 4; ++f) {
@@ -350,7 +361,7 @@ __device__ __forceinline__ void dn_body_up(const uint16_t* __restrict__ x,
       const int nt = cur.t + NB;
       if (nt >= TT) return false;
       cur = dn_tile(plan, pmax, nt, G);
-      nv = __builtin_amdgcn_readfirstlane(min(4, max(0, (cur.cnt - wc * 64 + 15) >> 4)));
+      nv = dn_groups(cur.cnt, wc);
     }
     return true;
   };
@@ -365,8 +376,9 @@ __device__ __forceinline__ void dn_body_up(const uint16_t* __restrict__ x,
 
 // The down projection's fragments of one stage for one wave, read from LDS
 // in one asm block that also waits for them: the weight fragments (8 blocks
-// of 1 KB from byte address `a`), the hi fragments (4 blocks from `b`) and
-// the lo fragments (4 blocks from `c`), each lane at its fragment slot. The
+// of 1 KB from byte address `a`), the hi fragments (every fourth 1 KB block
+// from `b`: the wave quarter's token groups) and the lo fragments (likewise
+// from `c`), each lane at its fragment slot. The
 // loads that fill a stage are published to the block by the stage's explicit
 // wait and barrier. The outputs are early-clobber: the asm's later reads
 // still use the address registers, which no output may share.
@@ -382,13 +394,13 @@ __device__ __forceinline__ void dn_frags(bf16x8 (&af)[8], bf16x8 (&bf)[4], bf16x
       "ds_read_b128 %6, %16 offset:6144\n"
       "ds_read_b128 %7, %16 offset:7168\n"
       "ds_read_b128 %8, %17\n"
-      "ds_read_b128 %9, %17 offset:1024\n"
-      "ds_read_b128 %10, %17 offset:2048\n"
-      "ds_read_b128 %11, %17 offset:3072\n"
+      "ds_read_b128 %9, %17 offset:4096\n"
+      "ds_read_b128 %10, %17 offset:8192\n"
+      "ds_read_b128 %11, %17 offset:12288\n"
       "ds_read_b128 %12, %18\n"
-      "ds_read_b128 %13, %18 offset:1024\n"
-      "ds_read_b128 %14, %18 offset:2048\n"
-      "ds_read_b128 %15, %18 offset:3072\n"
+      "ds_read_b128 %13, %18 offset:4096\n"
+      "ds_read_b128 %14, %18 offset:8192\n"
+      "ds_read_b128 %15, %18 offset:12288\n"
       "s_waitcnt lgkmcnt(0)\n"
       : "=&v"(af[0]), "=&v"(af[1]), "=&v"(af[2]), "=&v"(af[3]), "=&v"(af[4]), "=&v"(af[5]),
         "=&v"(af[6]), "=&v"(af[7]), "=&v"(bf[0]), "=&v"(bf[1]), "=&v"(bf[2]), "=&v"(bf[3]),
@@ -431,7 +443,7 @@ __device__ __forceinline__ void dn_body_down(const uint16_t* __restrict__ h_hi,
   const uint32_t lds0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)lds;
   const uint32_t fs = (uint32_t)dn_frag_slot(lane) * 16u;
   const uint32_t fa = lds0 + (uint32_t)(wr * 8) * 1024u + fs;
-  const uint32_t fb = lds0 + DN_REGION * 16u + (uint32_t)(wc * 4) * 1024u + fs;
+  const uint32_t fb = lds0 + DN_REGION * 16u + (uint32_t)wc * 1024u + fs;
 
   DnIssue is;
   is.t = b;
@@ -464,7 +476,7 @@ __device__ __forceinline__ void dn_body_down(const uint16_t* __restrict__ h_hi,
 
   DnTile cur = dn_tile(plan, pmax, b, G);
   int kc = 0, done = 0;
-  int nv = __builtin_amdgcn_readfirstlane(min(4, max(0, (cur.cnt - wc * 64 + 15) >> 4)));
+  int nv = dn_groups(cur.cnt, wc);
   f32x4 acc[32];
 #pragma unroll
   for (int i = 0; i < 32; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -494,7 +506,7 @@ __device__ __forceinline__ void dn_body_down(const uint16_t* __restrict__ h_hi,
     if (++kc == C) {
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        const int n = wc * 64 + t * 16 + (lane & 15);
+        const int n = (t * 4 + wc) * 16 + (lane & 15);
         if (n < cur.cnt) {
 #pragma unroll
           for (int f = 0; f < 8; ++f) {
@@ -509,7 +521,7 @@ __device__ __forceinline__ void dn_body_down(const uint16_t* __restrict__ h_hi,
       const int nt = cur.t + NB;
       if (nt >= TT) return;
       cur = dn_tile(plan, pmax, nt, G);
-      nv = __builtin_amdgcn_readfirstlane(min(4, max(0, (cur.cnt - wc * 64 + 15) >> 4)));
+      nv = dn_groups(cur.cnt, wc);
     }
   }
 }
