@@ -79,11 +79,12 @@ def log(msg):
 
 
 def ffn_source_digest():
-    """Digest of the grouped-FFN code (ffn.hip, ffn_sk.hip, device.h) with
-    line comments, trailing blanks and empty lines removed, so that editing a
-    comment does not retire a committed counter summary."""
+    """Digest of the grouped-FFN code (ffn.hip, ffn_sk.hip, ffn_dense.hip,
+    plan.h, device.h) with line comments, trailing blanks and empty lines
+    removed, so that editing a comment does not retire a committed counter
+    summary."""
     h = hashlib.sha256()
-    for name in ("ffn.hip", "ffn_sk.hip", "device.h"):
+    for name in ("ffn.hip", "ffn_sk.hip", "ffn_dense.hip", "plan.h", "device.h"):
         with open(os.path.join(ROOT, "routing_grouped_expert_amd", "csrc", name)) as f:
             for line in f:
                 code = re.sub(r"//.*$", "", line).rstrip()
