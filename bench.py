@@ -60,9 +60,11 @@ def parse_args():
                     help="expert weight format: bf16 (the headline), or FP8 E4M3 codes with "
                          "per-row fp32 scales (moe_forward_fp8; x stays bf16)")
     ap.add_argument("--routing-sweep", action="store_true",
-                    help="instead of the layer step: route + permute microseconds over "
-                         "T in {1, 64, 4096} x E in {8 .. 4096}, k = 8 (k = E below 8), warm and "
-                         "with the caches flushed before each call; one JSON line")
+                    help="instead of the layer step: the routing variants' microseconds per "
+                         "call over T in {1, 4, .., 4096} x E in {8 .. 4096}, k = --routing-k "
+                         "(k = E below it), from replayed graphs; one JSON line")
+    ap.add_argument("--routing-k", type=int, default=8,
+                    help="selections per token of the routing sweep (default 8)")
     ap.add_argument("--routing-only", action="store_true",
                     help="only the routing timings at 1024 experts (one JSON line)")
     ap.add_argument("--probe-only", action="store_true",
@@ -470,7 +472,7 @@ def mfma_probe(torch, base, steps):
     return res
 
 
-def routing_sweep():
+def routing_sweep(k_sweep=8):
     """Cost table of the routing variants (selection + permutation through
     moe_route_permute_variant) over token counts and expert counts:
     microseconds per call from a replayed graph of 50 back-to-back calls
@@ -485,7 +487,7 @@ def routing_sweep():
     table = []
     n_it = 50
     for E in (8, 16, 32, 64, 128, 256, 512, 1024, 2048, 4096):
-        k = min(8, E)
+        k = min(k_sweep, E)
         for T in (1, 4, 16, 64, 256, 1024, 4096):
             lg = torch.from_numpy(configs.routing_logits(T, E=E)).to(dev)
             bufs = [torch.empty((T, k), dtype=torch.int32, device=dev),
@@ -543,7 +545,7 @@ def main():
               "expert-parallel path is not built.", file=sys.stderr)
         sys.exit(2)
     if args.routing_sweep:
-        routing_sweep()
+        routing_sweep(args.routing_k)
         return
 
     import torch

@@ -360,12 +360,14 @@ hipError_t launch_permute_block(const int* ids, int T, int k, int E, int first, 
 
 // Measured cost of the routing variants (microseconds per call of
 // selection + permutation, back-to-back calls replayed from a captured
-// graph on MI355X; N(0, 1) logits, k = 8, all experts local), by
-// values-per-lane tier (E = 64, 128, .., 4096), token count (1, 4, 16, .., 4096)
-// and variant (ONE_BLOCK, TWO_KERNELS, TILED); 0 where the variant does not
-// apply to that cell.
+// graph on MI355X; N(0, 1) logits, all experts local), by values-per-lane
+// tier (E = 64, 128, .., 4096), token count (1, 4, 16, .., 4096) and variant
+// (ONE_BLOCK, TWO_KERNELS, TILED); 0 where the variant does not apply to that
+// cell. Two tables: k = 8 and k = 2 selections per token (below 4 values per
+// lane the selection takes k rounds, so the one-block variant, which selects
+// every token on one CU, costs much less at small k).
 constexpr int kCostTiers = 7, kCostPoints = 7;
-constexpr float kCost[kCostTiers][kCostPoints][3] = {
+constexpr float kCost8[kCostTiers][kCostPoints][3] = {
     {{4.30f, 5.53f, 7.75f}, {4.61f, 5.97f, 8.00f}, {5.35f, 6.51f, 8.98f}, {12.56f, 6.70f, 9.52f}, {0.f, 7.95f, 10.47f}, {0.f, 13.21f, 10.80f}, {0.f, 36.02f, 12.31f}},  // VPL 1 (E = 64)
     {{4.51f, 5.89f, 8.59f}, {4.80f, 6.27f, 8.46f}, {5.52f, 6.56f, 9.37f}, {13.22f, 6.99f, 10.02f}, {0.f, 8.36f, 10.89f}, {0.f, 14.29f, 10.97f}, {0.f, 0.f, 12.45f}},  // VPL 2 (E = 128)
     {{4.37f, 5.60f, 8.58f}, {4.47f, 5.64f, 8.41f}, {5.11f, 6.37f, 8.84f}, {10.81f, 6.74f, 9.55f}, {0.f, 8.02f, 9.89f}, {0.f, 14.28f, 10.67f}, {0.f, 0.f, 11.94f}},  // VPL 4 (E = 256)
@@ -374,12 +376,22 @@ constexpr float kCost[kCostTiers][kCostPoints][3] = {
     {{6.51f, 7.01f, 12.95f}, {7.00f, 7.55f, 13.67f}, {10.00f, 8.40f, 14.38f}, {26.33f, 8.46f, 15.17f}, {0.f, 0.f, 15.78f}, {0.f, 0.f, 16.39f}, {0.f, 0.f, 20.31f}},  // VPL 32 (E = 2048)
     {{10.88f, 0.f, 19.01f}, {13.79f, 0.f, 19.00f}, {24.65f, 0.f, 21.67f}, {56.61f, 0.f, 22.04f}, {0.f, 0.f, 22.27f}, {0.f, 0.f, 22.81f}, {0.f, 0.f, 32.93f}},  // VPL 64 (E = 4096)
 };
+constexpr float kCost2[kCostTiers][kCostPoints][3] = {
+    {{3.42f, 4.83f, 6.66f}, {3.52f, 4.79f, 6.61f}, {3.88f, 5.37f, 7.56f}, {6.55f, 5.39f, 7.55f}, {0.f, 5.70f, 8.13f}, {0.f, 7.30f, 8.72f}, {0.f, 13.89f, 9.89f}},  // VPL 1 (E = 64)
+    {{3.59f, 4.91f, 7.34f}, {3.64f, 4.97f, 7.69f}, {4.05f, 5.47f, 7.68f}, {6.97f, 5.52f, 8.12f}, {0.f, 5.86f, 8.32f}, {0.f, 7.56f, 8.92f}, {0.f, 0.f, 10.40f}},  // VPL 2 (E = 128)
+    {{4.18f, 5.42f, 8.35f}, {4.30f, 5.45f, 8.36f}, {4.63f, 5.94f, 8.24f}, {8.91f, 6.13f, 8.63f}, {0.f, 6.49f, 9.04f}, {0.f, 8.13f, 9.66f}, {0.f, 0.f, 11.14f}},  // VPL 4 (E = 256)
+    {{4.26f, 5.58f, 8.82f}, {4.44f, 5.76f, 9.38f}, {5.10f, 6.52f, 9.63f}, {10.20f, 6.50f, 9.73f}, {0.f, 6.91f, 9.87f}, {0.f, 0.f, 10.33f}, {0.f, 0.f, 11.80f}},  // VPL 8 (E = 512)
+    {{5.16f, 6.01f, 9.80f}, {5.56f, 6.55f, 10.24f}, {6.07f, 6.91f, 11.06f}, {12.51f, 6.98f, 10.91f}, {0.f, 7.60f, 11.43f}, {0.f, 0.f, 11.81f}, {0.f, 0.f, 13.27f}},  // VPL 16 (E = 1024)
+    {{6.30f, 6.66f, 12.61f}, {6.45f, 6.93f, 12.45f}, {9.14f, 7.67f, 14.17f}, {22.51f, 8.00f, 14.23f}, {0.f, 0.f, 14.04f}, {0.f, 0.f, 14.48f}, {0.f, 0.f, 18.41f}},  // VPL 32 (E = 2048)
+    {{9.70f, 0.f, 18.29f}, {12.63f, 0.f, 18.53f}, {21.73f, 0.f, 20.22f}, {46.92f, 0.f, 20.10f}, {0.f, 0.f, 20.24f}, {0.f, 0.f, 20.36f}, {0.f, 0.f, 30.88f}},  // VPL 64 (E = 4096)
+};
 
-// Predicted microseconds of a variant for T tokens and E experts: the
-// measured costs of E's tier, linear in log2 T between the measured token
-// counts; past the last measured point of the variant (it stops applying
-// there, or T > 4096) the last segment's slope continues.
-double routing_cost(int variant, int T, int E) {
+// Predicted microseconds of a variant from one table for T tokens and E
+// experts: the measured costs of E's tier, linear in log2 T between the
+// measured token counts; past the last measured point of the variant (it
+// stops applying there, or T > 4096) the last segment's slope continues.
+double routing_cost_table(const float (&cost)[kCostTiers][kCostPoints][3], int variant, int T,
+                          int E) {
   int tier = 0;
   for (int vpl = 1; vpl * 64 < E && tier < kCostTiers - 1; vpl *= 2) ++tier;
   const int v = variant - kRoutingOneBlock;
@@ -388,12 +400,23 @@ double routing_cost(int variant, int T, int E) {
   const double x = lt / 2.0;                 // the measured points are 2 doublings apart
   int last = -1;
   for (int p = 0; p < kCostPoints; ++p)
-    if (kCost[tier][p][v] > 0.f) last = p;
+    if (cost[tier][p][v] > 0.f) last = p;
   if (last < 0) return 1e9;
   int lo = x >= last ? last - 1 : (int)x;
-  if (lo < 0) return kCost[tier][0][v];
-  const double c0 = kCost[tier][lo][v], c1 = kCost[tier][lo + 1][v];
+  if (lo < 0) return cost[tier][0][v];
+  const double c0 = cost[tier][lo][v], c1 = cost[tier][lo + 1][v];
   return c0 + (c1 - c0) * (x - lo);
+}
+
+// Predicted microseconds for k selections per token: the k = 2 and k = 8
+// tables, linear in log2 k between them (clamped outside).
+double routing_cost(int variant, int T, int E, int k) {
+  const double c2 = routing_cost_table(kCost2, variant, T, E);
+  const double c8 = routing_cost_table(kCost8, variant, T, E);
+  double lk = 0.0;
+  for (int j = 1; j < k; j *= 2) lk += 1.0;  // ceil(log2 k)
+  const double w = lk <= 1.0 ? 0.0 : lk >= 3.0 ? 1.0 : (lk - 1.0) / 2.0;
+  return c2 + (c8 - c2) * w;
 }
 
 bool routing_variant_applies(int variant, int T, int E, int L) {
@@ -435,12 +458,11 @@ hipError_t launch_route_permute(int variant, const float* logits, int T, int E, 
 // The variant moe_route_permute runs: the one with the smallest predicted
 // time among those that apply (routing_cost).
 int routing_plan(int T, int E, int k, int L) {
-  (void)k;
   int best = kRoutingTiled;
-  double best_us = routing_cost(kRoutingTiled, T, E);
+  double best_us = routing_cost(kRoutingTiled, T, E, k);
   for (int v : {kRoutingOneBlock, kRoutingTwoKernels}) {
     if (!routing_variant_applies(v, T, E, L)) continue;
-    const double us = routing_cost(v, T, E);
+    const double us = routing_cost(v, T, E, k);
     if (us < best_us) {
       best_us = us;
       best = v;

@@ -229,3 +229,23 @@ def test_routing_plan_picks_an_applicable_variant(E):
     assert moe.routing_plan(4096, E, k, E) == "tiled"
     if E == 1024:
         assert moe.routing_plan(64, E, k, E) == "two_kernels"
+
+
+def test_routing_plan_follows_k():
+    """The cost model holds a table for k = 8 and one for k = 2 (below 4
+    values per lane the selection takes k rounds): at the decode shape (E = 8,
+    k = 2, 32 tokens) the one-block variant is the measured fastest (4.8 us
+    against 5.3 us for the two kernels), at k = 8 it is not (12.5 us at 64
+    tokens); at 1024 tokens and E <= 256 two kernels beat the tiled split at
+    k = 2 (6.9 against 8.6 us at E = 8) but not at k = 8."""
+    assert moe.routing_plan(32, 8, 2, 8) == "one_block"
+    assert moe.routing_plan(32, 8, 8, 8) == "two_kernels"
+    assert moe.routing_plan(1024, 8, 2, 8) == "two_kernels"
+    assert moe.routing_plan(1024, 64, 8, 64) == "tiled"
+    for E in (8, 64, 256, 1024, 4096):
+        for k in (1, 2, 3, 4, 6, 8):
+            k = min(k, E)
+            for T in (1, 32, 64, 1024, 4096):
+                v = moe.routing_plan(T, E, k, E)
+                assert v != "one_block" or T <= 64
+                assert v != "two_kernels" or _block_permute_fits(T, E, E)
