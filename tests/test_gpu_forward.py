@@ -54,6 +54,15 @@ def test_forward_reduced(name, T, H, I):
     check_forward(configs.layer_inputs(configs.WORKLOADS[name], T=T, H=H, I=I), what=name)
 
 
+# The dense grouped-FFN kernels through the whole layer, every output
+# compared: the decode shape with 2048 tokens (512 entries per expert: two
+# passes of 256 each), and share 0 of the share-0 workload with 8192 tokens
+# (~170 local entries per local expert, chosen on the device from the counts).
+@pytest.mark.parametrize("name,T,H,I", [("decode", 2048, 512, 256), ("share0", 8192, 256, 128)])
+def test_forward_dense_complete(name, T, H, I):
+    check_forward(configs.layer_inputs(configs.WORKLOADS[name], T=T, H=H, I=I), what=f"{name} dense")
+
+
 def test_forward_odd_shapes():
     cfg = dict(configs.WORKLOADS["fine"], E=13, k=3, first=2, L=7)
     check_forward(configs.layer_inputs(cfg, T=45, H=200, I=72), what="odd shapes")
