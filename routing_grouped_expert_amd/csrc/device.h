@@ -124,33 +124,39 @@ __device__ __forceinline__ float wave_sum_f32(float v) {
   return v;
 }
 
-// Exclusive prefix sum over data[0, n) in shared memory by one block of
-// blockDim.x threads (a multiple of 64, at most 1024); data[n] receives the
-// total. `tmp` is shared scratch of at least blockDim.x / 64 ints. Must be
-// called by every thread of the block.
-__device__ inline void block_exclusive_scan(int* data, int n, int* tmp) {
-  const int nt = blockDim.x, tid = threadIdx.x;
+// Inclusive prefix sum over the 64 lanes (lane i ends with the sum of lanes
+// 0..i) by DPP: inside each row of 16 lanes, shifts by 1, 2, 4 and 8 (a lane
+// with no source lane adds 0); then the last lane of row 0 is added to row 1
+// and that of row 2 to row 3 (row broadcast of lane 15), and the last lane of
+// row 1 (rows 0-1 in all) to rows 2 and 3 (row broadcast of lane 31).
+__device__ __forceinline__ int wave_inclusive_sum(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);  // row_bcast:15, rows 1, 3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);  // row_bcast:31, rows 2, 3
+  return v;
+}
+
+// Exclusive prefix sum over data[0, n) in shared memory by one block of nt
+// threads (nt = blockDim.x, a multiple of 64, at most 1024; callers that know
+// it at compile time pass it, which spares a load of the launch's block size);
+// data[n] receives the total. `tmp` is shared scratch of at least nt / 64
+// ints. Must be called by every thread of the block.
+__device__ inline void block_exclusive_scan(int* data, int n, int* tmp, int nt) {
+  const int tid = threadIdx.x;
   const int per = (n + nt - 1) / nt;
   const int b = tid * per, e = min(b + per, n);
   int local = 0;
   for (int i = b; i < e; ++i) local += data[i];
   // inclusive scan of `local` across the block
   const int lane = tid % kWave, wave = tid / kWave;
-  int v = local;
-#pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) {
-    int o = __shfl_up(v, d, kWave);
-    if (lane >= d) v += o;
-  }
+  const int v = wave_inclusive_sum(local);
   if (lane == kWave - 1) tmp[wave] = v;
   __syncthreads();
   if (wave == 0) {
-    int w = lane < nt / kWave ? tmp[lane] : 0;
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {
-      int o = __shfl_up(w, d, kWave);
-      if (lane >= d) w += o;
-    }
+    const int w = wave_inclusive_sum(lane < nt / kWave ? tmp[lane] : 0);
     if (lane < nt / kWave) tmp[lane] = w;
   }
   __syncthreads();

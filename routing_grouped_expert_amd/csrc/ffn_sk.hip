@@ -124,12 +124,13 @@ __device__ __forceinline__ PlanRO plan_ro(const int* __restrict__ plan, int pmax
 // of every local expert with entries, and zero the fixup counters.
 __global__ __launch_bounds__(1024) void ffn_plan_kernel(const int* __restrict__ offsets, int L,
                                                         PlanOut po) {
+  constexpr int nt = 1024;
   extern __shared__ __attribute__((aligned(16))) int s_lds[];  // 2 (L + 1) + 16
   int* off = s_lds;
-  for (int i = threadIdx.x; i < po.ncounters; i += blockDim.x) po.counters[i] = 0;
-  for (int i = threadIdx.x; i <= L; i += blockDim.x) off[i] = offsets[i];
+  for (int i = threadIdx.x; i < po.ncounters; i += nt) po.counters[i] = 0;
+  for (int i = threadIdx.x; i <= L; i += nt) off[i] = offsets[i];
   __syncthreads();
-  write_ffn_plan(off, L, po, off + L + 1);
+  write_ffn_plan(off, L, po, off + L + 1, nt);
 }
 
 __device__ __forceinline__ bf16x8 ld8(const uint16_t* p) {

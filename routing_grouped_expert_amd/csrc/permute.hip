@@ -48,22 +48,32 @@ bool block_permute_fits(int T, int E, int L) {
   return nb * E * 12 + 2 * (size_t)(L + 1 + 16) * 4 <= kBlockLds;
 }
 
-// After the block's offsets scan: zero this block's share of the FFN fixup
-// counters and (block 0) write the FFN pass plan. s_pass: L + 1 + 16 ints.
-__device__ inline void maybe_write_plan(const int* off, int L, const PlanOut& po, int* s_pass) {
+// Share `part` of `parts` of zeroing the FFN fixup counters (given a plan),
+// by a block of nt threads.
+__device__ inline void zero_plan_counters(const PlanOut& po, int part, int parts, int nt) {
   if (!po.plan) return;
-  const int nt = blockDim.x;
-  for (int i = blockIdx.x * nt + threadIdx.x; i < po.ncounters; i += gridDim.x * nt)
-    po.counters[i] = 0;
-  if (blockIdx.x == 0) write_ffn_plan(off, L, po, s_pass);
+  for (int i = part * nt + threadIdx.x; i < po.ncounters; i += parts * nt) po.counters[i] = 0;
 }
 
+// After the block's offsets scan: zero this block's share of the FFN fixup
+// counters and (block 0) write the FFN pass plan. s_pass: L + 1 + 16 ints.
+__device__ inline void maybe_write_plan(const int* off, int L, const PlanOut& po, int* s_pass,
+                                        int nt) {
+  zero_plan_counters(po, blockIdx.x, gridDim.x, nt);
+  if (po.plan && blockIdx.x == 0) write_ffn_plan(off, L, po, s_pass, nt);
+}
+
+// The first kPermRegs entries of each thread are loaded into registers before
+// the masks are cleared (their latency overlaps the clearing) and kept for the
+// placement; entries beyond that (more than 1024 kPermRegs) are read again.
+constexpr int kPermRegs = 4;
 __global__ __launch_bounds__(1024) void permute_block_kernel(const int* __restrict__ ids, int T,
                                                              int k, int E, int first, int L,
                                                              int* __restrict__ counts,
                                                              int* __restrict__ offsets,
                                                              int* __restrict__ perm,
                                                              int* __restrict__ e2p, PlanOut po) {
+  constexpr int nt = 1024;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int nb = (T + TILE - 1) / TILE;
   unsigned long long* mask = reinterpret_cast<unsigned long long*>(smem);  // [nb][E]
@@ -71,14 +81,23 @@ __global__ __launch_bounds__(1024) void permute_block_kernel(const int* __restri
   int* off = base + (size_t)nb * E;
   int* tmp = off + (L + 1);
   int* s_pass = tmp + 16;
-  const int tid = threadIdx.x, nt = blockDim.x;
+  const int tid = threadIdx.x;
   const int n = T * k;
+  int ex[kPermRegs];
+#pragma unroll
+  for (int j = 0; j < kPermRegs; ++j) {
+    const int r = tid + j * nt;
+    ex[j] = r < n ? ids[r] : -1;
+  }
   for (int i = tid; i < nb * E; i += nt) mask[i] = 0ull;
   __syncthreads();
-  for (int r = tid; r < n; r += nt) {
-    const int e = ids[r], t = r / k;
+  auto mark = [&](int r, int e) {
+    const int t = r / k;
     if (e >= 0 && e < E) atomicOr(&mask[(t / TILE) * E + e], 1ull << (t % TILE));
-  }
+  };
+#pragma unroll
+  for (int j = 0; j < kPermRegs; ++j) mark(tid + j * nt, ex[j]);
+  for (int r = tid + kPermRegs * nt; r < n; r += nt) mark(r, ids[r]);
   __syncthreads();
   for (int e = tid; e < E; e += nt) {
     int run = 0;
@@ -90,11 +109,10 @@ __global__ __launch_bounds__(1024) void permute_block_kernel(const int* __restri
     if (e >= first && e < first + L) off[e - first] = run;
   }
   __syncthreads();
-  block_exclusive_scan(off, L, tmp);
+  block_exclusive_scan(off, L, tmp, nt);
   for (int i = tid; i <= L; i += nt) offsets[i] = off[i];
-  maybe_write_plan(off, L, po, s_pass);
-  for (int r = tid; r < n; r += nt) {
-    const int e = ids[r];
+  maybe_write_plan(off, L, po, s_pass, nt);
+  auto place = [&](int r, int e) {
     int p = -1;
     if (e >= first && e < first + L) {
       const int t = r / k, b = t / TILE, tl = t % TILE;
@@ -102,7 +120,11 @@ __global__ __launch_bounds__(1024) void permute_block_kernel(const int* __restri
       perm[p] = r;
     }
     e2p[r] = p;
-  }
+  };
+#pragma unroll
+  for (int j = 0; j < kPermRegs; ++j)
+    if (tid + j * nt < n) place(tid + j * nt, ex[j]);
+  for (int r = tid + kPermRegs * nt; r < n; r += nt) place(r, ids[r]);
 }
 
 // Grid: one block per 64-token tile. masks[tile * E + e].
@@ -112,17 +134,17 @@ __global__ __launch_bounds__(256) void tile_masks_kernel(const int* __restrict__
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   unsigned long long* mask = reinterpret_cast<unsigned long long*>(smem);
   const int b = blockIdx.x, tid = threadIdx.x;
-  for (int e = tid; e < E; e += blockDim.x) mask[e] = 0ull;
+  for (int e = tid; e < E; e += 256) mask[e] = 0ull;
   __syncthreads();
   const int t0 = b * TILE;
   const int n = min(TILE, T - t0) * k;
   const int* tid_ids = ids + (size_t)t0 * k;
-  for (int q = tid; q < n; q += blockDim.x) {
+  for (int q = tid; q < n; q += 256) {
     const int e = tid_ids[q];
     if (e >= 0 && e < E) atomicOr(&mask[e], 1ull << (q / k));
   }
   __syncthreads();
-  for (int e = tid; e < E; e += blockDim.x) masks[(size_t)b * E + e] = mask[e];
+  for (int e = tid; e < E; e += 256) masks[(size_t)b * E + e] = mask[e];
 }
 
 // Grid: ceil(E / 64) blocks of SW waves; lane j of every wave owns expert
@@ -158,8 +180,12 @@ __global__ __launch_bounds__(SW * 64) void expert_scan_kernel(const unsigned lon
   }
   part[wave][lane] = c;
   __syncthreads();
-  int run = 0;  // entries of expert e in tiles before b0
-  for (int w = 0; w < wave; ++w) run += part[w][lane];
+  int run = 0;  // entries of expert e in tiles before b0 (independent reads)
+#pragma unroll
+  for (int w = 0; w < SW; ++w) {
+    const int x = part[w][lane];
+    run += w < wave ? x : 0;
+  }
   const int i = e - first;
   if (e < E && i >= 0 && i < L) {
     if (inreg) {
@@ -183,41 +209,67 @@ __global__ __launch_bounds__(SW * 64) void expert_scan_kernel(const unsigned lon
   }
 }
 
-// Grid: one block per 64-token tile. Every block scans the local experts'
-// counts into offsets in LDS (block 0 also writes them out, and the FFN pass
-// plan given a PlanOut), then places its tile's entries. Dynamic LDS:
+// Grid: one block per 64-token tile, kScatterThreads threads. Every block
+// scans the local experts' counts into offsets in LDS (block 0 also writes
+// them out, and the FFN pass plan given a PlanOut), then places its tile's
+// entries. The entries, their masks and their bases do not depend on the
+// offsets, so they are loaded first and arrive while the block scans (the
+// counts, which the scan needs first, are loaded before them). Dynamic LDS:
 // 2 ((L + 1) + 16) ints.
-__global__ __launch_bounds__(256) void scatter_kernel(const int* __restrict__ ids, int T, int k,
-                                                      int E, int first, int L,
-                                                      const unsigned long long* __restrict__ masks,
-                                                      const int* __restrict__ counts,
-                                                      int* __restrict__ offsets,
-                                                      const int* __restrict__ base,
-                                                      int* __restrict__ perm,
-                                                      int* __restrict__ e2p, PlanOut po) {
+constexpr int kScatterThreads = 256;
+constexpr int kScatterRegs = TILE * 32 / kScatterThreads;      // entries per thread at k = 32
+constexpr int kScatterCounts = 4096 / kScatterThreads;         // counts per thread at L = 4096
+__global__ __launch_bounds__(kScatterThreads) void scatter_kernel(
+    const int* __restrict__ ids, int T, int k, int E, int first, int L,
+    const unsigned long long* __restrict__ masks, const int* __restrict__ counts,
+    int* __restrict__ offsets, const int* __restrict__ base, int* __restrict__ perm,
+    int* __restrict__ e2p, PlanOut po) {
   extern __shared__ int off[];
-  for (int j = threadIdx.x; j < L; j += blockDim.x) off[j] = counts[first + j];
-  __syncthreads();
-  block_exclusive_scan(off, L, off + L + 1);
-  if (blockIdx.x == 0)
-    for (int j = threadIdx.x; j <= L; j += blockDim.x) offsets[j] = off[j];
-  maybe_write_plan(off, L, po, off + L + 1 + 16);
   const int b = blockIdx.x;
   const int t0 = b * TILE;
   const int n = min(TILE, T - t0) * k;
   const int r0 = t0 * k;
-  for (int q = threadIdx.x; q < n; q += blockDim.x) {
-    const int r = r0 + q;
-    const int e = ids[r];
-    int p = -1;
-    if (e >= first && e < first + L) {
-      const int tl = q / k;
-      const unsigned long long m = masks[(size_t)b * E + e];
-      p = off[e - first] + base[(size_t)b * L + (e - first)] +
-          __popcll(m & ((1ull << tl) - 1ull));
-      perm[p] = r;
+  int cnt[kScatterCounts], ex[kScatterRegs], bs[kScatterRegs];
+  unsigned long long m[kScatterRegs];
+#pragma unroll
+  for (int j = 0; j < kScatterCounts; ++j) {
+    const int i = threadIdx.x + j * kScatterThreads;
+    cnt[j] = i < L ? counts[first + i] : 0;
+  }
+#pragma unroll
+  for (int j = 0; j < kScatterRegs; ++j) {
+    const int q = threadIdx.x + j * kScatterThreads;
+    ex[j] = q < n ? ids[r0 + q] : -1;
+  }
+#pragma unroll
+  for (int j = 0; j < kScatterRegs; ++j) {
+    const bool local = ex[j] >= first && ex[j] < first + L;
+    m[j] = local ? masks[(size_t)b * E + ex[j]] : 0ull;
+    bs[j] = local ? base[(size_t)b * L + (ex[j] - first)] : 0;
+  }
+#pragma unroll
+  for (int j = 0; j < kScatterCounts; ++j) {
+    const int i = threadIdx.x + j * kScatterThreads;
+    if (i < L) off[i] = cnt[j];
+  }
+  __syncthreads();
+  block_exclusive_scan(off, L, off + L + 1, kScatterThreads);
+  if (blockIdx.x == 0)
+    for (int j = threadIdx.x; j <= L; j += kScatterThreads) offsets[j] = off[j];
+  maybe_write_plan(off, L, po, off + L + 1 + 16, kScatterThreads);
+#pragma unroll
+  for (int j = 0; j < kScatterRegs; ++j) {
+    const int q = threadIdx.x + j * kScatterThreads;
+    if (q < n) {
+      const int r = r0 + q, e = ex[j];
+      int p = -1;
+      if (e >= first && e < first + L) {
+        const int tl = q / k;
+        p = off[e - first] + bs[j] + __popcll(m[j] & ((1ull << tl) - 1ull));
+        perm[p] = r;
+      }
+      e2p[r] = p;
     }
-    e2p[r] = p;
   }
 }
 }  // namespace
@@ -242,7 +294,8 @@ __global__ __launch_bounds__(NW * kWave) void route_permute_small_kernel(
   int* tmp = off + (L + 1);
   int* ids_s = tmp + 16;
   int* s_pass = ids_s + T * k;
-  const int tid = threadIdx.x, nt = blockDim.x, lane = tid % kWave, wave = tid / kWave;
+  constexpr int nt = NW * kWave;
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   const int n = T * k;
   for (int e = tid; e < E; e += nt) mask[e] = 0ull;
   __syncthreads();
@@ -269,9 +322,9 @@ __global__ __launch_bounds__(NW * kWave) void route_permute_small_kernel(
   for (int e = tid; e < E; e += nt) counts[e] = __popcll(mask[e]);
   for (int i = tid; i < L; i += nt) off[i] = __popcll(mask[first + i]);
   __syncthreads();
-  block_exclusive_scan(off, L, tmp);
+  block_exclusive_scan(off, L, tmp, nt);
   for (int i = tid; i <= L; i += nt) offsets[i] = off[i];
-  maybe_write_plan(off, L, po, s_pass);
+  maybe_write_plan(off, L, po, s_pass, nt);
   for (int r = tid; r < n; r += nt) {
     const int e = ids_s[r];
     int p = -1;
@@ -311,11 +364,12 @@ hipError_t launch_scan_scatter(const int* ids, int T, int k, int E, int first, i
                                int* offsets, int* perm, int* e2p, const PermWs& w,
                                const PlanOut& po, hipStream_t stream) {
   const int nb = (T + TILE - 1) / TILE;
+  if (L > kScatterThreads * kScatterCounts) return hipErrorInvalidValue;  // (E <= 4096)
   hipLaunchKernelGGL(expert_scan_kernel, dim3((E + kWave - 1) / kWave), dim3(SW * kWave), 0,
                      stream, w.masks, nb, E, first, L, counts, w.base);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(scatter_kernel, dim3(nb), dim3(256), 2 * (size_t)(L + 1 + 16) * 4, stream,
+  hipLaunchKernelGGL(scatter_kernel, dim3(nb), dim3(kScatterThreads), 2 * (size_t)(L + 1 + 16) * 4, stream,
                      ids, T, k, E, first, L, w.masks, counts, offsets, w.base, perm, e2p, po);
   return hipGetLastError();
 }
@@ -368,22 +422,22 @@ hipError_t launch_permute_block(const int* ids, int T, int k, int E, int first, 
 // every token on one CU, costs much less at small k).
 constexpr int kCostTiers = 7, kCostPoints = 7;
 constexpr float kCost8[kCostTiers][kCostPoints][3] = {
-    {{4.30f, 5.53f, 7.75f}, {4.61f, 5.97f, 8.00f}, {5.35f, 6.51f, 8.98f}, {12.56f, 6.70f, 9.52f}, {0.f, 7.95f, 10.47f}, {0.f, 13.21f, 10.80f}, {0.f, 36.02f, 12.31f}},  // VPL 1 (E = 64)
-    {{4.51f, 5.89f, 8.59f}, {4.80f, 6.27f, 8.46f}, {5.52f, 6.56f, 9.37f}, {13.22f, 6.99f, 10.02f}, {0.f, 8.36f, 10.89f}, {0.f, 14.29f, 10.97f}, {0.f, 0.f, 12.45f}},  // VPL 2 (E = 128)
-    {{4.37f, 5.60f, 8.58f}, {4.47f, 5.64f, 8.41f}, {5.11f, 6.37f, 8.84f}, {10.81f, 6.74f, 9.55f}, {0.f, 8.02f, 9.89f}, {0.f, 14.28f, 10.67f}, {0.f, 0.f, 11.94f}},  // VPL 4 (E = 256)
-    {{4.39f, 5.75f, 8.82f}, {4.77f, 6.06f, 9.49f}, {5.70f, 6.80f, 10.01f}, {12.15f, 6.98f, 10.67f}, {0.f, 8.46f, 11.11f}, {0.f, 0.f, 11.46f}, {0.f, 0.f, 12.85f}},  // VPL 8 (E = 512)
-    {{5.13f, 6.24f, 10.22f}, {5.78f, 6.98f, 10.50f}, {6.64f, 7.44f, 12.15f}, {14.61f, 7.50f, 12.47f}, {0.f, 9.48f, 12.88f}, {0.f, 0.f, 13.39f}, {0.f, 0.f, 15.50f}},  // VPL 16 (E = 1024)
-    {{6.51f, 7.01f, 12.95f}, {7.00f, 7.55f, 13.67f}, {10.00f, 8.40f, 14.38f}, {26.33f, 8.46f, 15.17f}, {0.f, 0.f, 15.78f}, {0.f, 0.f, 16.39f}, {0.f, 0.f, 20.31f}},  // VPL 32 (E = 2048)
-    {{10.88f, 0.f, 19.01f}, {13.79f, 0.f, 19.00f}, {24.65f, 0.f, 21.67f}, {56.61f, 0.f, 22.04f}, {0.f, 0.f, 22.27f}, {0.f, 0.f, 22.81f}, {0.f, 0.f, 32.93f}},  // VPL 64 (E = 4096)
+    {{3.83f, 5.28f, 8.08f}, {3.95f, 5.35f, 8.13f}, {4.69f, 5.76f, 8.96f}, {11.89f, 5.96f, 9.75f}, {0.f, 7.15f, 10.17f}, {0.f, 12.61f, 10.68f}, {0.f, 35.09f, 12.04f}},  // VPL 1 (E = 64)
+    {{3.95f, 5.36f, 8.55f}, {4.21f, 5.70f, 9.36f}, {5.20f, 6.10f, 10.16f}, {12.59f, 6.30f, 10.20f}, {0.f, 7.44f, 10.24f}, {0.f, 13.59f, 11.36f}, {0.f, 0.f, 12.49f}},  // VPL 2 (E = 128)
+    {{3.90f, 5.13f, 8.23f}, {3.92f, 5.11f, 8.38f}, {4.51f, 5.77f, 9.08f}, {10.15f, 5.91f, 9.30f}, {0.f, 7.11f, 9.88f}, {0.f, 13.43f, 10.36f}, {0.f, 0.f, 11.82f}},  // VPL 4 (E = 256)
+    {{3.92f, 5.27f, 8.65f}, {4.24f, 5.60f, 8.94f}, {5.23f, 6.08f, 10.23f}, {11.75f, 6.24f, 9.93f}, {0.f, 7.46f, 10.44f}, {0.f, 0.f, 11.45f}, {0.f, 0.f, 12.39f}},  // VPL 8 (E = 512)
+    {{4.61f, 5.62f, 9.38f}, {5.29f, 6.25f, 10.12f}, {6.12f, 6.55f, 11.17f}, {14.30f, 7.00f, 11.11f}, {0.f, 8.39f, 11.89f}, {0.f, 0.f, 12.10f}, {0.f, 0.f, 13.58f}},  // VPL 16 (E = 1024)
+    {{6.13f, 6.45f, 11.14f}, {6.57f, 6.88f, 11.95f}, {9.75f, 7.72f, 13.29f}, {26.32f, 7.96f, 13.13f}, {0.f, 0.f, 13.54f}, {0.f, 0.f, 13.83f}, {0.f, 0.f, 18.07f}},  // VPL 32 (E = 2048)
+    {{10.54f, 0.f, 15.60f}, {13.48f, 0.f, 15.80f}, {24.27f, 0.f, 18.26f}, {56.28f, 0.f, 18.14f}, {0.f, 0.f, 17.97f}, {0.f, 0.f, 18.39f}, {0.f, 0.f, 28.93f}},  // VPL 64 (E = 4096)
 };
 constexpr float kCost2[kCostTiers][kCostPoints][3] = {
-    {{3.42f, 4.83f, 6.66f}, {3.52f, 4.79f, 6.61f}, {3.88f, 5.37f, 7.56f}, {6.55f, 5.39f, 7.55f}, {0.f, 5.70f, 8.13f}, {0.f, 7.30f, 8.72f}, {0.f, 13.89f, 9.89f}},  // VPL 1 (E = 64)
-    {{3.59f, 4.91f, 7.34f}, {3.64f, 4.97f, 7.69f}, {4.05f, 5.47f, 7.68f}, {6.97f, 5.52f, 8.12f}, {0.f, 5.86f, 8.32f}, {0.f, 7.56f, 8.92f}, {0.f, 0.f, 10.40f}},  // VPL 2 (E = 128)
-    {{4.18f, 5.42f, 8.35f}, {4.30f, 5.45f, 8.36f}, {4.63f, 5.94f, 8.24f}, {8.91f, 6.13f, 8.63f}, {0.f, 6.49f, 9.04f}, {0.f, 8.13f, 9.66f}, {0.f, 0.f, 11.14f}},  // VPL 4 (E = 256)
-    {{4.26f, 5.58f, 8.82f}, {4.44f, 5.76f, 9.38f}, {5.10f, 6.52f, 9.63f}, {10.20f, 6.50f, 9.73f}, {0.f, 6.91f, 9.87f}, {0.f, 0.f, 10.33f}, {0.f, 0.f, 11.80f}},  // VPL 8 (E = 512)
-    {{5.16f, 6.01f, 9.80f}, {5.56f, 6.55f, 10.24f}, {6.07f, 6.91f, 11.06f}, {12.51f, 6.98f, 10.91f}, {0.f, 7.60f, 11.43f}, {0.f, 0.f, 11.81f}, {0.f, 0.f, 13.27f}},  // VPL 16 (E = 1024)
-    {{6.30f, 6.66f, 12.61f}, {6.45f, 6.93f, 12.45f}, {9.14f, 7.67f, 14.17f}, {22.51f, 8.00f, 14.23f}, {0.f, 0.f, 14.04f}, {0.f, 0.f, 14.48f}, {0.f, 0.f, 18.41f}},  // VPL 32 (E = 2048)
-    {{9.70f, 0.f, 18.29f}, {12.63f, 0.f, 18.53f}, {21.73f, 0.f, 20.22f}, {46.92f, 0.f, 20.10f}, {0.f, 0.f, 20.24f}, {0.f, 0.f, 20.36f}, {0.f, 0.f, 30.88f}},  // VPL 64 (E = 4096)
+    {{2.76f, 4.12f, 6.66f}, {2.98f, 4.30f, 7.51f}, {3.18f, 4.60f, 7.48f}, {5.96f, 4.75f, 8.00f}, {0.f, 5.04f, 8.35f}, {0.f, 6.21f, 8.47f}, {0.f, 12.85f, 9.92f}},  // VPL 1 (E = 64)
+    {{2.89f, 4.28f, 7.63f}, {3.11f, 4.47f, 7.41f}, {3.42f, 4.78f, 7.87f}, {6.35f, 4.74f, 7.88f}, {0.f, 5.16f, 8.29f}, {0.f, 6.48f, 8.64f}, {0.f, 0.f, 10.08f}},  // VPL 2 (E = 128)
+    {{3.45f, 4.61f, 7.98f}, {3.66f, 4.79f, 8.01f}, {3.97f, 5.34f, 8.72f}, {8.32f, 5.23f, 9.01f}, {0.f, 5.67f, 9.39f}, {0.f, 7.12f, 9.58f}, {0.f, 0.f, 11.15f}},  // VPL 4 (E = 256)
+    {{3.71f, 4.92f, 8.41f}, {3.90f, 5.05f, 8.66f}, {4.68f, 5.68f, 9.19f}, {9.65f, 5.91f, 9.03f}, {0.f, 6.11f, 9.85f}, {0.f, 0.f, 10.31f}, {0.f, 0.f, 11.60f}},  // VPL 8 (E = 512)
+    {{4.51f, 5.41f, 9.15f}, {4.89f, 6.02f, 9.65f}, {5.36f, 6.18f, 10.33f}, {11.80f, 6.45f, 10.10f}, {0.f, 6.79f, 10.27f}, {0.f, 0.f, 10.84f}, {0.f, 0.f, 13.15f}},  // VPL 16 (E = 1024)
+    {{5.92f, 6.18f, 10.77f}, {5.95f, 6.21f, 11.35f}, {8.63f, 7.01f, 12.51f}, {22.13f, 6.95f, 12.23f}, {0.f, 0.f, 12.16f}, {0.f, 0.f, 12.62f}, {0.f, 0.f, 16.45f}},  // VPL 32 (E = 2048)
+    {{9.29f, 0.f, 14.85f}, {12.19f, 0.f, 15.18f}, {21.33f, 0.f, 17.11f}, {46.86f, 0.f, 16.75f}, {0.f, 0.f, 16.40f}, {0.f, 0.f, 17.09f}, {0.f, 0.f, 27.36f}},  // VPL 64 (E = 4096)
 };
 
 // Predicted microseconds of a variant from one table for T tokens and E

@@ -43,11 +43,12 @@ struct PlanOut {
 };
 
 // The plan from the exclusive scan `off` of the local experts' entry counts
-// (LDS, off[L] = entries in all). One block, every thread calls it; `s_pass`
-// is LDS scratch of L + 1 + 16 ints. The counters are zeroed by this block
-// (counter_stride = 1) or shared out over many (see callers).
-__device__ inline void write_ffn_plan(const int* off, int L, const PlanOut& po, int* s_pass) {
-  const int tid = threadIdx.x, nt = blockDim.x;
+// (LDS, off[L] = entries in all). One block of nt threads (blockDim.x), every
+// thread calls it; `s_pass` is LDS scratch of L + 1 + 16 ints. The callers
+// zero the counters.
+__device__ inline void write_ffn_plan(const int* off, int L, const PlanOut& po, int* s_pass,
+                                      int nt) {
+  const int tid = threadIdx.x;
   const int n_local = max(0, min(off[L], po.nmax)) - max(0, min(off[0], po.nmax));
   const bool dense = po.nr_dense > 0 && (long)n_local >= (long)po.dense_min * L;
   const int nr = dense ? po.nr_dense : po.nr;
@@ -57,7 +58,7 @@ __device__ inline void write_ffn_plan(const int* off, int L, const PlanOut& po, 
     s_pass[i] = (e - b + nr - 1) / nr;
   }
   __syncthreads();
-  block_exclusive_scan(s_pass, L, s_pass + L + 1);
+  block_exclusive_scan(s_pass, L, s_pass + L + 1, nt);
   const PlanView pv = plan_view(po.plan, po.pmax);
   for (int i = tid; i < L; i += nt) {
     const int b = max(0, min(off[i], po.nmax));

@@ -38,7 +38,7 @@ __global__ __launch_bounds__(MASKS ? kMaskWaves * kWave : 4 * kWave) void route_
   float v[VPL];
   if (t < T) sel::load_logits<VPL, VEC>(logits + (size_t)t * E, lane, E, v);
   if constexpr (MASKS) {  // (the logits are in flight meanwhile)
-    for (int e = threadIdx.x; e < E; e += blockDim.x) msk[e] = 0u;
+    for (int e = threadIdx.x; e < E; e += NW * kWave) msk[e] = 0u;
     __syncthreads();
   }
   if (t < T) {
@@ -55,7 +55,7 @@ __global__ __launch_bounds__(MASKS ? kMaskWaves * kWave : 4 * kWave) void route_
     // each 64-bit mask (little-endian: the s-th 16-bit half-word)
     const int tile = blockIdx.x / 4, s = blockIdx.x % 4;
     const bool last = blockIdx.x == (int)gridDim.x - 1;
-    for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    for (int e = threadIdx.x; e < E; e += NW * kWave) {
       uint16_t* w = masks16 + ((size_t)tile * E + e) * 4;
       w[s] = static_cast<uint16_t>(msk[e]);
       if (last)  // slices of the last tile past T: no tokens

@@ -234,10 +234,11 @@ def test_routing_plan_picks_an_applicable_variant(E):
 def test_routing_plan_follows_k():
     """The cost model holds a table for k = 8 and one for k = 2 (below 4
     values per lane the selection takes k rounds): at the decode shape (E = 8,
-    k = 2, 32 tokens) the one-block variant is the measured fastest (4.8 us
-    against 5.3 us for the two kernels), at k = 8 it is not (12.5 us at 64
-    tokens); at 1024 tokens and E <= 256 two kernels beat the tiled split at
-    k = 2 (6.9 against 8.6 us at E = 8) but not at k = 8."""
+    k = 2, 32 tokens) the one-block variant is the predicted fastest (3.2 us at
+    16 and 6.0 us at 64 tokens, against 4.6 and 4.8 us for the two kernels),
+    at k = 8 it is not (12.0 us at 64 tokens); at 1024 tokens and E <= 256
+    two kernels beat the tiled split at k = 2 (6.1 against 8.8 us at E = 8)
+    but not at k = 8 (13.3 against 10.6 us)."""
     assert moe.routing_plan(32, 8, 2, 8) == "one_block"
     assert moe.routing_plan(32, 8, 8, 8) == "two_kernels"
     assert moe.routing_plan(1024, 8, 2, 8) == "two_kernels"
