@@ -223,7 +223,10 @@ struct Sched {
   int C, NB, TD, nb;
   long US;        // units of the stream-K part
   Pos ps, pe, p0; // the block's first and last stream-K unit, its first unit
-  __device__ Sched(int b, int TT, int C_, int NB_) : C(C_), NB(NB_) {
+  // A = 2: the stream-K cuts fall on even units only (C even), so a block's
+  // units come in aligned pairs (the FP8 staged kernels load a pair's weight
+  // codes as full lines); the fixup then counts in pairs (C / A, US / A).
+  __device__ Sched(int b, int TT, int C_, int NB_, int A = 1) : C(C_), NB(NB_) {
     const int rounds = (TT + NB - 1) / NB;
     if ((long)TT * 100 >= (long)rounds * NB * 85) {
       TD = TT;
@@ -237,8 +240,8 @@ struct Sched {
     const int R = TT >= 2 * NB ? TT / NB - 1 : 0;
     TD = R * NB;
     US = (long)(TT - TD) * C;
-    nb = (int)min((long)NB, US);
-    const long s = first_unit(b, US, nb), e = first_unit(b + 1, US, nb) - 1;
+    nb = (int)min((long)NB, US / A);
+    const long s = A * first_unit(b, US / A, nb), e = A * first_unit(b + 1, US / A, nb) - 1;
     ps = Pos{TD + (int)(s / C), (int)(s % C)};
     pe = Pos{TD + (int)(e / C), (int)(e % C)};
     p0 = R > 0 ? Pos{b, 0} : ps;
@@ -966,18 +969,20 @@ __device__ __forceinline__ void pf_stage_store(const PfStage<NR>& st, pf_row_t* 
   }
 }
 
-// A lane's weight operands of one chunk: bf16, a full-line slab per group
-// (two MFMA fragments once through the LDS tile); FP8, 16 codes per group in
-// fragment layout (lane l: row l % 16, codes 16 (l / 16) .. + 15 of the
-// 64-wide chunk; codes + 0..7 feed the first MFMA step, + 8..15 the second,
-// and the token fragments are read in that K order).
+// A lane's weight operands: bf16, one chunk, a full-line slab per group (two
+// MFMA fragments once through the LDS tile); FP8, the aligned pair of chunks
+// that one 128-code line per row spans, loaded as a full-line slab per group
+// and put through the LDS tile into fragment layout: v[q][h] holds chunk h of
+// the pair, lane l row l % 16, codes 16 (l / 16) .. + 15 of the 64-wide chunk
+// (codes + 0..7 feed the first MFMA step, + 8..15 the second, and the token
+// fragments are read in that K order).
 template <bool F8>
 struct PfA {
   bf16x8 v[PF_GROUPS][PF_STEPS];
 };
 template <>
 struct PfA<true> {
-  u32x4 v[PF_GROUPS];
+  u32x4 v[PF_GROUPS][2];
 };
 
 // acc[q * NT + nt] += A(group q) * B(token tile nt) over one chunk for the
@@ -986,13 +991,16 @@ struct PfA<true> {
 // intermediate.
 template <int NT, int NV, bool UP, bool F8>
 __device__ __forceinline__ void pf_mma(const PfA<F8>& a, const pf_row_t* b0, const pf_row_t* b1,
-                                       int lane, f32x4* acc, int nv) {
+                                       int lane, f32x4* acc, int nv, int half) {
 #pragma unroll
   for (int st = 0; st < PF_STEPS; ++st) {
     bf16x8 w[PF_GROUPS];
 #pragma unroll
     for (int q = 0; q < PF_GROUPS; ++q) {
-      if constexpr (F8) w[q] = e4m3x8_to_bf16(a.v[q][2 * st], a.v[q][2 * st + 1]);
+      if constexpr (F8) {
+        const u32x4& c = half ? a.v[q][1] : a.v[q][0];
+        w[q] = e4m3x8_to_bf16(c[2 * st], c[2 * st + 1]);
+      }
       else w[q] = a.v[q][st];
     }
 #pragma unroll
@@ -1077,7 +1085,7 @@ __device__ __forceinline__ void pf_finish(PfTile<NT>& st, const PfRaw<NT>& raw, 
   const int row = UP ? raw.g * PF_UP_COLS + wave * 8 * PF_GROUPS
                      : raw.g * PF_ROWS + wave * 16 * PF_GROUPS;
   st.wrow = (UP ? ((size_t)raw.ex * 2 * I + row) : ((size_t)raw.ex * H + row)) * K +
-            (F8 ? (size_t)(lane & 15) * K + (lane >> 4) * 16
+            (F8 ? slab_lane<16>(lane, K)
                 : (kFullLines ? slab_lane(lane, K) : (size_t)(lane & 15) * K + kq));
 #pragma unroll
   for (int i = 0; i < PfStage<NT * 16>::PER; ++i) {
@@ -1109,11 +1117,12 @@ __global__ __launch_bounds__(PF_THREADS, (NT <= 4 && UP) ? 4 : 1) void ffn_pf_ke
   using WT = std::conditional_t<F8, uint8_t, uint16_t>;
   const WT* w = static_cast<const WT*>(wv);
   constexpr bool FL = kFullLines && !F8;  // bf16 slabs through the wave's LDS tile
+  constexpr bool SLAB = FL || F8;          // FP8: pair slabs through the same tile
   constexpr int NR = NT * 16;
   constexpr int NACC = PF_GROUPS * NT;
   constexpr int NB_ARR = UP ? 1 : 2;  // B arrays: x, or h_hi and h_lo
   __shared__ __attribute__((aligned(16))) pf_row_t bs[2][NB_ARR][NR];
-  __shared__ u16x8 slab_t[FL ? PF_WAVES : 1][FL ? PF_GROUPS * 128 : 1];
+  __shared__ u16x8 slab_t[SLAB ? PF_WAVES : 1][SLAB ? PF_GROUPS * 128 : 1];
   __shared__ int fix_flag;
   const PlanRO pv = plan_ro(plan, pmax);
   if (pv.hdr[1] != 0) return;  // the dense kernels take this plan
@@ -1121,7 +1130,8 @@ __global__ __launch_bounds__(PF_THREADS, (NT <= 4 && UP) ? 4 : 1) void ffn_pf_ke
   const int K = UP ? H : I;
   const int G = UP ? I / PF_UP_COLS : H / PF_ROWS, C = K / PF_K;
   const int b = xcd_block(blockIdx.x, NB);
-  const Sched sc(b, P * G, C, NB);
+  constexpr int A = F8 ? 2 : 1;  // FP8: units in aligned pairs (C is even)
+  const Sched sc(b, P * G, C, NB, A);
   if (b >= sc.nb) return;
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
   const Pos p0 = sc.p0;
@@ -1157,12 +1167,14 @@ __global__ __launch_bounds__(PF_THREADS, (NT <= 4 && UP) ? 4 : 1) void ffn_pf_ke
     return (size_t)rot_chunk(kc, t.rot, C) * PF_K;
   };
   auto load_a = [&](PfA<F8>& a, const PfTile<NT>& t, int kc) {
-    const size_t kb = chunk(t, kc);
-    if constexpr (F8) {
+    if constexpr (F8) {  // the pair holding chunk kc (FP8 tiles are not rotated)
+      const size_t kb = (size_t)(kc & ~1) * PF_K;
 #pragma unroll
-      for (int q = 0; q < PF_GROUPS; ++q)
-        a.v[q] = *reinterpret_cast<const u32x4*>(w + t.wrow + pf_group_offset<UP>(q, H, I) + kb);
-    } else if constexpr (kFullLines) {
+      for (int q = 0; q < PF_GROUPS; ++q) slab_load(a.v[q], w + t.wrow + pf_group_offset<UP>(q, H, I) + kb, K);
+      return;
+    }
+    const size_t kb = chunk(t, kc);
+    if constexpr (kFullLines) {
       static_assert(PF_STEPS == 2, "a slab is two MFMA steps");
 #pragma unroll
       for (int q = 0; q < PF_GROUPS; ++q)
@@ -1190,7 +1202,7 @@ __global__ __launch_bounds__(PF_THREADS, (NT <= 4 && UP) ? 4 : 1) void ffn_pf_ke
   auto tile_end = [&](Pos p) {
     bool done = true;
     if (sc.split(p.t))
-      done = fixup_block<NACC, PF_WAVES>(acc, slots, counters, p.t - sc.TD, C, sc.US, sc.nb, b,
+      done = fixup_block<NACC, PF_WAVES>(acc, slots, counters, p.t - sc.TD, C / A, sc.US / A, sc.nb, b,
                                          lane, wave, &fix_flag);
     if (done) {
 #pragma unroll
@@ -1242,12 +1254,12 @@ __global__ __launch_bounds__(PF_THREADS, (NT <= 4 && UP) ? 4 : 1) void ffn_pf_ke
   // registers; chunk p1's token rows in flight
   // A3: the up projection with 8 token tiles (238 VGPRs) fetches its weights
   // two units ahead, through three register sets (share 0: 882 us against
-  // 911 us one unit ahead), and so do the FP8 kernels, whose register sets
-  // are small (fine-grained FP8 call: 2.26 ms against 2.31 ms; share 0
-  // unchanged), and the down projection with 4 token tiles (one block per
-  // CU, see the launch bounds); the bf16 down projection at 8 tiles measured
-  // the same either way and stays at one unit ahead.
-  constexpr bool A3 = (UP && NT >= 8) || F8 || (!UP && NT == 4);
+  // 911 us one unit ahead), and so does the down projection with 4 token
+  // tiles (one block per CU, see the launch bounds); the bf16 down projection
+  // at 8 tiles measured the same either way and stays at one unit ahead.
+  // FP8: two register sets, each the full-line slab of a pair of units,
+  // fetched at the pair's first unit for the pair two units ahead.
+  constexpr bool A3 = !F8 && ((UP && NT >= 8) || (!UP && NT == 4));
   PfA<F8> a0, a1, a2;  // a2: A3 only
   PfStage<NR> sb0[NB_ARR], sb1[NB_ARR];
   load_b(sb1, t0, p0.kc);
@@ -1257,12 +1269,13 @@ __global__ __launch_bounds__(PF_THREADS, (NT <= 4 && UP) ? 4 : 1) void ffn_pf_ke
   load_b(sb0, t1, p1.kc);
   __syncthreads();
 
-  // One unit: issue chunk p2's token rows and chunk p1's (A3: p2's) weights,
-  // multiply chunk p (weights `ca`, token rows in LDS buffer `cb`), write chunk p1's
-  // token rows (`cs`, loaded a step earlier) into the other buffer, finish the
-  // tile if p ends it here, and synchronise the block. Returns false after
-  // the block's last unit.
-  auto step = [&](PfA<F8>& ca, PfA<F8>& na, PfStage<NR> (&cs)[NB_ARR],
+  // One unit: issue chunk p2's token rows and chunk p1's (A3: p2's; FP8 at a
+  // pair's first unit: the pair p2 starts) weights, multiply chunk p (weights
+  // `ca`, half `half` of an FP8 pair; token rows in LDS buffer `cb`), write
+  // chunk p1's token rows (`cs`, loaded a step earlier) into the other
+  // buffer, finish the tile if p ends it here, and synchronise the block.
+  // Returns false after the block's last unit.
+  auto step = [&](int half, PfA<F8>& ca, PfA<F8>& na, PfStage<NR> (&cs)[NB_ARR],
                   PfStage<NR> (&ns)[NB_ARR], int cb, Pos& p) -> bool {
     const Pos p2 = sc.next(p1);
     if (p2.t != p1.t) {
@@ -1272,9 +1285,14 @@ __global__ __launch_bounds__(PF_THREADS, (NT <= 4 && UP) ? 4 : 1) void ffn_pf_ke
       t2 = t1;
     }
     load_b(ns, t2, p2.kc);
-    if constexpr (A3) load_a(na, t2, p2.kc);
-    else load_a(na, t1, p1.kc);
-    if constexpr (FL) {
+    if constexpr (F8) {
+      if (half == 0) load_a(na, t2, p2.kc);  // (after the last pair: its own again)
+    } else if constexpr (A3) {
+      load_a(na, t2, p2.kc);
+    } else {
+      load_a(na, t1, p1.kc);
+    }
+    if (FL || (F8 && half == 0)) {
 #pragma unroll
       for (int q = 0; q < PF_GROUPS; ++q) slab_frags(ca.v[q], slab_t[wave] + q * 128, lane);
     }
@@ -1285,7 +1303,7 @@ __global__ __launch_bounds__(PF_THREADS, (NT <= 4 && UP) ? 4 : 1) void ffn_pf_ke
     // test sits inside the tile loop: dispatching to kernels unrolled for
     // fewer tiles made every variant spill.
     const int nv = __builtin_amdgcn_readfirstlane(t0.ntiles);
-    pf_mma<NT, NT, UP, F8>(ca, bs[cb][0], bs[cb][NB_ARR - 1], lane, acc, nv);
+    pf_mma<NT, NT, UP, F8>(ca, bs[cb][0], bs[cb][NB_ARR - 1], lane, acc, nv, half);
     store_b(cs, cb ^ 1);
     const bool last = sc.last(p);
     if (sc.ends_tile(p)) tile_end(p);
@@ -1298,14 +1316,19 @@ __global__ __launch_bounds__(PF_THREADS, (NT <= 4 && UP) ? 4 : 1) void ffn_pf_ke
     return true;
   };
 
+  constexpr int h0 = 0, h1 = 1;
   Pos p = p0;
-  if constexpr (A3) {
-    while (step(a0, a2, sb0, sb1, 0, p) && step(a1, a0, sb1, sb0, 1, p) &&
-           step(a2, a1, sb0, sb1, 0, p) && step(a0, a2, sb1, sb0, 1, p) &&
-           step(a1, a0, sb0, sb1, 0, p) && step(a2, a1, sb1, sb0, 1, p)) {
+  if constexpr (F8) {
+    while (step(h0, a0, a1, sb0, sb1, 0, p) && step(h1, a0, a1, sb1, sb0, 1, p) &&
+           step(h0, a1, a0, sb0, sb1, 0, p) && step(h1, a1, a0, sb1, sb0, 1, p)) {
+    }
+  } else if constexpr (A3) {
+    while (step(h0, a0, a2, sb0, sb1, 0, p) && step(h0, a1, a0, sb1, sb0, 1, p) &&
+           step(h0, a2, a1, sb0, sb1, 0, p) && step(h0, a0, a2, sb1, sb0, 1, p) &&
+           step(h0, a1, a0, sb0, sb1, 0, p) && step(h0, a2, a1, sb1, sb0, 1, p)) {
     }
   } else {
-    while (step(a0, a1, sb0, sb1, 0, p) && step(a1, a0, sb1, sb0, 1, p)) {
+    while (step(h0, a0, a1, sb0, sb1, 0, p) && step(h0, a1, a0, sb1, sb0, 1, p)) {
     }
   }
 }
