@@ -22,7 +22,10 @@ The same run also measures:
   - an MFMA-bound probe: the share-0 expert weights with T=32768 tokens, the
     grouped FFN's useful bf16 TFLOP/s against the 2.5 PFLOP/s dense peak;
   - routing microseconds at 1024 experts (route + permute, T = 1 / 64 / 4096),
-    replayed from a captured graph (and issued call by call from Python);
+    replayed from a captured graph (and issued call by call from Python, and
+    as single calls warm and cold, the Infinity Cache flushed before each);
+  - the tiny layer (T=16, E=8, top-2) as single moe_forward calls, warm and
+    cold;
   - the oracle timed on the host cores as a CPU baseline (headline layer).
 Prints one JSON line.
 """
@@ -43,6 +46,9 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 PROBE_TOKENS = 32768
+# A GPU spin (~0.5 ms) queued before each single timed call, so that the call
+# waits behind running work and its events hold no host launch latency.
+SPIN_CYCLES = 1000000
 
 
 def parse_args():
@@ -226,21 +232,25 @@ class Layer:
         return self.torch.cuda.Event(enable_timing=True)
 
     def time_forward(self, steps, warmup):
-        """Wall time of `steps` moe_forward calls (synchronised on both sides)
-        and each call's event duration on the stream."""
+        """Wall time of `steps` back-to-back moe_forward calls (synchronised on
+        both sides), then each call's event duration on the stream over another
+        `steps` calls. The timed loop records no events: an event pair between
+        two calls holds the stream for ~10 us."""
         torch = self.torch
         for _ in range(warmup):
             self.forward()
         torch.cuda.synchronize()
-        evs = [(self.ev(), self.ev()) for _ in range(steps)]
-        torch.cuda.synchronize()
         t0 = time.perf_counter()
+        for _ in range(steps):
+            self.forward()
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+        evs = [(self.ev(), self.ev()) for _ in range(steps)]
         for a, b in evs:
             a.record(self.stream)
             self.forward()
             b.record(self.stream)
         torch.cuda.synchronize()
-        elapsed = time.perf_counter() - t0
         per = [a.elapsed_time(b) for a, b in evs]
         return elapsed, per
 
@@ -352,13 +362,19 @@ def routing_timings(torch):
     k = 8, T = 1 / 64 / 4096 through moe_route_permute, microseconds per call:
     `graph` replays 200 captured calls (each replay checked against the eager
     outputs), `eager` issues 200 calls from Python back to back, `separate`
-    replays 200 captured moe_route + moe_permute pairs."""
+    replays 200 captured moe_route + moe_permute pairs, `cold` times single
+    calls (median of 30, HIP events around the call) each issued after a kernel
+    that writes a 512 MiB buffer (the 256 MB Infinity Cache then holds none of
+    the routing's inputs or outputs) and `warm_single` the same single calls
+    without that write; both queue a GPU spin of ~0.5 ms before the call, so
+    the call waits behind running work and no host launch latency is timed."""
     import routing_grouped_expert_amd as moe
     from synth import configs
 
     Er, kr = configs.ROUTING["E"], configs.ROUTING["k"]
-    out = {"graph": {}, "eager": {}, "separate": {}}
+    out = {"graph": {}, "eager": {}, "separate": {}, "cold": {}, "warm_single": {}}
     n_it = 200
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda:0")
     for Tr in configs.ROUTING["T"]:
         lg = torch.from_numpy(configs.routing_logits(Tr)).to("cuda:0")
         bufs = dict(ri=torch.empty((Tr, kr), dtype=torch.int32, device="cuda:0"),
@@ -390,6 +406,19 @@ def routing_timings(torch):
         torch.cuda.synchronize()
         out["eager"][f"T{Tr}"] = round(a.elapsed_time(b) / n_it * 1e3, 2)
 
+        for key, cold in (("cold", True), ("warm_single", False)):
+            one = []
+            for i in range(30):
+                if cold:
+                    flush.fill_(i & 0xFF)
+                torch.cuda._sleep(SPIN_CYCLES)
+                a.record(stream)
+                pair(stream)
+                b.record(stream)
+                torch.cuda.synchronize()
+                one.append(a.elapsed_time(b) * 1e3)
+            out[key][f"T{Tr}"] = round(float(np.median(one)), 2)
+
         for key, fn in (("graph", pair), ("separate", separate)):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
@@ -415,6 +444,38 @@ def routing_timings(torch):
             out[key][f"T{Tr}"] = round(float(np.median(reps)), 2)
             del g
     return out
+
+
+def tiny_layer_us(torch):
+    """The tiny layer (T=16 H=128 I=256 E=8 top-2) through moe_forward: the
+    median of 50 single calls (HIP events around each call) warm, and cold,
+    each issued after a kernel that writes a 512 MiB buffer (so the Infinity
+    Cache holds none of the layer's 1.6 MB); both queue a GPU spin of ~0.5 ms
+    before the call (no host launch latency is timed). Its bytes and flops take
+    well under a microsecond at the roofs: the figure is the kernels' latency
+    chain."""
+    lay = Layer("tiny")
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda:0")
+    for _ in range(5):
+        lay.forward()
+    torch.cuda.synchronize()
+    res = {"workload": lay.describe()}
+    for key, cold in (("warm_us", False), ("cold_us", True)):
+        one = []
+        for i in range(50):
+            if cold:
+                flush.fill_(i & 0xFF)
+            torch.cuda._sleep(SPIN_CYCLES)
+            a, b = lay.ev(), lay.ev()
+            a.record(lay.stream)
+            lay.forward()
+            b.record(lay.stream)
+            torch.cuda.synchronize()
+            one.append(a.elapsed_time(b) * 1e3)
+        res[key] = round(float(np.median(one)), 2)
+    lay.check_output()
+    del flush
+    return res
 
 
 def cpu_baseline(layer, n_tok=32):
@@ -554,7 +615,9 @@ def main():
         r = routing_timings(torch)
         print(json.dumps({"routing_us_1024_experts": r["graph"],
                           "routing_us_1024_experts_eager": r["eager"],
-                          "routing_us_1024_experts_separate_calls": r["separate"]}))
+                          "routing_us_1024_experts_separate_calls": r["separate"],
+                          "routing_us_1024_experts_cold": r["cold"],
+                          "routing_us_1024_experts_warm_single": r["warm_single"]}))
         return
     if args.probe_only:
         base = Layer("share0", fp8=False)
@@ -564,6 +627,8 @@ def main():
     extras = {}
     probe = None
     if not args.no_extras:
+        extras["tiny"] = tiny_layer_us(torch)
+        log(f"tiny: {extras['tiny']['warm_us']} us warm, {extras['tiny']['cold_us']} us cold")
         for name in ("share0", "decode"):
             if name == args.workload:
                 continue
@@ -638,6 +703,8 @@ def main():
         "routing_us_1024_experts": None if routing is None else routing["graph"],
         "routing_us_1024_experts_eager": None if routing is None else routing["eager"],
         "routing_us_1024_experts_separate_calls": None if routing is None else routing["separate"],
+        "routing_us_1024_experts_cold": None if routing is None else routing["cold"],
+        "routing_us_1024_experts_warm_single": None if routing is None else routing["warm_single"],
     }
     for name, e in extras.items():
         out[name] = e
