@@ -254,6 +254,36 @@ class Layer:
         per = [a.elapsed_time(b) for a, b in evs]
         return elapsed, per
 
+    def time_forward_graph(self, steps):
+        """ms per step of `steps` moe_forward calls captured in one HIP graph
+        and replayed (median of 3 replays, events around each replay); the
+        outputs of every replay must equal those of the eager calls."""
+        torch = self.torch
+        torch.cuda.synchronize()
+        ref = self.y.clone()
+        g = torch.cuda.CUDAGraph()
+        saved = self.stream
+        with torch.cuda.graph(g):
+            self.stream = torch.cuda.current_stream()  # the capture stream
+            try:
+                for _ in range(steps):
+                    self.forward()
+            finally:
+                self.stream = saved
+        torch.cuda.synchronize()
+        reps = []
+        for _ in range(3):
+            self.y.fill_(7)
+            a, b = self.ev(), self.ev()
+            a.record(self.stream)
+            g.replay()
+            b.record(self.stream)
+            torch.cuda.synchronize()
+            reps.append(a.elapsed_time(b) / steps)
+            assert torch.equal(self.y, ref), f"{self.name}: graph replay output differs"
+        del g
+        return float(np.median(reps))
+
     def time_calls(self, steps):
         """Mean event duration (ms) of each of the five calls over `steps`
         back-to-back layer passes."""
@@ -307,6 +337,7 @@ class Layer:
 def summarize(layer, steps, warmup):
     """Layer timing, per-call breakdown and the grouped-FFN roofline figures."""
     elapsed, per = layer.time_forward(steps, warmup)
+    graph_ms = layer.time_forward_graph(steps)
     calls = layer.time_calls(steps)
     layer.check_output()
     fbytes, fflops, n_local, touched, cnt = layer.ffn_counts()
@@ -318,6 +349,7 @@ def summarize(layer, steps, warmup):
         "tokens_per_s": round(layer.T / (ms * 1e-3), 1),
         "step_ms_median": round(pct(per, 50), 4), "step_ms_p10": round(pct(per, 10), 4),
         "step_ms_p90": round(pct(per, 90), 4),
+        "ms_per_step_graph": round(graph_ms, 4),
         "layer_hbm_frac": round(lbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "call_ms": {n: round(v, 4) for n, v in calls.items()},
         "ffn_ms": round(ffn_ms, 4),
@@ -698,6 +730,7 @@ def main():
         "cpu_baseline": cpu,
         "step_ms": {"median": head["step_ms_median"], "p10": head["step_ms_p10"],
                     "p90": head["step_ms_p90"]},
+        "ms_per_step_graph": head["ms_per_step_graph"],
         "layer_hbm_frac": head["layer_hbm_frac"],
         "call_ms": head["call_ms"],
         "routing_us_1024_experts": None if routing is None else routing["graph"],
