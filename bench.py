@@ -234,8 +234,7 @@ class Layer:
     def time_forward(self, steps, warmup):
         """Wall time of `steps` back-to-back moe_forward calls (synchronised on
         both sides), then each call's event duration on the stream over another
-        `steps` calls. The timed loop records no events: an event pair between
-        two calls holds the stream for ~10 us."""
+        `steps` calls (the timed loop itself issues nothing but the calls)."""
         torch = self.torch
         for _ in range(warmup):
             self.forward()
