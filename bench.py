@@ -55,7 +55,7 @@ def parse_args():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="fine", choices=["tiny", "decode", "fine", "share0"])
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the share-0 / decode / FP8 extra keys and the MFMA probe")
@@ -636,11 +636,19 @@ def main():
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU "
               "expert-parallel path is not built.", file=sys.stderr)
         sys.exit(2)
+    import torch
+    # Everything runs on one created stream (default priority), as a serving
+    # loop would, not on the legacy null stream: the fine-grained layer ran
+    # 3.568 against 3.582 ms per step there.
+    with torch.cuda.stream(torch.cuda.Stream()):
+        run(args, torch)
+
+
+def run(args, torch):
     if args.routing_sweep:
         routing_sweep(args.routing_k)
         return
 
-    import torch
     fp8 = args.weights == "fp8"
     if args.routing_only:
         r = routing_timings(torch)
