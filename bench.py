@@ -254,9 +254,10 @@ class Layer:
         return elapsed, per
 
     def time_forward_graph(self, steps):
-        """ms per step of `steps` moe_forward calls captured in one HIP graph
-        and replayed (median of 3 replays, events around each replay); the
-        outputs of every replay must equal those of the eager calls."""
+        """(ms per step, outputs equal) for `steps` moe_forward calls captured
+        in one HIP graph and replayed: the median of 3 replays (events around
+        each replay), and whether every replay's output equals the eager
+        calls' (reported, not asserted: the GPU tests check replays)."""
         torch = self.torch
         torch.cuda.synchronize()
         ref = self.y.clone()
@@ -270,7 +271,7 @@ class Layer:
             finally:
                 self.stream = saved
         torch.cuda.synchronize()
-        reps = []
+        reps, same = [], True
         for _ in range(3):
             self.y.fill_(7)
             a, b = self.ev(), self.ev()
@@ -279,9 +280,11 @@ class Layer:
             b.record(self.stream)
             torch.cuda.synchronize()
             reps.append(a.elapsed_time(b) / steps)
-            assert torch.equal(self.y, ref), f"{self.name}: graph replay output differs"
+            same = same and torch.equal(self.y, ref)
         del g
-        return float(np.median(reps))
+        if not same:
+            log(f"{self.name}: graph replay output differs from the eager calls")
+        return float(np.median(reps)), same
 
     def time_calls(self, steps):
         """Mean event duration (ms) of each of the five calls over `steps`
@@ -336,7 +339,7 @@ class Layer:
 def summarize(layer, steps, warmup):
     """Layer timing, per-call breakdown and the grouped-FFN roofline figures."""
     elapsed, per = layer.time_forward(steps, warmup)
-    graph_ms = layer.time_forward_graph(steps)
+    graph_ms, graph_same = layer.time_forward_graph(steps)
     calls = layer.time_calls(steps)
     layer.check_output()
     fbytes, fflops, n_local, touched, cnt = layer.ffn_counts()
@@ -349,6 +352,7 @@ def summarize(layer, steps, warmup):
         "step_ms_median": round(pct(per, 50), 4), "step_ms_p10": round(pct(per, 10), 4),
         "step_ms_p90": round(pct(per, 90), 4),
         "ms_per_step_graph": round(graph_ms, 4),
+        "graph_replay_matches_eager": graph_same,
         "layer_hbm_frac": round(lbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "call_ms": {n: round(v, 4) for n, v in calls.items()},
         "ffn_ms": round(ffn_ms, 4),
@@ -738,6 +742,7 @@ def run(args, torch):
         "step_ms": {"median": head["step_ms_median"], "p10": head["step_ms_p10"],
                     "p90": head["step_ms_p90"]},
         "ms_per_step_graph": head["ms_per_step_graph"],
+        "graph_replay_matches_eager": head["graph_replay_matches_eager"],
         "layer_hbm_frac": head["layer_hbm_frac"],
         "call_ms": head["call_ms"],
         "routing_us_1024_experts": None if routing is None else routing["graph"],
